@@ -1,0 +1,230 @@
+"""ctypes binding of the C ABI in include/infini_attn.h (argument marshalling only).
+
+Every step of the forward pass runs in the HIP library; this module only turns
+torch tensors into device pointers and the current torch stream into a
+``hipStream_t``. If the library is missing it raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Dict, Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libinfini_attn.so")
+
+OK = 0
+ERR_INVALID = -1
+ERR_UNSUPPORTED = -2
+ERR_HIP = -3
+ERR_OOM = -4
+F32 = 0
+BF16 = 1
+LINEAR = 0
+DELTA = 1
+
+EXPORTS = ("infini_attn_check", "infini_attn_workspace_size", "infini_attn_create",
+           "infini_attn_forward", "infini_attn_destroy", "infini_attn_strerror",
+           "infini_attn_set_timing", "infini_attn_get_timing")
+
+
+class InfiniAttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("d_k", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("stream", ctypes.c_void_p),
+        ("device", ctypes.c_int32),
+    ]
+
+
+class InfiniAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"{p} is missing: build the HIP library first "
+                "(python -m compressive_memory_transformers_segment_amd.build)")
+        lib = ctypes.CDLL(p)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        dp = ctypes.POINTER(InfiniAttnDesc)
+        lib.infini_attn_check.argtypes = [dp, i32, i32]
+        lib.infini_attn_check.restype = ctypes.c_int
+        lib.infini_attn_workspace_size.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_size_t)]
+        lib.infini_attn_workspace_size.restype = ctypes.c_int
+        lib.infini_attn_create.argtypes = [ctypes.POINTER(vp), dp]
+        lib.infini_attn_create.restype = ctypes.c_int
+        lib.infini_attn_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
+        lib.infini_attn_forward.restype = ctypes.c_int
+        lib.infini_attn_destroy.argtypes = [vp]
+        lib.infini_attn_destroy.restype = ctypes.c_int
+        lib.infini_attn_set_timing.argtypes = [vp, i32]
+        lib.infini_attn_set_timing.restype = ctypes.c_int
+        lib.infini_attn_get_timing.argtypes = [vp, ctypes.POINTER(i32),
+                                               ctypes.POINTER(ctypes.c_float),
+                                               ctypes.POINTER(ctypes.c_float)]
+        lib.infini_attn_get_timing.restype = ctypes.c_int
+        lib.infini_attn_strerror.argtypes = [ctypes.c_int]
+        lib.infini_attn_strerror.restype = ctypes.c_char_p
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def strerror(status: int) -> str:
+    try:
+        return load().infini_attn_strerror(int(status)).decode()
+    except RuntimeError:
+        return f"status {status}"
+
+
+def make_desc(batch, n_q_heads, n_kv_heads, seq_len, d_k, d_v, dtype, eps=1e-6, stream=None,
+              device=0) -> InfiniAttnDesc:
+    return InfiniAttnDesc(int(batch), int(n_q_heads), int(n_kv_heads), int(seq_len), int(d_k),
+                          int(d_v), int(dtype), float(eps), stream, int(device))
+
+
+# ---- the C entry points, same names ----------------------------------------
+
+def infini_attn_check(desc: InfiniAttnDesc, seg_len: int, update_mode: int) -> int:
+    return load().infini_attn_check(ctypes.byref(desc), int(seg_len), int(update_mode))
+
+
+def infini_attn_workspace_size(desc: InfiniAttnDesc, seg_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().infini_attn_workspace_size(ctypes.byref(desc), int(seg_len), ctypes.byref(n))
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_workspace_size")
+    return int(n.value)
+
+
+def infini_attn_create(desc: InfiniAttnDesc) -> int:
+    h = ctypes.c_void_p(None)
+    st = load().infini_attn_create(ctypes.byref(h), ctypes.byref(desc))
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_create")
+    return h.value
+
+
+def infini_attn_forward(handle: int, q: int, k: int, v: int, beta: int, M: int, z: int,
+                        seg_len: int, update_mode: int, out: int) -> None:
+    st = load().infini_attn_forward(handle, q, k, v, beta, M, z, int(seg_len), int(update_mode),
+                                    out)
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_forward")
+
+
+def infini_attn_destroy(handle: Optional[int]) -> None:
+    st = load().infini_attn_destroy(handle)
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_destroy")
+
+
+def infini_attn_set_timing(handle: int, enable: bool) -> None:
+    st = load().infini_attn_set_timing(handle, int(bool(enable)))
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_set_timing")
+
+
+def infini_attn_get_timing(handle: int) -> Tuple[int, float, float]:
+    """(calls, scan_ms, fused_ms) summed over the calls timed since the last get."""
+    n = ctypes.c_int32(0)
+    a = ctypes.c_float(0.0)
+    b = ctypes.c_float(0.0)
+    st = load().infini_attn_get_timing(handle, ctypes.byref(n), ctypes.byref(a), ctypes.byref(b))
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_get_timing")
+    return int(n.value), float(a.value), float(b.value)
+
+
+# ---- torch-tensor convenience ------------------------------------------------
+
+_handles: Dict[Tuple, int] = {}
+
+
+def _mode(update_mode) -> int:
+    if isinstance(update_mode, str):
+        return {"linear": LINEAR, "delta": DELTA}[update_mode]
+    return int(update_mode)
+
+
+def handle_for(q, k, eps: float = 1e-6, stream=None) -> int:
+    """Cached handle for this shape, dtype, eps, device and stream."""
+    import torch
+
+    B, Hq, L, D = q.shape
+    Hkv = k.shape[1]
+    dtype = {torch.float32: F32, torch.bfloat16: BF16}.get(q.dtype)
+    if dtype is None:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    key = (B, Hq, Hkv, L, D, k.shape[3], dtype, float(eps), int(stream), dev)
+    h = _handles.get(key)
+    if h is None:
+        h = infini_attn_create(make_desc(B, Hq, Hkv, L, D, k.shape[3], dtype, eps, stream, dev))
+        _handles[key] = h
+    return h
+
+
+def forward(q, k, v, beta, M, z, seg_len: int, update_mode="linear", out=None,
+            eps: float = 1e-6):
+    """Infini-attention forward on device tensors; (M, z) are updated in place.
+
+    q [B, Hq, L, d], k/v [B, Hkv, L, d] (fp32 or bf16, contiguous), beta [Hq]
+    fp32, M [B, Hkv, d, d] fp32, z [B, Hkv, d] fp32. Returns out [B, Hq, L, d].
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("M", M), ("z", z)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    for name, t in (("beta", beta), ("M", M), ("z", z)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    B, Hq, L, D = q.shape
+    Hkv = k.shape[1]
+    if (tuple(k.shape) != (B, Hkv, L, D) or tuple(v.shape) != (B, Hkv, L, v.shape[3])
+            or tuple(beta.shape) != (Hq,) or tuple(M.shape) != (B, Hkv, D, v.shape[3])
+            or tuple(z.shape) != (B, Hkv, D)):
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, Hq, L, v.shape[3]), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (B, Hq, L, v.shape[3]) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    h = handle_for(q, k, eps)
+    infini_attn_forward(h, q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                        M.data_ptr(), z.data_ptr(), seg_len, _mode(update_mode), out.data_ptr())
+    return out
+
+
+def release_handles() -> None:
+    for h in list(_handles.values()):
+        infini_attn_destroy(h)
+    _handles.clear()

@@ -1,0 +1,345 @@
+// Fused per-segment kernel, bf16 storage path: MFMA bf16 with fp32 accumulate.
+//
+// For each (batch, query head, segment, 128-row query tile):
+//   A_dot = causal softmax(Q K^T / sqrt(d_k)) V inside the segment
+//           ([HF-repro] "Infini-Attention メカニズム", step Local Attention;
+//           [LNCB-review] "基本アイデア"),
+//   A_mem = sigma(Q) M_{s-1} / (sigma(Q) z_{s-1} + eps)
+//           (step Memory Retrieval; [LNCB-review] "メモリの読み出し"),
+//   out   = g A_mem + (1 - g) A_dot with g = sigmoid(beta_h)
+//           (step Integration; [LNCB-review] "長期情報と短期情報の統合").
+//
+// Design (gfx950, wave64, v_mfma_f32_32x32x16_bf16):
+//   * 4 waves per workgroup, 32 query rows per wave. Everything is computed
+//     transposed: S^T = K Q^T and O^T = V^T P^T. In the 32x32 MFMA result
+//     layout a lane owns one column, so with queries as columns every lane owns
+//     one query row: the running max / sum of the online softmax are per lane
+//     (plus one exchange with the lane 32 away), and the probabilities P leave
+//     the first MFMA already in the operand layout of the second (the key index
+//     is the contraction index of P V, and the order in which the hardware
+//     walks a contraction does not matter as long as both operands agree).
+//   * Q stays in registers for the whole key loop (its d-contiguous rows are
+//     exactly the B operand of S^T = K Q^T).
+//   * K tiles are staged row-major in LDS (A operand of S^T, d-contiguous).
+//     V tiles are staged transposed in LDS, [d][key], so the A operand of
+//     O^T = V^T P^T is two 8-byte LDS reads per lane. Global loads of the next
+//     tile are issued before the current tile's MFMAs.
+//   * Causal skipping: a query tile visits key tiles up to its diagonal only;
+//     a wave skips tiles entirely in its future and masks only diagonal tiles.
+//   * Epilogue: the pre-segment snapshot M^T (bf16, [d_v][d_k]) is staged in
+//     LDS and multiplied with sigma(Q) (computed from the Q registers) on MFMA;
+//     the denominator sigma(Q).z is a per-lane dot product plus one exchange.
+
+#include "common.h"
+#include "launch.h"
+
+namespace ia {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBM = 128;  // query rows per workgroup (32 per wave)
+constexpr int kBN = 64;   // key rows per tile
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+template <int D>
+struct Tile {
+  static constexpr int KSTR = D + 8;    // sK row stride in bf16 (16-byte pad)
+  static constexpr int VSTR = kBN + 4;  // sVt row stride in bf16 (8-byte pad)
+  static constexpr int MSTR = D + 8;    // staged M^T row stride in bf16
+  static constexpr int KCH = kBN * D / 8 / kThreads;  // 16-byte K chunks per thread
+  static constexpr int VC = D / 16;                   // V columns per thread (x 4 rows)
+  static constexpr int LDS_ATT = kBN * KSTR + D * VSTR;
+  static constexpr int LDS_MEM = D * MSTR;
+  static constexpr int LDS = LDS_ATT > LDS_MEM ? LDS_ATT : LDS_MEM;
+};
+
+// Load VC consecutive bf16 (VC in {2, 4, 8}) as VC/2 packed words.
+template <int VC>
+__device__ __forceinline__ void load_cols(const uint16_t *p, uint32_t (&w)[VC / 2]) {
+  if constexpr (VC == 8) {
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(p);
+    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+  } else if constexpr (VC == 4) {
+    const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+    w[0] = x[0]; w[1] = x[1];
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t *>(p);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const float *__restrict__ beta,
+    const float *__restrict__ z_pre, const uint16_t *__restrict__ mt_pre,
+    uint16_t *__restrict__ out, int Hq, int Hkv, int L, int N, int S, int n_qt, float eps,
+    float scale_log2) {
+  using TL = Tile<D>;
+  constexpr int NT = D / 16;  // k-steps over d
+  constexpr int ND = D / 32;  // 32-row d tiles of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS];
+  __shared__ float sZ[D];
+  uint16_t *sK = smem;
+  uint16_t *sVt = smem + kBN * TL::KSTR;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+
+  // Longest query tiles (most key tiles under the causal mask) first.
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x);
+  const int s = blockIdx.y;
+  const int bhq = blockIdx.z;
+  const int b = bhq / Hq, h = bhq - b * Hq;
+  const int hk = h / (Hq / Hkv);
+  const int a = s * N;
+  const int e = min(a + N, L);
+  const int q0 = a + qt * kBM;
+  if (q0 >= e) return;  // short last segment: whole workgroup idle
+  const int qw = q0 + w * 32;  // first query row of this wave
+  const int qrow = qw + l32;   // query row owned by this lane
+  const bool wave_live = qw < e;
+
+  const uint16_t *qp = q + static_cast<size_t>(bhq) * L * D;
+  const size_t kvoff = (static_cast<size_t>(b) * Hkv + hk) * L * D;
+  const uint16_t *kp = k + kvoff;
+  const uint16_t *vp = v + kvoff;
+
+  // Q^T operand: k-step t covers d in [16t, 16t+16); lane holds d = 16t + 8g + 0..7.
+  u32x4 qf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    qf[t] = (qrow < e) ? *reinterpret_cast<const u32x4 *>(qp + static_cast<size_t>(qrow) * D +
+                                                          16 * t + 8 * g)
+                       : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  f32x16 o[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x16{};
+  float m = -INFINITY;  // running max of this row, log2 domain
+  float lsum = 0.f;     // running sum over this lane's key slots
+
+  const int kv_end = min(q0 + kBM, e);
+
+  // Register staging of the next K / V tile.
+  u32x4 kreg[TL::KCH];
+  uint32_t vreg[4][TL::VC / 2];
+  const int v_kg = tid & 15;  // 4-row key group
+  const int v_cc = tid >> 4;  // VC-column chunk
+
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int r = 0; r < TL::KCH; ++r) {
+      const int c = tid + kThreads * r;
+      const int row = c / (D / 8), col8 = c % (D / 8);
+      kreg[r] = (kv0 + row < e)
+                    ? *reinterpret_cast<const u32x4 *>(kp + static_cast<size_t>(kv0 + row) * D +
+                                                      col8 * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = kv0 + 4 * v_kg + r;
+      if (row < e) {
+        load_cols<TL::VC>(vp + static_cast<size_t>(row) * D + v_cc * TL::VC, vreg[r]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < TL::VC / 2; ++i) vreg[r][i] = 0u;
+      }
+    }
+  };
+
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int r = 0; r < TL::KCH; ++r) {
+      const int c = tid + kThreads * r;
+      const int row = c / (D / 8), col8 = c % (D / 8);
+      *reinterpret_cast<u32x4 *>(sK + row * TL::KSTR + col8 * 8) = kreg[r];
+    }
+    // Transpose 4 rows x VC columns: one 8-byte write of 4 keys per column.
+#pragma unroll
+    for (int i = 0; i < TL::VC / 2; ++i) {
+      const uint32_t r0 = vreg[0][i], r1 = vreg[1][i], r2 = vreg[2][i], r3 = vreg[3][i];
+      const u32x2 lo = {(r0 & 0xffffu) | (r1 << 16), (r2 & 0xffffu) | (r3 << 16)};
+      const u32x2 hi = {(r0 >> 16) | (r1 & 0xffff0000u), (r2 >> 16) | (r3 & 0xffff0000u)};
+      const int col = v_cc * TL::VC + 2 * i;
+      *reinterpret_cast<u32x2 *>(sVt + col * TL::VSTR + 4 * v_kg) = lo;
+      *reinterpret_cast<u32x2 *>(sVt + (col + 1) * TL::VSTR + 4 * v_kg) = hi;
+    }
+  };
+
+  load_tile(a);
+  for (int kv0 = a; kv0 < kv_end; kv0 += kBN) {
+    __syncthreads();  // every wave is done reading the previous tile
+    store_tile();
+    __syncthreads();
+    if (kv0 + kBN < kv_end) load_tile(kv0 + kBN);
+
+    if (wave_live && kv0 <= qw + 31) {
+      // S^T tile pair: rows = keys kv0 + 32T + ..., columns = this wave's queries.
+      f32x16 st[2];
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        st[T] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const u32x4 ka = *reinterpret_cast<const u32x4 *>(sK + (32 * T + l32) * TL::KSTR +
+                                                           16 * t + 8 * g);
+          st[T] = mfma32(as_bf16x8(ka), as_bf16x8(qf[t]), st[T]);
+        }
+      }
+      // Scale to the log2 domain; mask future keys and keys past the segment end.
+      const bool diag = (kv0 + kBN - 1 > qw) || (kv0 + kBN > e);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = st[T][i] * scale_log2;
+          if (diag) {
+            const int kvi = kv0 + 32 * T + (i >> 2) * 8 + 4 * g + (i & 3);
+            if (kvi > qrow || kvi >= e) x = -INFINITY;
+          }
+          st[T][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);  // finite: the segment's first key is always visible
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      float psum = 0.f;
+      u32x4 pb[2][2];
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          uint32_t pw[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float p0 = __builtin_amdgcn_exp2f(st[T][8 * u + 2 * jj] - m_new);
+            const float p1 = __builtin_amdgcn_exp2f(st[T][8 * u + 2 * jj + 1] - m_new);
+            psum += p0 + p1;
+            pw[jj] = pack_bf16x2(p0, p1);
+          }
+          pb[T][u] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+        }
+      }
+      lsum = lsum * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+      // O^T += V^T P^T. Slot j of lane group g is key 16u + 8(j/4) + 4g + j%4 of
+      // the 32-key half T, matching the S^T result layout.
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const uint16_t *vrow = sVt + (32 * dt + l32) * TL::VSTR + 4 * g;
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vrow + 32 * T + 16 * u);
+            const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vrow + 32 * T + 16 * u + 8);
+            const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+            o[dt] = mfma32(as_bf16x8(va), as_bf16x8(pb[T][u]), o[dt]);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- retrieval from the pre-segment snapshot and the gate ----
+  const size_t head = static_cast<size_t>(b) * Hkv + hk;
+  const uint16_t *mt = mt_pre + (head * S + s) * D * D;
+  const float *zs = z_pre + (head * (S + 1) + s) * D;
+  __syncthreads();  // key loop done: reuse smem for M^T
+  for (int c = tid; c < D * D / 8; c += kThreads) {
+    const int row = c / (D / 8), col8 = c % (D / 8);
+    *reinterpret_cast<u32x4 *>(smem + row * TL::MSTR + col8 * 8) =
+        *reinterpret_cast<const u32x4 *>(mt + static_cast<size_t>(row) * D + col8 * 8);
+  }
+  if (tid < D) sZ[tid] = zs[tid];
+  __syncthreads();
+
+  if (!wave_live) return;
+  // sigma(Q) as the B operand, and this lane's part of sigma(q).z.
+  float den = 0.f;
+  u32x4 sq[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    uint32_t wv[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float x0 = elu1(lo_bf16(qf[t][jj]));
+      const float x1 = elu1(hi_bf16(qf[t][jj]));
+      den += x0 * sZ[16 * t + 8 * g + 2 * jj] + x1 * sZ[16 * t + 8 * g + 2 * jj + 1];
+      wv[jj] = pack_bf16x2(x0, x1);
+    }
+    sq[t] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+  }
+  den += __shfl_xor(den, 32);
+  den += eps;
+  const float inv_den = 1.f / den;
+  const float inv_l = 1.f / (lsum + __shfl_xor(lsum, 32));
+  const float gam = 1.f / (1.f + __expf(-beta[h]));
+  const float w_mem = gam * inv_den;
+  const float w_dot = (1.f - gam) * inv_l;
+
+  uint16_t *op = out + (static_cast<size_t>(bhq) * L + qrow) * D;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+    f32x16 am = f32x16{};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 ma = *reinterpret_cast<const u32x4 *>(smem + (32 * dt + l32) * TL::MSTR +
+                                                       16 * t + 8 * g);
+      am = mfma32(as_bf16x8(ma), as_bf16x8(sq[t]), am);
+    }
+    if (qrow < e) {
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        uint32_t pk[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int i0 = 4 * gi + 2 * jj;
+          pk[jj] = pack_bf16x2(w_mem * am[i0] + w_dot * o[dt][i0],
+                               w_mem * am[i0 + 1] + w_dot * o[dt][i0 + 1]);
+        }
+        *reinterpret_cast<u32x2 *>(op + 32 * dt + 8 * gi + 4 * g) = u32x2{pk[0], pk[1]};
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_t(const Geometry &g, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const float *beta, const Workspace &ws, uint16_t *out, hipStream_t stream) {
+  const int rows = g.N < g.L ? g.N : g.L;
+  const int n_qt = (rows + kBM - 1) / kBM;
+  dim3 grid(n_qt, g.S, g.B * g.Hq);
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  fused_bf16_kernel<D><<<grid, kThreads, 0, stream>>>(q, k, v, beta, ws.z_pre, ws.mt_pre_bf16,
+                                                      out, g.Hq, g.Hkv, g.L, g.N, g.S, n_qt,
+                                                      g.eps, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fused_bf16(const Geometry &g, const uint16_t *q, const uint16_t *k,
+                             const uint16_t *v, const float *beta, const Workspace &ws,
+                             uint16_t *out, hipStream_t stream) {
+  switch (g.D) {
+    case 32: return launch_t<32>(g, q, k, v, beta, ws, out, stream);
+    case 64: return launch_t<64>(g, q, k, v, beta, ws, out, stream);
+    case 128: return launch_t<128>(g, q, k, v, beta, ws, out, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ia

@@ -1,0 +1,278 @@
+// Host side of the C ABI declared in include/infini_attn.h: argument
+// validation, the handle and its workspace, and the launch sequence
+//   segment scan  ->  fused per-segment attention  ->  copy of the final z
+// enqueued on the handle's stream with no host synchronisation.
+
+#include "infini_attn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <new>
+#include <vector>
+
+#include "launch.h"
+
+struct TimedCall {
+  hipEvent_t ev[3];  // before scan, after scan, after fused kernel
+};
+
+struct infini_attn_handle {
+  infini_attn_desc desc;
+  hipStream_t stream;
+  void *ws;
+  size_t ws_bytes;
+  bool timing;
+  std::vector<TimedCall> recorded;  // calls timed since the last get
+  std::vector<TimedCall> spare;     // event triples ready for reuse
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_desc(const infini_attn_desc *d) {
+  if (!d) return INFINI_ATTN_ERR_INVALID;
+  if (d->batch < 0 || d->seq_len < 0) return INFINI_ATTN_ERR_INVALID;
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->d_k < 1 || d->d_v < 1)
+    return INFINI_ATTN_ERR_INVALID;
+  if (d->n_q_heads % d->n_kv_heads != 0) return INFINI_ATTN_ERR_INVALID;
+  if (d->dtype != INFINI_ATTN_F32 && d->dtype != INFINI_ATTN_BF16) return INFINI_ATTN_ERR_INVALID;
+  if (!(d->eps > 0.f) || !(d->eps < 3.0e38f)) return INFINI_ATTN_ERR_INVALID;  // rejects NaN/inf
+  if (d->device < 0) return INFINI_ATTN_ERR_INVALID;
+  if (d->d_k != d->d_v) return INFINI_ATTN_ERR_UNSUPPORTED;
+  if (d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return INFINI_ATTN_ERR_UNSUPPORTED;
+  // Every tensor is addressed with 64-bit offsets, but grid dimensions are
+  // limited: B * Hq blocks along one axis.
+  if (static_cast<int64_t>(d->batch) * d->n_q_heads > 65535) return INFINI_ATTN_ERR_UNSUPPORTED;
+  return INFINI_ATTN_OK;
+}
+
+int n_segments(int L, int N) { return L == 0 ? 0 : (L + N - 1) / N; }
+
+// Workspace layout (each part 256-byte aligned):
+//   z_pre  [B*Hkv][S+1][D] fp32   (slot S receives the final z)
+//   mt_pre [B*Hkv][S][D][D]       fp32 or bf16 by storage type
+size_t ws_parts(const infini_attn_desc *d, int S, size_t *z_bytes) {
+  const size_t heads = static_cast<size_t>(d->batch) * d->n_kv_heads;
+  const size_t D = static_cast<size_t>(d->d_k);
+  *z_bytes = round_up(heads * (S + 1) * D * sizeof(float));
+  const size_t el = d->dtype == INFINI_ATTN_F32 ? sizeof(float) : sizeof(uint16_t);
+  return *z_bytes + round_up(heads * S * D * D * el);
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return INFINI_ATTN_OK;
+  if (e == hipErrorOutOfMemory) return INFINI_ATTN_ERR_OOM;
+  return INFINI_ATTN_ERR_HIP;
+}
+
+// Makes `dev` current for the lifetime of the guard and restores the caller's
+// device afterwards.
+struct DeviceGuard {
+  int prev = -1;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int infini_attn_check(const infini_attn_desc *desc, int32_t seg_len, int32_t update_mode) {
+  const int st = check_desc(desc);
+  if (st != INFINI_ATTN_OK) return st;
+  if (seg_len < 1) return INFINI_ATTN_ERR_INVALID;
+  if (update_mode != INFINI_ATTN_LINEAR && update_mode != INFINI_ATTN_DELTA)
+    return INFINI_ATTN_ERR_INVALID;
+  if (static_cast<int64_t>(n_segments(desc->seq_len, seg_len)) > 65535)
+    return INFINI_ATTN_ERR_UNSUPPORTED;
+  return INFINI_ATTN_OK;
+}
+
+int infini_attn_workspace_size(const infini_attn_desc *desc, int32_t seg_len, size_t *bytes) {
+  if (!bytes) return INFINI_ATTN_ERR_INVALID;
+  const int st = infini_attn_check(desc, seg_len, INFINI_ATTN_LINEAR);
+  if (st != INFINI_ATTN_OK) return st;
+  size_t zb = 0;
+  *bytes = ws_parts(desc, n_segments(desc->seq_len, seg_len), &zb);
+  return INFINI_ATTN_OK;
+}
+
+int infini_attn_create(infini_attn_t **h, const infini_attn_desc *desc) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  *h = nullptr;
+  const int st = check_desc(desc);
+  if (st != INFINI_ATTN_OK) return st;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return INFINI_ATTN_ERR_HIP;
+  if (desc->device >= count) return INFINI_ATTN_ERR_INVALID;
+  DeviceGuard guard(desc->device);
+  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  infini_attn_handle *p = new (std::nothrow) infini_attn_handle;
+  if (!p) return INFINI_ATTN_ERR_OOM;
+  p->desc = *desc;
+  p->stream = static_cast<hipStream_t>(desc->stream);
+  p->ws = nullptr;
+  p->ws_bytes = 0;
+  p->timing = false;
+  *h = p;
+  return INFINI_ATTN_OK;
+}
+
+int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const void *v,
+                        const float *beta, float *M, float *z, int32_t seg_len,
+                        int32_t update_mode, void *out) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  const infini_attn_desc &d = h->desc;
+  int st = infini_attn_check(&d, seg_len, update_mode);
+  if (st != INFINI_ATTN_OK) return st;
+  if (d.batch == 0 || d.seq_len == 0) return INFINI_ATTN_OK;  // nothing to do; state unchanged
+  if (!q || !k || !v || !beta || !M || !z || !out) return INFINI_ATTN_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return INFINI_ATTN_ERR_INVALID;
+  if (!aligned(beta, 4) || !aligned(M, 4) || !aligned(z, 4)) return INFINI_ATTN_ERR_INVALID;
+
+  DeviceGuard guard(d.device);
+  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+
+  ia::Geometry g;
+  g.B = d.batch;
+  g.Hq = d.n_q_heads;
+  g.Hkv = d.n_kv_heads;
+  g.L = d.seq_len;
+  g.D = d.d_k;
+  g.N = seg_len;
+  g.S = n_segments(d.seq_len, seg_len);
+  g.eps = d.eps;
+
+  size_t z_bytes = 0;
+  const size_t need = ws_parts(&d, g.S, &z_bytes);
+  if (need > h->ws_bytes) {
+    if (h->ws) {
+      // hipFree waits for work still using the old buffer.
+      if (hipFree(h->ws) != hipSuccess) return INFINI_ATTN_ERR_HIP;
+      h->ws = nullptr;
+      h->ws_bytes = 0;
+    }
+    void *p = nullptr;
+    const hipError_t e = hipMalloc(&p, need);
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? INFINI_ATTN_ERR_OOM : INFINI_ATTN_ERR_HIP;
+    h->ws = p;
+    h->ws_bytes = need;
+  }
+  ia::Workspace ws;
+  ws.z_pre = static_cast<float *>(h->ws);
+  void *mt = static_cast<char *>(h->ws) + z_bytes;
+  const bool bf16 = d.dtype == INFINI_ATTN_BF16;
+  ws.mt_pre_f32 = bf16 ? nullptr : static_cast<float *>(mt);
+  ws.mt_pre_bf16 = bf16 ? static_cast<uint16_t *>(mt) : nullptr;
+
+  TimedCall tc{};
+  if (h->timing) {
+    if (!h->spare.empty()) {
+      tc = h->spare.back();
+      h->spare.pop_back();
+    } else {
+      for (int i = 0; i < 3; ++i) {
+        if (hipEventCreate(&tc.ev[i]) != hipSuccess) {
+          for (int j = 0; j < i; ++j) (void)hipEventDestroy(tc.ev[j]);
+          return INFINI_ATTN_ERR_HIP;
+        }
+      }
+    }
+    h->recorded.push_back(tc);
+    if (hipEventRecord(tc.ev[0], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  }
+  hipError_t e = ia::launch_segment_scan(g, bf16, k, v, M, z, update_mode == INFINI_ATTN_DELTA,
+                                         ws, h->stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (h->timing && hipEventRecord(tc.ev[1], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  if (bf16) {
+    e = ia::launch_fused_bf16(g, static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                              static_cast<const uint16_t *>(v), beta, ws,
+                              static_cast<uint16_t *>(out), h->stream);
+  } else {
+    e = ia::launch_fused_f32(g, static_cast<const float *>(q), static_cast<const float *>(k),
+                             static_cast<const float *>(v), beta, ws, static_cast<float *>(out),
+                             h->stream);
+  }
+  if (e != hipSuccess) return hip_status(e);
+  if (h->timing && hipEventRecord(tc.ev[2], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  // Final z: slot S of every head's snapshot row -> z [B*Hkv][D].
+  const size_t row = static_cast<size_t>(g.D) * sizeof(float);
+  e = hipMemcpy2DAsync(z, row, ws.z_pre + static_cast<size_t>(g.S) * g.D, (g.S + 1) * row, row,
+                       static_cast<size_t>(g.B) * g.Hkv, hipMemcpyDeviceToDevice, h->stream);
+  return hip_status(e);
+}
+
+int infini_attn_set_timing(infini_attn_t *h, int32_t enable) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  h->timing = enable != 0;
+  return INFINI_ATTN_OK;
+}
+
+int infini_attn_get_timing(infini_attn_t *h, int32_t *calls, float *scan_ms, float *fused_ms) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  DeviceGuard guard(h->desc.device);
+  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  double scan = 0.0, fused = 0.0;
+  int st = INFINI_ATTN_OK;
+  for (TimedCall &tc : h->recorded) {
+    float a = 0.f, b = 0.f;
+    if (hipEventSynchronize(tc.ev[2]) != hipSuccess ||
+        hipEventElapsedTime(&a, tc.ev[0], tc.ev[1]) != hipSuccess ||
+        hipEventElapsedTime(&b, tc.ev[1], tc.ev[2]) != hipSuccess) {
+      st = INFINI_ATTN_ERR_HIP;
+    }
+    scan += a;
+    fused += b;
+    h->spare.push_back(tc);
+  }
+  if (calls) *calls = static_cast<int32_t>(h->recorded.size());
+  if (scan_ms) *scan_ms = static_cast<float>(scan);
+  if (fused_ms) *fused_ms = static_cast<float>(fused);
+  h->recorded.clear();
+  return st;
+}
+
+int infini_attn_destroy(infini_attn_t *h) {
+  if (!h) return INFINI_ATTN_OK;
+  int st = INFINI_ATTN_OK;
+  {
+    DeviceGuard guard(h->desc.device);
+    for (auto *list : {&h->recorded, &h->spare})
+      for (TimedCall &tc : *list)
+        for (hipEvent_t ev : tc.ev) (void)hipEventDestroy(ev);
+  }
+  if (h->ws) {
+    DeviceGuard guard(h->desc.device);
+    if (guard.err != hipSuccess || hipFree(h->ws) != hipSuccess) st = INFINI_ATTN_ERR_HIP;
+  }
+  delete h;
+  return st;
+}
+
+const char *infini_attn_strerror(int status) {
+  switch (status) {
+    case INFINI_ATTN_OK: return "ok";
+    case INFINI_ATTN_ERR_INVALID: return "invalid argument";
+    case INFINI_ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case INFINI_ATTN_ERR_HIP: return "HIP runtime or launch failure";
+    case INFINI_ATTN_ERR_OOM: return "out of device memory";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

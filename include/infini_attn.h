@@ -1,0 +1,147 @@
+/*
+ * infini_attn.h — C ABI of the gfx950 Infini-attention forward library.
+ *
+ * The operation (per batch element b and query head h, reading kv head
+ * j = h / (Hq / Hkv)):
+ *   the sequence of L rows is cut into segments of seg_len rows, the last one
+ *   possibly shorter ([HF-repro] "Infini-Attention メカニズム", step
+ *   Segmentation). For every segment s, in order:
+ *     A_dot = softmax(mask(Q_s K_s^T / sqrt(d_k))) V_s, causal inside the
+ *             segment only (step Local Attention; [LNCB-review] "基本アイデア");
+ *     A_mem = sigma(Q_s) M_{s-1} / (sigma(Q_s) z_{s-1} + eps), row by row, with
+ *             sigma = ELU + 1 (step Memory Retrieval; [LNCB-review]
+ *             "メモリの読み出し");
+ *     out_s = g_h A_mem + (1 - g_h) A_dot, g_h = 1 / (1 + exp(-beta_h)) (step
+ *             Integration; [LNCB-review] "長期情報と短期情報の統合");
+ *   then, per kv head, the segment is written into the memory (step Memory
+ *   Update; [LNCB-review] "メモリの更新"):
+ *     LINEAR: M_s = M_{s-1} + sigma(K_s)^T V_s
+ *     DELTA:  M_s = M_{s-1} + sigma(K_s)^T (V_s - sigma(K_s) M_{s-1} /
+ *                                              (sigma(K_s) z_{s-1} + eps))
+ *     both:   z_s = z_{s-1} + sum over the segment's rows of sigma(k)
+ *   and only (M, z) passes to the next segment (step State Transfer).
+ *
+ * Pages cited: [HF-repro] "Hugging Face Infini-Attention 再現分析";
+ * [LNCB-review] the abeam-guide review of "Leave No Context Behind: Efficient
+ * Infinite Context Transformers with Infini-attention".
+ *
+ * Conventions shared by every entry point:
+ *   - Every function returns an int status: INFINI_ATTN_OK (0) or a negative
+ *     INFINI_ATTN_ERR_* code. No C++ exception crosses this boundary.
+ *   - Device pointers point to device memory of the handle's device. The caller
+ *     owns every tensor; the library owns only its handle and the workspace
+ *     inside it.
+ *   - Work is enqueued on the handle's stream and the call returns without
+ *     waiting for it. Errors raised by the kernels themselves surface at the
+ *     caller's next synchronisation. A handle must not be used by two host
+ *     threads or two streams at once.
+ */
+#ifndef INFINI_ATTN_H
+#define INFINI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define INFINI_ATTN_OK 0
+#define INFINI_ATTN_ERR_INVALID (-1)     /* null/misaligned pointer, bad size, mode or dtype */
+#define INFINI_ATTN_ERR_UNSUPPORTED (-2) /* valid request this build has no kernel for */
+#define INFINI_ATTN_ERR_HIP (-3)         /* HIP runtime or launch failure, no device */
+#define INFINI_ATTN_ERR_OOM (-4)         /* workspace allocation failed */
+
+/* Storage type of q, k, v and out. beta, M and z are always fp32. */
+#define INFINI_ATTN_F32 0
+#define INFINI_ATTN_BF16 1
+
+/* Memory update rule ([LNCB-review] "メモリの更新"). */
+#define INFINI_ATTN_LINEAR 0
+#define INFINI_ATTN_DELTA 1
+
+typedef struct infini_attn_desc {
+  int32_t batch;      /* B >= 1 */
+  int32_t n_q_heads;  /* Hq >= 1, a multiple of n_kv_heads */
+  int32_t n_kv_heads; /* Hkv >= 1; query head h reads kv head h / (Hq / Hkv) */
+  int32_t seq_len;    /* L >= 1 rows per call */
+  int32_t d_k;        /* key / query width; supported: 32, 64, 128 */
+  int32_t d_v;        /* value width; this build requires d_v == d_k */
+  int32_t dtype;      /* INFINI_ATTN_F32 or INFINI_ATTN_BF16 */
+  float eps;          /* retrieval denominator offset, > 0 and finite (1e-6 typical) */
+  void *stream;       /* hipStream_t to enqueue on; NULL = the null stream */
+  int32_t device;     /* HIP device ordinal of every pointer passed to forward */
+} infini_attn_desc;
+
+typedef struct infini_attn_handle infini_attn_t;
+
+/*
+ * Validate a descriptor and the per-call arguments of infini_attn_forward
+ * without touching any device. Returns OK, ERR_INVALID or ERR_UNSUPPORTED.
+ * Pure host code: safe to call on a machine with no GPU.
+ */
+int infini_attn_check(const infini_attn_desc *desc, int32_t seg_len, int32_t update_mode);
+
+/*
+ * Bytes of device workspace a handle with this descriptor allocates for a
+ * forward call with this segment length: the per-segment state snapshots
+ * (M_{s-1}, z_{s-1}) that the segment-scan kernel writes and the fused
+ * attention kernel reads. Writes the size to *bytes. Host only.
+ */
+int infini_attn_workspace_size(const infini_attn_desc *desc, int32_t seg_len, size_t *bytes);
+
+/*
+ * Create a handle for one problem shape. Validates *desc, makes desc->device
+ * current, and records the stream. *h receives the handle, or NULL on error.
+ * The workspace is allocated by the first forward call that needs it and
+ * grown (never shrunk) by later calls with more segments.
+ * Errors: ERR_INVALID (null h/desc or bad field), ERR_UNSUPPORTED, ERR_HIP
+ * (no device, or the device cannot be selected).
+ */
+int infini_attn_create(infini_attn_t **h, const infini_attn_desc *desc);
+
+/*
+ * One forward pass over seq_len rows.
+ *   q    [B, Hq,  L, d_k]  dtype, contiguous, 16-byte aligned (device)
+ *   k    [B, Hkv, L, d_k]  dtype, contiguous, 16-byte aligned (device)
+ *   v    [B, Hkv, L, d_v]  dtype, contiguous, 16-byte aligned (device)
+ *   beta [Hq]              fp32, one gate parameter per query head (device)
+ *   M    [B, Hkv, d_k, d_v] fp32 in/out (device): M_0 on entry, M_S on exit
+ *   z    [B, Hkv, d_k]      fp32 in/out (device): z_0 on entry, z_S on exit
+ *   seg_len     >= 1 rows per segment; S = ceil(L / seg_len) segments
+ *   update_mode INFINI_ATTN_LINEAR or INFINI_ATTN_DELTA
+ *   out  [B, Hq, L, d_v]   dtype (device), written; must not overlap any input
+ * Passing (M_S, z_S) back with the next L rows continues the same stream of
+ * segments when the previous L was a multiple of seg_len.
+ * Errors: ERR_INVALID (null or misaligned pointer, seg_len < 1, bad mode),
+ * ERR_OOM (workspace), ERR_HIP (launch failure). After an error M and z are
+ * unspecified.
+ */
+int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const void *v,
+                        const float *beta, float *M, float *z, int32_t seg_len,
+                        int32_t update_mode, void *out);
+
+/*
+ * Per-kernel timing for profiling. With timing enabled, every forward call
+ * records HIP events on the handle's stream around its segment-scan kernel
+ * and its fused attention kernel. infini_attn_get_timing waits for the
+ * recorded events, returns the number of timed calls since the previous get
+ * and the summed durations (milliseconds) of the two kernels over those
+ * calls, and clears the record. Any output pointer may be NULL.
+ * Errors: ERR_INVALID (null handle), ERR_HIP (event failure).
+ */
+int infini_attn_set_timing(infini_attn_t *h, int32_t enable);
+int infini_attn_get_timing(infini_attn_t *h, int32_t *calls, float *scan_ms, float *fused_ms);
+
+/* Free the workspace and the handle. destroy(NULL) returns OK. */
+int infini_attn_destroy(infini_attn_t *h);
+
+/* Static, human-readable text for a status code. */
+const char *infini_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFINI_ATTN_H */
