@@ -1,0 +1,246 @@
+"""Throughput of the Infini-attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode delta|linear]
+
+One step is one forward pass of the whole path (segment scan, then the fused
+per-segment kernel) over one batch of synthetic, seeded input already resident
+in HBM. Prints ONE JSON line on stdout; progress goes to stderr.
+
+Default workload: the Llama-3-8B attention shape (B=1, 32 query heads, 8 kv
+heads, d=128, segments of 2048 rows, L=32768, bf16 storage).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Infini-attn fwd tokens/sec on 1 MI355X; % MFMA bf16 peak; HBM GB/s"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 bf16 FLOP/clk x 2.4 GHz (dense)
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_bf16_llama3_8b_gqa_traffic.txt")
+FUSED_SRC = os.path.join(ROOT, "compressive_memory_transformers_segment_amd", "csrc",
+                         "fused_bf16.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def segment_rows(L: int, N: int):
+    return [min(N, L - a) for a in range(0, L, N)]
+
+
+def work_counts(w, mode: str) -> dict:
+    """Algorithmic FLOPs and bytes of one forward pass.
+
+    Fused kernel, per (query head, segment of n rows): local causal attention
+    over n(n+1)/2 (query, key) pairs, 2d FLOPs each for Q K^T and for P V,
+    plus 2 n d^2 for the retrieval sigma(Q) M. Scan, per (kv head, segment):
+    2 n d^2 (sigma(K)^T V) for the linear rule, 4 n d^2 with the delta rule's
+    retrieval. Softmax, feature-map and normaliser arithmetic is not counted.
+    Bytes: Q, K, V read once and out written once (storage dtype), plus the
+    fp32 state read and written once.
+    """
+    d = w.d
+    el = 2 if w.dtype == "bf16" else 4
+    rows = segment_rows(w.seq_len, w.seg_len)
+    attn = sum(4 * d * n * (n + 1) // 2 for n in rows)
+    retr = sum(2 * n * d * d for n in rows)
+    fused = w.batch * w.n_q_heads * (attn + retr)
+    per_upd = (4 if mode == "delta" else 2) * d * d
+    scan = w.batch * w.n_kv_heads * sum(per_upd * n for n in rows)
+    qo = 2 * w.batch * w.n_q_heads * w.seq_len * d * el
+    kv = 2 * w.batch * w.n_kv_heads * w.seq_len * d * el
+    state = 2 * w.batch * w.n_kv_heads * (d * d + d) * 4
+    return dict(fused_flops=fused, scan_flops=scan, total_flops=fused + scan,
+                bytes=qo + kv + state, fused_bytes=qo + kv)
+
+
+def stored_traffic(fused_launch_bytes: float):
+    """HBM traffic of the fused kernel from committed rocprofv3 counter runs,
+    or None when the counters were taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    src_hash = hashlib.sha256(open(FUSED_SRC, "rb").read()).hexdigest()[:16]
+    if kv.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp, mode: str, budget_s: float) -> dict:
+    """The fp64 oracle on the host cores, on the first segments of the same
+    workload (all batch entries and heads), scaled to tokens/s."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    N = w.seg_len
+
+    def run(n_seg: int) -> float:
+        L = min(n_seg * N, w.seq_len)
+        q = synth.as_f64(inp["q"][:, :, :L], w.dtype)
+        k = synth.as_f64(inp["k"][:, :, :L], w.dtype)
+        v = synth.as_f64(inp["v"][:, :, :L], w.dtype)
+        t0 = time.perf_counter()
+        oracle.infini_attention(q, k, v, inp["beta"].astype(np.float64),
+                                inp["M0"].astype(np.float64), inp["z0"].astype(np.float64), N,
+                                mode, float(inp["eps"]))
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    n = max(1, min(w.n_segments, int(budget_s / max(t1, 1e-3))))
+    if n > 1:
+        t = run(n)
+    else:
+        n, t = 1, t1
+    tokens = w.batch * min(n * N, w.seq_len)
+    return {"value": tokens / t, "unit": "tokens/s", "cores": blas_threads, "kind": "oracle",
+            "sample": f"first {n} of {w.n_segments} segments ({tokens} tokens, all "
+                      f"{w.batch * w.n_q_heads} query heads), {mode} rule, fp64 numpy; "
+                      f"{t:.2f} s; host cpus visible: {len(os.sched_getaffinity(0))}"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b_gqa")
+    ap.add_argument("--mode", default="delta", choices=["linear", "delta"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the Infini-attention forward here is a single-GPU kernel pair; heads would "
+              "shard across GPUs with no communication, see the design notes).",
+              file=sys.stderr)
+        return 2
+    rank = int(os.environ.get("RANK", "0"))
+
+    import numpy as np
+    import torch
+
+    import compressive_memory_transformers_segment_amd as ia
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        log("note: fp32 workload; roofline is still quoted against the bf16 MFMA peak")
+    ia.load()
+    log(f"generating {w.describe()}")
+    t0 = time.perf_counter()
+    inp = synth.generate(w)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, k, v = up(inp["q"]), up(inp["k"]), up(inp["v"])
+    beta = torch.from_numpy(inp["beta"]).to(dev)
+    M = torch.from_numpy(inp["M0"]).to(dev)
+    z = torch.from_numpy(inp["z0"]).to(dev)
+    out = torch.empty((w.batch, w.n_q_heads, w.seq_len, w.d), dtype=q.dtype, device=dev)
+    h = ia.handle_for(q, k, w.eps)
+
+    def step():
+        ia.forward(q, k, v, beta, M, z, w.seg_len, args.mode, out=out, eps=w.eps)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ia.infini_attn_set_timing(h, True)
+    ia.infini_attn_get_timing(h)  # clear
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    calls, scan_ms, fused_ms = ia.infini_attn_get_timing(h)
+    ia.infini_attn_set_timing(h, False)
+    assert calls == args.steps, (calls, args.steps)
+    if not bool(torch.isfinite(out.float()).all()):
+        log("ERROR: non-finite output")
+        return 1
+
+    wc = work_counts(w, args.mode)
+    ms_step = elapsed * 1e3 / args.steps
+    tokens = w.batch * w.seq_len
+    fused_avg_s = fused_ms / calls / 1e3
+    scan_avg_s = scan_ms / calls / 1e3
+    achieved = wc["fused_flops"] / fused_avg_s / 1e12
+    traffic = stored_traffic(wc["fused_bytes"])
+    result = {
+        "metric": METRIC,
+        "value": tokens * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1)/sqrt(d) q, k, v; see synth/)",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "d": w.d, "seg_len": w.seg_len,
+                   "seq_len": w.seq_len, "segments": w.n_segments, "update": args.mode},
+        "tflops_algorithmic": wc["total_flops"] * args.steps / elapsed / 1e12,
+        "mfma_bf16_peak_frac": wc["total_flops"] * args.steps / elapsed / 1e12 / PEAK_BF16_TFLOPS,
+        "hbm_gbs_algorithmic": wc["bytes"] * args.steps / elapsed / 1e9,
+        "kernels_ms": {"segment_scan": scan_avg_s * 1e3, "fused_attention": fused_avg_s * 1e3},
+        "roofline": {
+            "kernel": "fused_bf16_kernel<128>" if w.d == 128 else f"fused kernel d={w.d}",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "flops_per_launch": wc["fused_flops"],
+        },
+    }
+    if rank == 0 and not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host cores")
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.mode, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    ia.release_handles()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
