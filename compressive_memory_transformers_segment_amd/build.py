@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libinfini_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["infini_attn.hip", "segment_scan.hip", "fused_bf16.hip", "fused_f32.hip"]
+SOURCES = ["infini_attn.hip", "segment_scan.hip", "segment_scan_mfma.hip", "fused_bf16.hip",
+           "fused_f32.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -26,6 +26,15 @@
 //     tile are issued before the current tile's MFMAs.
 //   * Causal skipping: a query tile visits key tiles up to its diagonal only;
 //     a wave skips tiles entirely in its future and masks only diagonal tiles.
+//   * Two LDS buffers: the next tile is written into the idle buffer while the
+//     current one is consumed, so each key tile costs one barrier.
+//   * Online softmax with a lazy rescale: the running max m of a row moves
+//     (and O, l are rescaled) only when a tile's max exceeds m by more than
+//     kLazy (log2 units), so probabilities stay <= 2^kLazy and most tiles skip
+//     the rescale. The 1/sqrt(d) scale is folded into the exponent's FMA.
+//   * Block order is remapped so that consecutive work items share an XCD
+//     (blocks are dealt round-robin to the 8 XCDs): the query heads that read
+//     one kv head land on one XCD and share its L2.
 //   * Epilogue: the pre-segment snapshot M^T (bf16, [d_v][d_k]) is staged in
 //     LDS and multiplied with sigma(Q) (computed from the Q registers) on MFMA;
 //     the denominator sigma(Q).z is a per-lane dot product plus one exchange.
@@ -39,6 +48,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBM = 128;  // query rows per workgroup (32 per wave)
 constexpr int kBN = 64;   // key rows per tile
+constexpr float kLazy = 8.f;  // rescale threshold, log2 units
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -53,7 +64,8 @@ struct Tile {
   static constexpr int MSTR = D + 8;    // staged M^T row stride in bf16
   static constexpr int KCH = kBN * D / 8 / kThreads;  // 16-byte K chunks per thread
   static constexpr int VC = D / 16;                   // V columns per thread (x 4 rows)
-  static constexpr int LDS_ATT = kBN * KSTR + D * VSTR;
+  static constexpr int BUF = kBN * KSTR + D * VSTR;  // one K tile + one V^T tile
+  static constexpr int LDS_ATT = 2 * BUF;
   static constexpr int LDS_MEM = D * MSTR;
   static constexpr int LDS = LDS_ATT > LDS_MEM ? LDS_ATT : LDS_MEM;
 };
@@ -78,23 +90,24 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     const uint16_t *__restrict__ v, const float *__restrict__ beta,
     const float *__restrict__ z_pre, const uint16_t *__restrict__ mt_pre,
     uint16_t *__restrict__ out, int Hq, int Hkv, int L, int N, int S, int n_qt, float eps,
-    float scale_log2) {
+    float scale_log2, int xcd_chunk) {
   using TL = Tile<D>;
   constexpr int NT = D / 16;  // k-steps over d
   constexpr int ND = D / 32;  // 32-row d tiles of O^T
   __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS];
   __shared__ float sZ[D];
-  uint16_t *sK = smem;
-  uint16_t *sVt = smem + kBN * TL::KSTR;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
 
-  // Longest query tiles (most key tiles under the causal mask) first.
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x);
-  const int s = blockIdx.y;
-  const int bhq = blockIdx.z;
+  // Work item: dispatch index -> XCD-contiguous order (when the grid divides
+  // evenly), then (query tile, segment, batch * head) with the query tile
+  // fastest; longest query tiles (most key tiles under the mask) first.
+  int wi = blockIdx.x;
+  if (xcd_chunk > 0) wi = (wi % kXcds) * xcd_chunk + wi / kXcds;
+  const int qt = n_qt - 1 - wi % n_qt;
+  const int s = (wi / n_qt) % S;
+  const int bhq = wi / (n_qt * S);
   const int b = bhq / Hq, h = bhq - b * Hq;
   const int hk = h / (Hq / Hkv);
   const int a = s * N;
@@ -155,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     }
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&](uint16_t *sK, uint16_t *sVt) {
 #pragma unroll
     for (int r = 0; r < TL::KCH; ++r) {
       const int c = tid + kThreads * r;
@@ -175,11 +188,14 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   };
 
   load_tile(a);
+  store_tile(smem, smem + kBN * TL::KSTR);
+  __syncthreads();
+  int buf = 0;
   for (int kv0 = a; kv0 < kv_end; kv0 += kBN) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (kv0 + kBN < kv_end) load_tile(kv0 + kBN);
+    const uint16_t *sK = smem + buf * TL::BUF;
+    const uint16_t *sVt = sK + kBN * TL::KSTR;
+    const bool has_next = kv0 + kBN < kv_end;
+    if (has_next) load_tile(kv0 + kBN);  // global loads in flight during the MFMAs
 
     if (wave_live && kv0 <= qw + 31) {
       // S^T tile pair: rows = keys kv0 + 32T + ..., columns = this wave's queries.
@@ -194,26 +210,34 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
           st[T] = mfma32(as_bf16x8(ka), as_bf16x8(qf[t]), st[T]);
         }
       }
-      // Scale to the log2 domain; mask future keys and keys past the segment end.
-      const bool diag = (kv0 + kBN - 1 > qw) || (kv0 + kBN > e);
+      // Mask future keys and keys past the segment end (diagonal tiles only).
+      if ((kv0 + kBN - 1 > qw) || (kv0 + kBN > e)) {
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kvi = kv0 + 32 * T + (i >> 2) * 8 + 4 * g + (i & 3);
+            if (kvi > qrow || kvi >= e) st[T][i] = -INFINITY;
+          }
+        }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = st[T][i] * scale_log2;
-          if (diag) {
-            const int kvi = kv0 + 32 * T + (i >> 2) * 8 + 4 * g + (i & 3);
-            if (kvi > qrow || kvi >= e) x = -INFINITY;
-          }
-          st[T][i] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(st[T][i], st[T][i + 1]));
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);  // finite: the segment's first key is always visible
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;  // finite: key a is always visible
+      const bool grow = mx > m + kLazy;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 1 where m stays
+        m = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+      }
+      const float neg_m = -m;
       float psum = 0.f;
       u32x4 pb[2][2];
 #pragma unroll
@@ -223,17 +247,17 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
           uint32_t pw[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const float p0 = __builtin_amdgcn_exp2f(st[T][8 * u + 2 * jj] - m_new);
-            const float p1 = __builtin_amdgcn_exp2f(st[T][8 * u + 2 * jj + 1] - m_new);
+            const float p0 =
+                __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][8 * u + 2 * jj], scale_log2, neg_m));
+            const float p1 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(st[T][8 * u + 2 * jj + 1], scale_log2, neg_m));
             psum += p0 + p1;
             pw[jj] = pack_bf16x2(p0, p1);
           }
           pb[T][u] = u32x4{pw[0], pw[1], pw[2], pw[3]};
         }
       }
-      lsum = lsum * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+      lsum += psum;
       // O^T += V^T P^T. Slot j of lane group g is key 16u + 8(j/4) + 4g + j%4 of
       // the 32-key half T, matching the S^T result layout.
 #pragma unroll
@@ -251,6 +275,13 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
         }
       }
     }
+    if (has_next) {
+      // The idle buffer was last read before the previous barrier.
+      uint16_t *nK = smem + (buf ^ 1) * TL::BUF;
+      store_tile(nK, nK + kBN * TL::KSTR);
+    }
+    __syncthreads();
+    buf ^= 1;
   }
 
   // ---- retrieval from the pre-segment snapshot and the gate ----
@@ -321,11 +352,13 @@ hipError_t launch_t(const Geometry &g, const uint16_t *q, const uint16_t *k, con
                     const float *beta, const Workspace &ws, uint16_t *out, hipStream_t stream) {
   const int rows = g.N < g.L ? g.N : g.L;
   const int n_qt = (rows + kBM - 1) / kBM;
-  dim3 grid(n_qt, g.S, g.B * g.Hq);
+  const long long nblk = static_cast<long long>(n_qt) * g.S * g.B * g.Hq;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int xcd_chunk = (nblk % kXcds == 0) ? static_cast<int>(nblk / kXcds) : 0;
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
-  fused_bf16_kernel<D><<<grid, kThreads, 0, stream>>>(q, k, v, beta, ws.z_pre, ws.mt_pre_bf16,
-                                                      out, g.Hq, g.Hkv, g.L, g.N, g.S, n_qt,
-                                                      g.eps, scale_log2);
+  fused_bf16_kernel<D><<<dim3(static_cast<unsigned>(nblk)), kThreads, 0, stream>>>(
+      q, k, v, beta, ws.z_pre, ws.mt_pre_bf16, out, g.Hq, g.Hkv, g.L, g.N, g.S, n_qt, g.eps,
+      scale_log2, xcd_chunk);
   return hipGetLastError();
 }
 

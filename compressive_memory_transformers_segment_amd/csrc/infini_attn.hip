@@ -54,15 +54,32 @@ int check_desc(const infini_attn_desc *d) {
 
 int n_segments(int L, int N) { return L == 0 ? 0 : (L + N - 1) / N; }
 
-// Workspace layout (each part 256-byte aligned):
+// Workspace layout (each part 256-byte aligned), in this order:
 //   z_pre  [B*Hkv][S+1][D] fp32   (slot S receives the final z)
 //   mt_pre [B*Hkv][S][D][D]       fp32 or bf16 by storage type
-size_t ws_parts(const infini_attn_desc *d, int S, size_t *z_bytes) {
+//   dz     [B*Hkv][S][P][D] fp32  (bf16 storage only; P = z_parts(N) row ranges)
+//   gh     [B*Hkv][S][2][D][D] fp32 (bf16 storage only)
+struct WsLayout {
+  size_t z, mt, dz, gh, total;
+};
+
+// Row ranges per segment for the sigma(k) column sums: about 512 rows each.
+int z_parts(int N) {
+  const int p = (N + 511) / 512;
+  return p < 1 ? 1 : (p > 8 ? 8 : p);
+}
+
+WsLayout ws_layout(const infini_attn_desc *d, int S, int N) {
   const size_t heads = static_cast<size_t>(d->batch) * d->n_kv_heads;
   const size_t D = static_cast<size_t>(d->d_k);
-  *z_bytes = round_up(heads * (S + 1) * D * sizeof(float));
-  const size_t el = d->dtype == INFINI_ATTN_F32 ? sizeof(float) : sizeof(uint16_t);
-  return *z_bytes + round_up(heads * S * D * D * el);
+  const bool bf16 = d->dtype == INFINI_ATTN_BF16;
+  WsLayout w;
+  w.z = round_up(heads * (S + 1) * D * sizeof(float));
+  w.mt = round_up(heads * S * D * D * (bf16 ? sizeof(uint16_t) : sizeof(float)));
+  w.dz = bf16 ? round_up(heads * S * z_parts(N) * D * sizeof(float)) : 0;
+  w.gh = bf16 ? round_up(heads * S * 2 * D * D * sizeof(float)) : 0;
+  w.total = w.z + w.mt + w.dz + w.gh;
+  return w;
 }
 
 int hip_status(hipError_t e) {
@@ -105,8 +122,7 @@ int infini_attn_workspace_size(const infini_attn_desc *desc, int32_t seg_len, si
   if (!bytes) return INFINI_ATTN_ERR_INVALID;
   const int st = infini_attn_check(desc, seg_len, INFINI_ATTN_LINEAR);
   if (st != INFINI_ATTN_OK) return st;
-  size_t zb = 0;
-  *bytes = ws_parts(desc, n_segments(desc->seq_len, seg_len), &zb);
+  *bytes = ws_layout(desc, n_segments(desc->seq_len, seg_len), seg_len).total;
   return INFINI_ATTN_OK;
 }
 
@@ -157,8 +173,8 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
   g.S = n_segments(d.seq_len, seg_len);
   g.eps = d.eps;
 
-  size_t z_bytes = 0;
-  const size_t need = ws_parts(&d, g.S, &z_bytes);
+  const WsLayout lay = ws_layout(&d, g.S, g.N);
+  const size_t need = lay.total;
   if (need > h->ws_bytes) {
     if (h->ws) {
       // hipFree waits for work still using the old buffer.
@@ -173,11 +189,15 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
     h->ws_bytes = need;
   }
   ia::Workspace ws;
-  ws.z_pre = static_cast<float *>(h->ws);
-  void *mt = static_cast<char *>(h->ws) + z_bytes;
+  char *base = static_cast<char *>(h->ws);
+  ws.z_pre = reinterpret_cast<float *>(base);
+  void *mt = base + lay.z;
   const bool bf16 = d.dtype == INFINI_ATTN_BF16;
   ws.mt_pre_f32 = bf16 ? nullptr : static_cast<float *>(mt);
   ws.mt_pre_bf16 = bf16 ? static_cast<uint16_t *>(mt) : nullptr;
+  ws.dz = bf16 ? reinterpret_cast<float *>(base + lay.z + lay.mt) : nullptr;
+  ws.z_parts = z_parts(g.N);
+  ws.gh = bf16 ? reinterpret_cast<float *>(base + lay.z + lay.mt + lay.dz) : nullptr;
 
   TimedCall tc{};
   if (h->timing) {
@@ -195,8 +215,14 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
     h->recorded.push_back(tc);
     if (hipEventRecord(tc.ev[0], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
   }
-  hipError_t e = ia::launch_segment_scan(g, bf16, k, v, M, z, update_mode == INFINI_ATTN_DELTA,
-                                         ws, h->stream);
+  const int delta = update_mode == INFINI_ATTN_DELTA;
+  hipError_t e =
+      bf16 ? ia::launch_segment_scan_bf16(g, static_cast<const uint16_t *>(k),
+                                          static_cast<const uint16_t *>(v), M, z, delta, ws,
+                                          h->stream)
+           : ia::launch_segment_scan_f32(g, static_cast<const float *>(k),
+                                         static_cast<const float *>(v), M, z, delta, ws,
+                                         h->stream);
   if (e != hipSuccess) return hip_status(e);
   if (h->timing && hipEventRecord(tc.ev[1], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
   if (bf16) {

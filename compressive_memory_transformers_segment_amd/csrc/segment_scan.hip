@@ -1,5 +1,7 @@
-// Segment scan: the only state that crosses segments is (M, z); this kernel
-// carries it in fp32 through all S segments of every (batch, kv head).
+// Segment scan for fp32 storage: the only state that crosses segments is
+// (M, z); this kernel carries it in fp32 through all S segments of every
+// (batch, kv head) with fp32 VALU arithmetic throughout (the precision path;
+// bf16 storage uses the MFMA scan).
 //
 //   [HF-repro] "Infini-Attention メカニズム", steps Memory Update and State
 //   Transfer; [LNCB-review] "メモリの更新" (outer-product write; delta rule).
@@ -126,32 +128,24 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
 }
 
 template <typename T, int D>
-hipError_t launch_scan_t(const Geometry &g, const void *k, const void *v, float *M, float *z,
+hipError_t launch_scan_t(const Geometry &g, const T *k, const T *v, float *M, const float *z,
                          int delta, const Workspace &ws, hipStream_t stream) {
   dim3 grid(D / kCB, g.B * g.Hkv);
   segment_scan_kernel<T, D><<<grid, kThreads, 0, stream>>>(
-      static_cast<const T *>(k), static_cast<const T *>(v), M, z, g.L, g.N, g.S, g.eps, delta,
+      k, v, M, z, g.L, g.N, g.S, g.eps, delta,
       ws.z_pre, ws.mt_pre_f32, ws.mt_pre_bf16);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_segment_scan(const Geometry &g, bool bf16_inputs, const void *k, const void *v,
-                               float *M, float *z, int delta, const Workspace &ws,
-                               hipStream_t stream) {
-  if (bf16_inputs) {
-    switch (g.D) {
-      case 32: return launch_scan_t<uint16_t, 32>(g, k, v, M, z, delta, ws, stream);
-      case 64: return launch_scan_t<uint16_t, 64>(g, k, v, M, z, delta, ws, stream);
-      case 128: return launch_scan_t<uint16_t, 128>(g, k, v, M, z, delta, ws, stream);
-    }
-  } else {
-    switch (g.D) {
-      case 32: return launch_scan_t<float, 32>(g, k, v, M, z, delta, ws, stream);
-      case 64: return launch_scan_t<float, 64>(g, k, v, M, z, delta, ws, stream);
-      case 128: return launch_scan_t<float, 128>(g, k, v, M, z, delta, ws, stream);
-    }
+hipError_t launch_segment_scan_f32(const Geometry &g, const float *k, const float *v, float *M,
+                                   const float *z, int delta, const Workspace &ws,
+                                   hipStream_t stream) {
+  switch (g.D) {
+    case 32: return launch_scan_t<float, 32>(g, k, v, M, z, delta, ws, stream);
+    case 64: return launch_scan_t<float, 64>(g, k, v, M, z, delta, ws, stream);
+    case 128: return launch_scan_t<float, 128>(g, k, v, M, z, delta, ws, stream);
   }
   return hipErrorInvalidValue;
 }

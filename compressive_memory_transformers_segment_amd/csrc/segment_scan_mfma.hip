@@ -1,0 +1,415 @@
+// Segment scan for bf16 storage on MFMA.
+//
+// Memory update per segment s ([HF-repro] "Infini-Attention メカニズム", steps
+// Memory Update and State Transfer; [LNCB-review] "メモリの更新"):
+//   LINEAR: M_s = M_{s-1} + H_s
+//   DELTA:  M_s = M_{s-1} + sigma(K_s)^T (V_s - sigma(K_s) M_{s-1} / (sigma(K_s) z_{s-1} + eps))
+//             = (I - G_s) M_{s-1} + H_s
+//   with H_s = sigma(K_s)^T V_s and G_s = sigma(K_s)^T diag(1 / (sigma(K_s) z_{s-1} + eps)) sigma(K_s),
+//   z_s = z_{s-1} + sum_i sigma(k_i).
+// The delta rule is written in this affine form so that the only work left on
+// the sequential path is one d x d by d x d product per segment; everything
+// that touches the N x d segment data is done for all segments in parallel.
+//
+// Four launches, in stream order:
+//   zsum    (segment, head)     dz_s = column sums of sigma(K_s)             [VALU]
+//   zprefix (head)              z_{s-1} for every s, and z_S                  [VALU]
+//   gh      (segment, head)     G_s (delta only) and H_s, contraction over    [MFMA bf16]
+//                               the segment's rows, stored in MFMA fragment
+//                               order as fp32
+//   seq     (column tile, head) M_s = M_{s-1} - G_s M_{s-1} + H_s, fp32      [MFMA fp32]
+//                               state in registers; writes the bf16 snapshot
+//                               M_{s-1}^T the fused kernel reads, and M_S.
+//
+// Fragment order: a d x d matrix is stored as (D/32)^2 tiles of 32 x 32; tile
+// (rt, ct) holds, for MFMA-result register r and lane l, the element at row
+// 32 rt + kappa(r, l / 32), column 32 ct + l % 32, where
+// kappa(r, g) = 8 (r / 4) + 4 g + r % 4 is the 32x32 MFMA result row map.
+// Element index: ((rt * (D/32) + ct) * 16 + r) * 64 + l.
+
+#include "common.h"
+#include "launch.h"
+
+namespace ia {
+namespace {
+
+constexpr int kStr = 64 + 4;  // transposed staging row stride (bf16): 64 keys + 8-byte pad
+
+__device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int kappa(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// ---------------------------------------------------------------------------
+// zsum: dz[head][s][part][c] = sum over rows of part `part` of segment s of
+// sigma(k_ic). A segment is split into `parts` row ranges so that short
+// launches (few segments) still spread over the chip; zprefix adds the parts.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void zsum_kernel(const uint16_t *__restrict__ k,
+                                                   float *__restrict__ dz, int L, int N, int S,
+                                                   int parts) {
+  constexpr int CCH = D / 8;      // 16-byte chunks per row
+  constexpr int RG = 256 / CCH;   // rows in flight per pass
+  constexpr int UNROLL = 4;
+  __shared__ float red[RG][D + 1];
+  const int s = blockIdx.x / parts, part = blockIdx.x % parts;
+  const int head = blockIdx.y;
+  const int a = s * N, e = min(a + N, L);
+  const int span = (e - a + parts - 1) / parts;
+  const int pa = min(a + part * span, e), pe = min(pa + span, e);
+  const int t = threadIdx.x, cc = t % CCH, rg = t / CCH;
+  const uint16_t *kp = k + static_cast<size_t>(head) * L * D + cc * 8;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (int i = pa + rg; i < pe; i += RG * UNROLL) {
+    u32x4 w[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int row = i + u * RG;
+      w[u] = row < pe ? *reinterpret_cast<const u32x4 *>(kp + static_cast<size_t>(row) * D)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      if (i + u * RG < pe) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          acc[2 * jj] += elu1(lo_bf16(w[u][jj]));
+          acc[2 * jj + 1] += elu1(hi_bf16(w[u][jj]));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rg][cc * 8 + j] = acc[j];
+  __syncthreads();
+  if (t < D) {
+    float sum = 0.f;
+    for (int r = 0; r < RG; ++r) sum += red[r][t];
+    dz[((static_cast<size_t>(head) * S + s) * parts + part) * D + t] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// zprefix: z_pre[head][s] = z_{s-1} (the state before segment s), slot S = z_S
+// ---------------------------------------------------------------------------
+__global__ void zprefix_kernel(const float *__restrict__ z0, const float *__restrict__ dz,
+                               float *__restrict__ z_pre, int S, int D, int parts) {
+  const int head = blockIdx.x, t = threadIdx.x;
+  if (t >= D) return;
+  float z = z0[static_cast<size_t>(head) * D + t];
+  float *out = z_pre + static_cast<size_t>(head) * (S + 1) * D + t;
+  const float *d = dz + static_cast<size_t>(head) * S * parts * D + t;
+  for (int s = 0; s < S; ++s) {
+    out[static_cast<size_t>(s) * D] = z;
+    float seg = 0.f;
+    for (int p = 0; p < parts; ++p) seg += d[(static_cast<size_t>(s) * parts + p) * D];
+    z += seg;
+  }
+  out[static_cast<size_t>(S) * D] = z;
+}
+
+// ---------------------------------------------------------------------------
+// gh: [G_s | H_s] = sigma(K_s)^T [diag(1/den) sigma(K_s) | V_s], den_i = sigma(k_i).z_{s-1} + eps
+// ---------------------------------------------------------------------------
+template <int D, bool DELTA>
+__global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
+                                                 const uint16_t *__restrict__ v,
+                                                 const float *__restrict__ z_pre,
+                                                 float *__restrict__ gh, int L, int N, int S,
+                                                 float eps, int csplit) {
+  constexpr int ND = D / 32;
+  constexpr int CCH = D / 8;            // 8-column chunks per row
+  constexpr int ITEMS = 16 * CCH;       // staging items: 4 rows x 8 columns each
+  constexpr int NPAIR = DELTA ? 2 * ND : ND;  // (matrix, column tile) pairs
+  constexpr int PPW = (NPAIR + 3) / 4;        // pairs per wave
+  static_assert(ITEMS <= 256, "one staging item per thread");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * kStr];  // sigma(K)^T  [col][key]
+  __shared__ __attribute__((aligned(16))) uint16_t sWt[DELTA ? D * kStr : 8];  // (sigma(K)/den)^T
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * kStr];  // V^T
+  __shared__ float sZ[D];
+  __shared__ float sDenPart[CCH][64];
+  __shared__ float sRden[64];
+
+  // Column split: workgroup cs of `csplit` owns pairs [p_lo, p_hi); every
+  // workgroup stages the whole chunk.
+  const int s = blockIdx.x / csplit, cs = blockIdx.x % csplit;
+  const int p_lo = cs * NPAIR / csplit, p_hi = (cs + 1) * NPAIR / csplit;
+  const int head = blockIdx.y;
+  const int a = s * N, e = min(a + N, L);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const uint16_t *kp = k + static_cast<size_t>(head) * L * D;
+  const uint16_t *vp = v + static_cast<size_t>(head) * L * D;
+  if (tid < D) sZ[tid] = z_pre[(static_cast<size_t>(head) * (S + 1) + s) * D + tid];
+
+  f32x16 acc[PPW][ND];
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+    for (int rt = 0; rt < ND; ++rt) acc[pi][rt] = f32x16{};
+
+  const bool has = tid < ITEMS;
+  const int kg = tid & 15, cc = tid >> 4;  // rows 4 kg .. 4 kg + 3, columns 8 cc .. 8 cc + 7
+
+  // Register staging of one 64-row chunk (4 rows x 8 columns per item); the
+  // next chunk's loads are issued before the current chunk's MFMAs.
+  u32x4 kw[4], vv[4];
+  auto load_chunk = [&](int i0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = i0 + 4 * kg + r;
+      kw[r] = vv[r] = u32x4{0u, 0u, 0u, 0u};
+      if (has && row < e) {
+        kw[r] = *reinterpret_cast<const u32x4 *>(kp + static_cast<size_t>(row) * D + cc * 8);
+        vv[r] = *reinterpret_cast<const u32x4 *>(vp + static_cast<size_t>(row) * D + cc * 8);
+      }
+    }
+  };
+  load_chunk(a);
+
+  for (int i0 = a; i0 < e; i0 += 64) {
+    __syncthreads();  // previous chunk consumed; sZ visible
+    float kf[4][8];
+    if (has) {
+      uint32_t vw[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool in = i0 + 4 * kg + r < e;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          // rows past the segment end contribute nothing: sigma forced to 0
+          kf[r][2 * jj] = in ? elu1(lo_bf16(kw[r][jj])) : 0.f;
+          kf[r][2 * jj + 1] = in ? elu1(hi_bf16(kw[r][jj])) : 0.f;
+          vw[r][jj] = vv[r][jj];
+        }
+      }
+      if (DELTA) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float p = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p += kf[r][j] * sZ[cc * 8 + j];
+          sDenPart[cc][4 * kg + r] = p;
+        }
+      }
+      // transposed stores: one 8-byte write of 4 keys per column
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x2 kk2 = {pack_bf16x2(kf[0][j], kf[1][j]), pack_bf16x2(kf[2][j], kf[3][j])};
+        *reinterpret_cast<u32x2 *>(sKt + (cc * 8 + j) * kStr + 4 * kg) = kk2;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t r0 = vw[0][jj], r1 = vw[1][jj], r2 = vw[2][jj], r3 = vw[3][jj];
+        const u32x2 lo = {(r0 & 0xffffu) | (r1 << 16), (r2 & 0xffffu) | (r3 << 16)};
+        const u32x2 hi = {(r0 >> 16) | (r1 & 0xffff0000u), (r2 >> 16) | (r3 & 0xffff0000u)};
+        *reinterpret_cast<u32x2 *>(sVt + (cc * 8 + 2 * jj) * kStr + 4 * kg) = lo;
+        *reinterpret_cast<u32x2 *>(sVt + (cc * 8 + 2 * jj + 1) * kStr + 4 * kg) = hi;
+      }
+    }
+    if constexpr (DELTA) {
+      __syncthreads();
+      if (tid < 64) {
+        float den = eps;
+        for (int c = 0; c < CCH; ++c) den += sDenPart[c][tid];
+        sRden[tid] = 1.f / den;
+      }
+      __syncthreads();
+      if (has) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x2 w2 = {pack_bf16x2(kf[0][j] * sRden[4 * kg], kf[1][j] * sRden[4 * kg + 1]),
+                            pack_bf16x2(kf[2][j] * sRden[4 * kg + 2], kf[3][j] * sRden[4 * kg + 3])};
+          *reinterpret_cast<u32x2 *>(sWt + (cc * 8 + j) * kStr + 4 * kg) = w2;
+        }
+      }
+    }
+    __syncthreads();
+    if (i0 + 64 < e) load_chunk(i0 + 64);
+
+    // Contraction over the 64 keys of the chunk, 16 per MFMA. Slot j of lane
+    // group g is key kb + 8 (j / 4) + 4 g + j % 4 in both operands.
+#pragma unroll
+    for (int kb = 0; kb < 64; kb += 16) {
+      u32x4 av[ND];
+#pragma unroll
+      for (int rt = 0; rt < ND; ++rt) {
+        const uint16_t *p = sKt + (32 * rt + l32) * kStr + kb + 4 * g;
+        const u32x2 x0 = *reinterpret_cast<const u32x2 *>(p);
+        const u32x2 x1 = *reinterpret_cast<const u32x2 *>(p + 8);
+        av[rt] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+      }
+#pragma unroll
+      for (int pi = 0; pi < PPW; ++pi) {
+        const int pr = p_lo + w + 4 * pi;
+        if (pr < p_hi) {
+          const bool is_g = DELTA && pr < ND;
+          const int ct = pr % ND;
+          const uint16_t *src = is_g ? sWt : sVt;
+          const uint16_t *p = src + (32 * ct + l32) * kStr + kb + 4 * g;
+          const u32x2 x0 = *reinterpret_cast<const u32x2 *>(p);
+          const u32x2 x1 = *reinterpret_cast<const u32x2 *>(p + 8);
+          const u32x4 bv = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+          for (int rt = 0; rt < ND; ++rt) acc[pi][rt] = mfma_bf16(av[rt], bv, acc[pi][rt]);
+        }
+      }
+    }
+  }
+
+  // Store in fragment order: matrix 0 = G, matrix 1 = H.
+  float *base = gh + (static_cast<size_t>(head) * S + s) * 2 * D * D;
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi) {
+    const int pr = p_lo + w + 4 * pi;
+    if (pr < p_hi) {
+      const int mat = (DELTA && pr < ND) ? 0 : 1;
+      const int ct = pr % ND;
+#pragma unroll
+      for (int rt = 0; rt < ND; ++rt) {
+        float *f = base + static_cast<size_t>(mat) * D * D + ((rt * ND + ct) * 16) * 64 + lane;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) f[r * 64] = acc[pi][rt][r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// seq: the recurrence over segments for one 32-column tile of M.
+// Wave w holds rows 32 w .. 32 w + 31 of the tile in MFMA-result layout
+// (lane: column 32 jt + l % 32; register r: row 32 w + kappa(r, l / 32)).
+// ---------------------------------------------------------------------------
+template <int D, bool DELTA>
+__global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *__restrict__ gh,
+                                                           float *__restrict__ M,
+                                                           uint16_t *__restrict__ mt_pre,
+                                                           int S) {
+  constexpr int ND = D / 32;
+  constexpr int SMS = 40;  // sM row stride in floats: lane groups land on disjoint banks
+  __shared__ float sM[DELTA ? D * SMS : 1];
+  const int jt = blockIdx.x, head = blockIdx.y;
+  const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int j = 32 * jt + l32;
+  float *Mh = M + static_cast<size_t>(head) * D * D;
+
+  f32x16 m;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m[r] = Mh[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j];
+  if constexpr (DELTA) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sM[(32 * ct + kappa(r, g)) * SMS + l32] = m[r];
+    __syncthreads();
+  }
+
+  // Fragments of step s are loaded one step ahead, so their latency overlaps
+  // the previous step's MFMAs.
+  constexpr int NG = DELTA ? ND : 1;
+  float gcur[NG][16], hcur[16];
+  auto load_step = [&](int st, float (&gd)[NG][16], float (&hd)[16]) {
+    const float *ghs = gh + (static_cast<size_t>(head) * S + st) * 2 * D * D;
+    const float *hf = ghs + static_cast<size_t>(D) * D + ((ct * ND + jt) * 16) * 64 + lane;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hd[r] = hf[r * 64];
+    if constexpr (DELTA) {
+#pragma unroll
+      for (int kt = 0; kt < ND; ++kt) {
+        const float *gf = ghs + ((kt * ND + ct) * 16) * 64 + lane;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gd[kt][r] = gf[r * 64];
+      }
+    }
+  };
+  if (S > 0) load_step(0, gcur, hcur);
+
+  for (int s = 0; s < S; ++s) {
+    float gnext[NG][16], hnext[16];
+    if (s + 1 < S) load_step(s + 1, gnext, hnext);
+    // Snapshot of M_{s-1}, transposed, bf16: mt[j][c] for this lane's 16 rows c.
+    uint16_t *mt = mt_pre + (static_cast<size_t>(head) * S + s) * D * D +
+                   static_cast<size_t>(j) * D + 32 * ct + 4 * g;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const u32x2 pk = {pack_bf16x2(m[4 * q4], m[4 * q4 + 1]),
+                        pack_bf16x2(m[4 * q4 + 2], m[4 * q4 + 3])};
+      *reinterpret_cast<u32x2 *>(mt + 8 * q4) = pk;
+    }
+    if constexpr (DELTA) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kt = 0; kt < ND; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float bv = sM[(32 * kt + kappa(r, g)) * SMS + l32];
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(gcur[kt][r], bv, acc, 0, 0, 0);
+        }
+      }
+      __syncthreads();  // every wave has read M_{s-1} from sM
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        m[r] = m[r] - acc[r] + hcur[r];
+        sM[(32 * ct + kappa(r, g)) * SMS + l32] = m[r];
+      }
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m[r] += hcur[r];
+    }
+    if (s + 1 < S) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hcur[r] = hnext[r];
+#pragma unroll
+      for (int kt = 0; kt < NG; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gcur[kt][r] = gnext[kt][r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) Mh[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j] = m[r];
+}
+
+template <int D>
+hipError_t launch_d(const Geometry &g, const uint16_t *k, const uint16_t *v, float *M,
+                    const float *z, int delta, const Workspace &ws, hipStream_t stream) {
+  const int heads = g.B * g.Hkv;
+  const int parts = ws.z_parts;
+  // Few (segment, head) pairs: split each one's output tiles over two
+  // workgroups so that the launch still covers the chip.
+  const int csplit = (g.S * heads < 512) ? 2 : 1;
+  zsum_kernel<D><<<dim3(g.S * parts, heads), 256, 0, stream>>>(k, ws.dz, g.L, g.N, g.S, parts);
+  zprefix_kernel<<<heads, D, 0, stream>>>(z, ws.dz, ws.z_pre, g.S, D, parts);
+  if (delta) {
+    gh_kernel<D, true><<<dim3(g.S * csplit, heads), 256, 0, stream>>>(
+        k, v, ws.z_pre, ws.gh, g.L, g.N, g.S, g.eps, csplit);
+    seq_kernel<D, true><<<dim3(D / 32, heads), 64 * (D / 32), 0, stream>>>(ws.gh, M,
+                                                                          ws.mt_pre_bf16, g.S);
+  } else {
+    gh_kernel<D, false><<<dim3(g.S * csplit, heads), 256, 0, stream>>>(
+        k, v, ws.z_pre, ws.gh, g.L, g.N, g.S, g.eps, csplit);
+    seq_kernel<D, false><<<dim3(D / 32, heads), 64 * (D / 32), 0, stream>>>(ws.gh, M,
+                                                                           ws.mt_pre_bf16, g.S);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_segment_scan_bf16(const Geometry &g, const uint16_t *k, const uint16_t *v,
+                                    float *M, const float *z, int delta, const Workspace &ws,
+                                    hipStream_t stream) {
+  switch (g.D) {
+    case 32: return launch_d<32>(g, k, v, M, z, delta, ws, stream);
+    case 64: return launch_d<64>(g, k, v, M, z, delta, ws, stream);
+    case 128: return launch_d<128>(g, k, v, M, z, delta, ws, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ia
