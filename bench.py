@@ -134,6 +134,9 @@ def main(argv=None) -> int:
     ap.add_argument("--mode", default="delta", choices=["linear", "delta"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed run, copy this many bytes device-to-device (a plain "
+                         "copy kernel of known size, used to calibrate HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -237,6 +240,13 @@ def main(argv=None) -> int:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.mode, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = args.copy_bytes
     ia.release_handles()
     print(json.dumps(result), flush=True)
     return 0

@@ -23,6 +23,11 @@ SOURCES = ["infini_attn.hip", "segment_scan.hip", "segment_scan_mfma.hip", "fuse
            "fused_f32.hip"]
 ARCH = "gfx950"
 
+# Extra flags per source. The fused attention kernel runs with the IEEE mode
+# bit off, so that max/min on MFMA results need no NaN-quieting instructions
+# (NaN inputs are not supported on that path).
+FILE_FLAGS = {"fused_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
@@ -59,8 +64,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             objs.append(obj)
-            cmds.append([hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
-                         os.path.join(CSRC, src), "-o", obj])
+            cmds.append([hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC,
+                         "-c", os.path.join(CSRC, src), "-o", obj])
         with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
             for out in ex.map(_run, cmds):
                 if verbose and out.strip():

@@ -146,24 +146,38 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   const int v_kg = tid & 15;  // 4-row key group
   const int v_cc = tid >> 4;  // VC-column chunk
 
+  // Per-thread element offsets of the K chunks and V rows it stages.
+  int koff[TL::KCH];
+#pragma unroll
+  for (int r = 0; r < TL::KCH; ++r) {
+    const int c = tid + kThreads * r;
+    koff[r] = (c / (D / 8)) * D + (c % (D / 8)) * 8;
+  }
+  const int voff = 4 * v_kg * D + v_cc * TL::VC;
+
   auto load_tile = [&](int kv0) {
+    const uint16_t *kt = kp + static_cast<size_t>(kv0) * D;
+    const uint16_t *vt = vp + static_cast<size_t>(kv0) * D + voff;
+    if (kv0 + kBN <= e) {  // whole tile inside the segment: no per-row guards
 #pragma unroll
-    for (int r = 0; r < TL::KCH; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / (D / 8), col8 = c % (D / 8);
-      kreg[r] = (kv0 + row < e)
-                    ? *reinterpret_cast<const u32x4 *>(kp + static_cast<size_t>(kv0 + row) * D +
-                                                      col8 * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
-    }
+      for (int r = 0; r < TL::KCH; ++r) kreg[r] = *reinterpret_cast<const u32x4 *>(kt + koff[r]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = kv0 + 4 * v_kg + r;
-      if (row < e) {
-        load_cols<TL::VC>(vp + static_cast<size_t>(row) * D + v_cc * TL::VC, vreg[r]);
-      } else {
+      for (int r = 0; r < 4; ++r) load_cols<TL::VC>(vt + r * D, vreg[r]);
+    } else {
 #pragma unroll
-        for (int i = 0; i < TL::VC / 2; ++i) vreg[r][i] = 0u;
+      for (int r = 0; r < TL::KCH; ++r) {
+        const int row = (tid + kThreads * r) / (D / 8);
+        kreg[r] = (kv0 + row < e) ? *reinterpret_cast<const u32x4 *>(kt + koff[r])
+                                  : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (kv0 + 4 * v_kg + r < e) {
+          load_cols<TL::VC>(vt + r * D, vreg[r]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < TL::VC / 2; ++i) vreg[r][i] = 0u;
+        }
       }
     }
   };
@@ -176,11 +190,14 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
       *reinterpret_cast<u32x4 *>(sK + row * TL::KSTR + col8 * 8) = kreg[r];
     }
     // Transpose 4 rows x VC columns: one 8-byte write of 4 keys per column.
+    // v_perm picks the low (resp. high) bf16 of two rows into one word.
 #pragma unroll
     for (int i = 0; i < TL::VC / 2; ++i) {
       const uint32_t r0 = vreg[0][i], r1 = vreg[1][i], r2 = vreg[2][i], r3 = vreg[3][i];
-      const u32x2 lo = {(r0 & 0xffffu) | (r1 << 16), (r2 & 0xffffu) | (r3 << 16)};
-      const u32x2 hi = {(r0 >> 16) | (r1 & 0xffff0000u), (r2 >> 16) | (r3 & 0xffff0000u)};
+      const u32x2 lo = {__builtin_amdgcn_perm(r1, r0, 0x05040100u),
+                        __builtin_amdgcn_perm(r3, r2, 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(r1, r0, 0x07060302u),
+                        __builtin_amdgcn_perm(r3, r2, 0x07060302u)};
       const int col = v_cc * TL::VC + 2 * i;
       *reinterpret_cast<u32x2 *>(sVt + col * TL::VSTR + 4 * v_kg) = lo;
       *reinterpret_cast<u32x2 *>(sVt + (col + 1) * TL::VSTR + 4 * v_kg) = hi;
@@ -199,16 +216,15 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
 
     if (wave_live && kv0 <= qw + 31) {
       // S^T tile pair: rows = keys kv0 + 32T + ..., columns = this wave's queries.
-      f32x16 st[2];
+      // Two independent accumulation chains, interleaved.
+      f32x16 st[2] = {f32x16{}, f32x16{}};
+      const uint16_t *krow = sK + l32 * TL::KSTR + 8 * g;
 #pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        st[T] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const u32x4 ka = *reinterpret_cast<const u32x4 *>(sK + (32 * T + l32) * TL::KSTR +
-                                                           16 * t + 8 * g);
-          st[T] = mfma32(as_bf16x8(ka), as_bf16x8(qf[t]), st[T]);
-        }
+      for (int t = 0; t < NT; ++t) {
+        const u32x4 ka0 = *reinterpret_cast<const u32x4 *>(krow + 16 * t);
+        const u32x4 ka1 = *reinterpret_cast<const u32x4 *>(krow + 32 * TL::KSTR + 16 * t);
+        st[0] = mfma32(as_bf16x8(ka0), as_bf16x8(qf[t]), st[0]);
+        st[1] = mfma32(as_bf16x8(ka1), as_bf16x8(qf[t]), st[1]);
       }
       // Mask future keys and keys past the segment end (diagonal tiles only).
       if ((kv0 + kBN - 1 > qw) || (kv0 + kBN > e)) {
@@ -221,12 +237,9 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
           }
         }
       }
-      float mx = -INFINITY;
+      float mx = fmaxf(st[0][0], st[1][0]);
 #pragma unroll
-      for (int T = 0; T < 2; ++T) {
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(st[T][i], st[T][i + 1]));
-      }
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(st[0][i], st[1][i]));
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;  // finite: key a is always visible
       const bool grow = mx > m + kLazy;
       if (__any(grow)) {
@@ -237,8 +250,12 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
       }
+      // p = 2^(s c - m) rounded to bf16; the row sum is taken over the same
+      // rounded values (bf16 dot2 with ones), so numerator and denominator
+      // of the softmax see identical weights.
       const float neg_m = -m;
-      float psum = 0.f;
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
       u32x4 pb[2][2];
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
@@ -251,24 +268,26 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
                 __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][8 * u + 2 * jj], scale_log2, neg_m));
             const float p1 = __builtin_amdgcn_exp2f(
                 __builtin_fmaf(st[T][8 * u + 2 * jj + 1], scale_log2, neg_m));
-            psum += p0 + p1;
             pw[jj] = pack_bf16x2(p0, p1);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[jj]), ones,
+                                                   lsum, false);
           }
           pb[T][u] = u32x4{pw[0], pw[1], pw[2], pw[3]};
         }
       }
-      lsum += psum;
       // O^T += V^T P^T. Slot j of lane group g is key 16u + 8(j/4) + 4g + j%4 of
       // the 32-key half T, matching the S^T result layout.
+      // ND independent accumulation chains, interleaved per key step.
+      const uint16_t *vrow = sVt + l32 * TL::VSTR + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        const uint16_t *vrow = sVt + (32 * dt + l32) * TL::VSTR + 4 * g;
+      for (int T = 0; T < 2; ++T) {
 #pragma unroll
-        for (int T = 0; T < 2; ++T) {
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vrow + 32 * T + 16 * u);
-            const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vrow + 32 * T + 16 * u + 8);
+          for (int dt = 0; dt < ND; ++dt) {
+            const uint16_t *vr = vrow + 32 * dt * TL::VSTR + 32 * T + 16 * u;
+            const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vr);
+            const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vr + 8);
             const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
             o[dt] = mfma32(as_bf16x8(va), as_bf16x8(pb[T][u]), o[dt]);
           }
@@ -316,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   den += __shfl_xor(den, 32);
   den += eps;
   const float inv_den = 1.f / den;
-  const float inv_l = 1.f / (lsum + __shfl_xor(lsum, 32));
+  const float inv_l = 1.f / (lsum + __shfl_xor(lsum, 32));  // both halves' key slots
   const float gam = 1.f / (1.f + __expf(-beta[h]));
   const float w_mem = gam * inv_den;
   const float w_dot = (1.f - gam) * inv_l;
