@@ -16,16 +16,24 @@
 //   zprefix (head)              z_{s-1} for every s, and z_S                  [VALU]
 //   gh      (segment, head)     G_s (delta only) and H_s, contraction over    [MFMA bf16]
 //                               the segment's rows, stored in MFMA fragment
-//                               order as fp32
-//   seq     (column tile, head) M_s = M_{s-1} - G_s M_{s-1} + H_s, fp32      [MFMA fp32]
-//                               state in registers; writes the bf16 snapshot
-//                               M_{s-1}^T the fused kernel reads, and M_S.
+//                               order: H_s as fp32, G_s as a bf16 hi/lo pair
+//   seq     (column tile, head) M_s = M_{s-1} - G_s M_{s-1} + H_s with the    [MFMA bf16 x3]
+//                               product as G_hi M_hi + G_hi M_lo + G_lo M_hi
+//                               (about 16 mantissa bits); fp32 state in
+//                               registers; writes the bf16 snapshot M_{s-1}^T
+//                               the fused kernel reads, and M_S.
 //
 // Fragment order: a d x d matrix is stored as (D/32)^2 tiles of 32 x 32; tile
 // (rt, ct) holds, for MFMA-result register r and lane l, the element at row
 // 32 rt + kappa(r, l / 32), column 32 ct + l % 32, where
 // kappa(r, g) = 8 (r / 4) + 4 g + r % 4 is the 32x32 MFMA result row map.
-// Element index: ((rt * (D/32) + ct) * 16 + r) * 64 + l.
+//   H_s (fp32): element index ((rt * (D/32) + ct) * 16 + r) * 64 + l.
+//   G_s (bf16 hi/lo): 32-bit word ((rt * (D/32) + ct) * 64 + l) * 16 + w, where
+//     word 4 h + p (h, p < 2, 4) packs the hi parts of registers 8 h + 2 p
+//     (low half) and 8 h + 2 p + 1 (high half), and word 8 + 4 h + p the lo
+//     parts; so words 4 h .. 4 h + 3 are directly the 8-slot bf16 A operand of
+//     a 32x32x16 MFMA over rows 32 rt + 16 h .. + 15. G_s is symmetric, so
+//     tile (kt, ct) read this way is the A operand for output rows of tile ct.
 
 #include "common.h"
 #include "launch.h"
@@ -95,38 +103,75 @@ __global__ __launch_bounds__(256) void zsum_kernel(const uint16_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// zprefix: z_pre[head][s] = z_{s-1} (the state before segment s), slot S = z_S
+// zprefix: z_pre[head][s] = z_{s-1} (the state before segment s), slot S = z_S.
+// One workgroup per head; thread (grp, c) owns column c of a contiguous range
+// of segments. Pass 1 sums the range, the workgroup prefix-sums the ranges in
+// LDS, pass 2 writes the running value. dz is read in batches of kZB
+// independent loads so that the sequential part waits on memory only once
+// per batch.
 // ---------------------------------------------------------------------------
-__global__ void zprefix_kernel(const float *__restrict__ z0, const float *__restrict__ dz,
-                               float *__restrict__ z_pre, int S, int D, int parts) {
-  const int head = blockIdx.x, t = threadIdx.x;
-  if (t >= D) return;
-  float z = z0[static_cast<size_t>(head) * D + t];
-  float *out = z_pre + static_cast<size_t>(head) * (S + 1) * D + t;
-  const float *d = dz + static_cast<size_t>(head) * S * parts * D + t;
-  for (int s = 0; s < S; ++s) {
-    out[static_cast<size_t>(s) * D] = z;
-    float seg = 0.f;
-    for (int p = 0; p < parts; ++p) seg += d[(static_cast<size_t>(s) * parts + p) * D];
-    z += seg;
+constexpr int kZB = 16;
+constexpr int kZThreads = 1024;
+
+__global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restrict__ z0,
+                                                            const float *__restrict__ dz,
+                                                            float *__restrict__ z_pre, int S,
+                                                            int D, int parts) {
+  __shared__ float tot[kZThreads];
+  const int head = blockIdx.x, G = kZThreads / D;
+  const int c = threadIdx.x % D, grp = threadIdx.x / D;
+  const int per = (S + G - 1) / G;
+  const int s0 = min(grp * per, S), s1 = min(s0 + per, S);
+  const int f0 = s0 * parts, f1 = s1 * parts;  // flat (segment, part) range
+  const float *d = dz + static_cast<size_t>(head) * S * parts * D + c;
+
+  float sum = 0.f;
+  for (int f = f0; f < f1; f += kZB) {
+    float x[kZB];
+#pragma unroll
+    for (int i = 0; i < kZB; ++i) x[i] = f + i < f1 ? d[static_cast<size_t>(f + i) * D] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kZB; ++i) sum += x[i];
   }
-  out[static_cast<size_t>(S) * D] = z;
+  tot[grp * D + c] = sum;
+  __syncthreads();
+  float z = z0[static_cast<size_t>(head) * D + c];
+  for (int q = 0; q < grp; ++q) z += tot[q * D + c];
+
+  float *out = z_pre + static_cast<size_t>(head) * (S + 1) * D + c;
+  for (int f = f0; f < f1; f += kZB) {
+    float x[kZB];
+#pragma unroll
+    for (int i = 0; i < kZB; ++i) x[i] = f + i < f1 ? d[static_cast<size_t>(f + i) * D] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kZB; ++i) {
+      if (f + i < f1) {
+        if ((f + i) % parts == 0) out[static_cast<size_t>((f + i) / parts) * D] = z;
+        z += x[i];
+      }
+    }
+  }
+  if (grp == G - 1) {
+    float zs = z0[static_cast<size_t>(head) * D + c];
+    for (int q = 0; q < G; ++q) zs += tot[q * D + c];
+    out[static_cast<size_t>(S) * D] = zs;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // gh: [G_s | H_s] = sigma(K_s)^T [diag(1/den) sigma(K_s) | V_s], den_i = sigma(k_i).z_{s-1} + eps
 // ---------------------------------------------------------------------------
-template <int D, bool DELTA>
+template <int D, bool DELTA, int CS>
 __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
                                                  const uint16_t *__restrict__ v,
                                                  const float *__restrict__ z_pre,
                                                  float *__restrict__ gh, int L, int N, int S,
-                                                 float eps, int csplit) {
+                                                 float eps) {
   constexpr int ND = D / 32;
   constexpr int CCH = D / 8;            // 8-column chunks per row
   constexpr int ITEMS = 16 * CCH;       // staging items: 4 rows x 8 columns each
   constexpr int NPAIR = DELTA ? 2 * ND : ND;  // (matrix, column tile) pairs
-  constexpr int PPW = (NPAIR + 3) / 4;        // pairs per wave
+  constexpr int PPW = (NPAIR + 4 * CS - 1) / (4 * CS);  // pairs per wave
   static_assert(ITEMS <= 256, "one staging item per thread");
 
   __shared__ __attribute__((aligned(16))) uint16_t sKt[D * kStr];  // sigma(K)^T  [col][key]
@@ -136,11 +181,16 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
   __shared__ float sDenPart[CCH][64];
   __shared__ float sRden[64];
 
-  // Column split: workgroup cs of `csplit` owns pairs [p_lo, p_hi); every
-  // workgroup stages the whole chunk.
-  const int s = blockIdx.x / csplit, cs = blockIdx.x % csplit;
-  const int p_lo = cs * NPAIR / csplit, p_hi = (cs + 1) * NPAIR / csplit;
-  const int head = blockIdx.y;
+  // Work item wi = (head * S + s) * CS + cs. When the launch divides evenly,
+  // consecutive work items go to one XCD (hardware hands out workgroups
+  // round-robin over the 8 XCDs), so the CS workgroups that read the same rows
+  // share that XCD's L2. Column split: workgroup cs owns pairs [p_lo, p_hi);
+  // every workgroup stages the whole chunk.
+  int wi = blockIdx.y * gridDim.x + blockIdx.x;
+  const int total = gridDim.x * gridDim.y;
+  if (CS > 1 && total % (8 * CS) == 0) wi = (wi % 8) * (total / 8) + wi / 8;
+  const int cs = wi % CS, s = (wi / CS) % S, head = wi / CS / S;
+  const int p_lo = cs * NPAIR / CS, p_hi = (cs + 1) * NPAIR / CS;
   const int a = s * N, e = min(a + N, L);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -157,24 +207,27 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
   const bool has = tid < ITEMS;
   const int kg = tid & 15, cc = tid >> 4;  // rows 4 kg .. 4 kg + 3, columns 8 cc .. 8 cc + 7
 
-  // Register staging of one 64-row chunk (4 rows x 8 columns per item); the
-  // next chunk's loads are issued before the current chunk's MFMAs.
-  u32x4 kw[4], vv[4];
-  auto load_chunk = [&](int i0) {
+  // Register staging of 64-row chunks (4 rows x 8 columns per item), two
+  // register sets: a chunk's loads are issued two chunks before it is staged.
+  struct Stage {
+    u32x4 k[4], v[4];
+  };
+  auto load_chunk = [&](Stage &st, int i0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = i0 + 4 * kg + r;
-      kw[r] = vv[r] = u32x4{0u, 0u, 0u, 0u};
+      st.k[r] = st.v[r] = u32x4{0u, 0u, 0u, 0u};
       if (has && row < e) {
-        kw[r] = *reinterpret_cast<const u32x4 *>(kp + static_cast<size_t>(row) * D + cc * 8);
-        vv[r] = *reinterpret_cast<const u32x4 *>(vp + static_cast<size_t>(row) * D + cc * 8);
+        st.k[r] = *reinterpret_cast<const u32x4 *>(kp + static_cast<size_t>(row) * D + cc * 8);
+        st.v[r] = *reinterpret_cast<const u32x4 *>(vp + static_cast<size_t>(row) * D + cc * 8);
       }
     }
   };
-  load_chunk(a);
 
-  for (int i0 = a; i0 < e; i0 += 64) {
+  auto chunk = [&](int i0, Stage &cur) {
     __syncthreads();  // previous chunk consumed; sZ visible
+    const u32x4 *kw = cur.k;
+    const u32x4 *vv = cur.v;
     float kf[4][8];
     if (has) {
       uint32_t vw[4][4];
@@ -231,7 +284,7 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
       }
     }
     __syncthreads();
-    if (i0 + 64 < e) load_chunk(i0 + 64);
+    if (i0 + 128 < e) load_chunk(cur, i0 + 128);  // cur is free once staged
 
     // Contraction over the 64 keys of the chunk, 16 per MFMA. Slot j of lane
     // group g is key kb + 8 (j / 4) + 4 g + j % 4 in both operands.
@@ -261,9 +314,21 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
         }
       }
     }
+  };
+  Stage sa, sb;
+  load_chunk(sa, a);
+  if (a + 64 < e) load_chunk(sb, a + 64);
+  for (int i0 = a;;) {
+    chunk(i0, sa);
+    i0 += 64;
+    if (i0 >= e) break;
+    chunk(i0, sb);
+    i0 += 64;
+    if (i0 >= e) break;
   }
 
-  // Store in fragment order: matrix 0 = G, matrix 1 = H.
+  // Store in fragment order: matrix 0 = G as bf16 hi/lo operand words
+  // (hi = bf16(x), lo = bf16(x - hi)), matrix 1 = H as fp32.
   float *base = gh + (static_cast<size_t>(head) * S + s) * 2 * D * D;
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi) {
@@ -273,9 +338,24 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
       const int ct = pr % ND;
 #pragma unroll
       for (int rt = 0; rt < ND; ++rt) {
-        float *f = base + static_cast<size_t>(mat) * D * D + ((rt * ND + ct) * 16) * 64 + lane;
+        if (mat == 0) {
+          uint32_t wd[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) f[r * 64] = acc[pi][rt][r];
+          for (int q = 0; q < 8; ++q) {
+            const float x0 = acc[pi][rt][2 * q], x1 = acc[pi][rt][2 * q + 1];
+            const uint32_t hw = pack_bf16x2(x0, x1);
+            wd[q] = hw;
+            wd[8 + q] = pack_bf16x2(x0 - lo_bf16(hw), x1 - hi_bf16(hw));
+          }
+          u32x4 *f = reinterpret_cast<u32x4 *>(base) + ((rt * ND + ct) * 64 + lane) * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            f[q] = u32x4{wd[4 * q], wd[4 * q + 1], wd[4 * q + 2], wd[4 * q + 3]};
+        } else {
+          float *f = base + static_cast<size_t>(D) * D + ((rt * ND + ct) * 16) * 64 + lane;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) f[r * 64] = acc[pi][rt][r];
+        }
       }
     }
   }
@@ -285,6 +365,9 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
 // seq: the recurrence over segments for one 32-column tile of M.
 // Wave w holds rows 32 w .. 32 w + 31 of the tile in MFMA-result layout
 // (lane: column 32 jt + l % 32; register r: row 32 w + kappa(r, l / 32)).
+// The tile's current state is also kept in LDS, transposed, as bf16 hi and lo
+// parts (sMh[n][c], sMl[n][c]: column n of the tile, row c of M), which is the
+// B operand of G_s M_{s-1}. Its hi part is the bf16 snapshot M_{s-1}^T.
 // ---------------------------------------------------------------------------
 template <int D, bool DELTA>
 __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *__restrict__ gh,
@@ -292,8 +375,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *__restr
                                                            uint16_t *__restrict__ mt_pre,
                                                            int S) {
   constexpr int ND = D / 32;
-  constexpr int SMS = 40;  // sM row stride in floats: lane groups land on disjoint banks
-  __shared__ float sM[DELTA ? D * SMS : 1];
+  constexpr int MS = D + 4;  // sMh / sMl row stride (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t sMh[DELTA ? 32 * MS : 4];
+  __shared__ __attribute__((aligned(16))) uint16_t sMl[DELTA ? 32 * MS : 4];
   const int jt = blockIdx.x, head = blockIdx.y;
   const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -303,17 +387,35 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *__restr
   f32x16 m;
 #pragma unroll
   for (int r = 0; r < 16; ++r) m[r] = Mh[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j];
-  if constexpr (DELTA) {
+
+  // Publish the state before segment st: global bf16 snapshot (if st < S) and,
+  // for the delta rule, the hi/lo operand copy in LDS. This lane's rows
+  // 32 ct + 8 q4 + 4 g + 0..3 are contiguous in the transposed layouts.
+  auto publish = [&](int st) {
+    uint16_t *mt = mt_pre + (static_cast<size_t>(head) * S + st) * D * D +
+                   static_cast<size_t>(j) * D + 32 * ct + 4 * g;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sM[(32 * ct + kappa(r, g)) * SMS + l32] = m[r];
-    __syncthreads();
-  }
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint32_t h0 = pack_bf16x2(m[4 * q4], m[4 * q4 + 1]);
+      const uint32_t h1 = pack_bf16x2(m[4 * q4 + 2], m[4 * q4 + 3]);
+      if (st < S) *reinterpret_cast<u32x2 *>(mt + 8 * q4) = u32x2{h0, h1};
+      if constexpr (DELTA) {
+        const int off = l32 * MS + 32 * ct + 8 * q4 + 4 * g;
+        *reinterpret_cast<u32x2 *>(sMh + off) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2 *>(sMl + off) =
+            u32x2{pack_bf16x2(m[4 * q4] - lo_bf16(h0), m[4 * q4 + 1] - hi_bf16(h0)),
+                  pack_bf16x2(m[4 * q4 + 2] - lo_bf16(h1), m[4 * q4 + 3] - hi_bf16(h1))};
+      }
+    }
+  };
 
   // Fragments of step s are loaded one step ahead, so their latency overlaps
-  // the previous step's MFMAs.
+  // the previous step's MFMAs. G: 4 operand vectors (hi h=0,1, lo h=0,1) per
+  // 32-row tile kt of the contraction.
   constexpr int NG = DELTA ? ND : 1;
-  float gcur[NG][16], hcur[16];
-  auto load_step = [&](int st, float (&gd)[NG][16], float (&hd)[16]) {
+  u32x4 gcur[NG][4];
+  float hcur[16];
+  auto load_step = [&](int st, u32x4 (&gd)[NG][4], float (&hd)[16]) {
     const float *ghs = gh + (static_cast<size_t>(head) * S + st) * 2 * D * D;
     const float *hf = ghs + static_cast<size_t>(D) * D + ((ct * ND + jt) * 16) * 64 + lane;
 #pragma unroll
@@ -321,46 +423,49 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *__restr
     if constexpr (DELTA) {
 #pragma unroll
       for (int kt = 0; kt < ND; ++kt) {
-        const float *gf = ghs + ((kt * ND + ct) * 16) * 64 + lane;
+        const u32x4 *gf = reinterpret_cast<const u32x4 *>(ghs) + ((kt * ND + ct) * 64 + lane) * 4;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) gd[kt][r] = gf[r * 64];
+        for (int q = 0; q < 4; ++q) gd[kt][q] = gf[q];
       }
     }
   };
   if (S > 0) load_step(0, gcur, hcur);
+  publish(0);
+  if constexpr (DELTA) __syncthreads();
 
   for (int s = 0; s < S; ++s) {
-    float gnext[NG][16], hnext[16];
+    u32x4 gnext[NG][4];
+    float hnext[16];
     if (s + 1 < S) load_step(s + 1, gnext, hnext);
-    // Snapshot of M_{s-1}, transposed, bf16: mt[j][c] for this lane's 16 rows c.
-    uint16_t *mt = mt_pre + (static_cast<size_t>(head) * S + s) * D * D +
-                   static_cast<size_t>(j) * D + 32 * ct + 4 * g;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const u32x2 pk = {pack_bf16x2(m[4 * q4], m[4 * q4 + 1]),
-                        pack_bf16x2(m[4 * q4 + 2], m[4 * q4 + 3])};
-      *reinterpret_cast<u32x2 *>(mt + 8 * q4) = pk;
-    }
     if constexpr (DELTA) {
+      // (G M)[32 ct + m][j] = sum_c G[c][32 ct + m] M[c][j] over c = 32 kt +
+      // 16 h + 8 (slot / 4) + 4 g + slot % 4 in both operands.
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int kt = 0; kt < ND; ++kt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float bv = sM[(32 * kt + kappa(r, g)) * SMS + l32];
-          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(gcur[kt][r], bv, acc, 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+          const int off = l32 * MS + 32 * kt + 16 * h + 4 * g;
+          const u32x2 h0 = *reinterpret_cast<const u32x2 *>(sMh + off);
+          const u32x2 h1 = *reinterpret_cast<const u32x2 *>(sMh + off + 8);
+          const u32x2 l0 = *reinterpret_cast<const u32x2 *>(sMl + off);
+          const u32x2 l1 = *reinterpret_cast<const u32x2 *>(sMl + off + 8);
+          const u32x4 bh = {h0[0], h0[1], h1[0], h1[1]};
+          const u32x4 bl = {l0[0], l0[1], l1[0], l1[1]};
+          acc = mfma_bf16(gcur[kt][h], bh, acc);
+          acc = mfma_bf16(gcur[kt][h], bl, acc);
+          acc = mfma_bf16(gcur[kt][2 + h], bh, acc);
         }
       }
-      __syncthreads();  // every wave has read M_{s-1} from sM
+      __syncthreads();  // every wave has read M_{s-1} from LDS
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        m[r] = m[r] - acc[r] + hcur[r];
-        sM[(32 * ct + kappa(r, g)) * SMS + l32] = m[r];
-      }
+      for (int r = 0; r < 16; ++r) m[r] = m[r] - acc[r] + hcur[r];
+      publish(s + 1);
       __syncthreads();
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) m[r] += hcur[r];
+      publish(s + 1);
     }
     if (s + 1 < S) {
 #pragma unroll
@@ -368,7 +473,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *__restr
 #pragma unroll
       for (int kt = 0; kt < NG; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) gcur[kt][r] = gnext[kt][r];
+        for (int q = 0; q < 4; ++q) gcur[kt][q] = gnext[kt][q];
     }
   }
 #pragma unroll
@@ -382,19 +487,26 @@ hipError_t launch_d(const Geometry &g, const uint16_t *k, const uint16_t *v, flo
   const int parts = ws.z_parts;
   // Few (segment, head) pairs: split each one's output tiles over two
   // workgroups so that the launch still covers the chip.
-  const int csplit = (g.S * heads < 512) ? 2 : 1;
+  const bool split = g.S * heads < 512;
+  const dim3 ghgrid(g.S * (split ? 2 : 1), heads), seqgrid(D / 32, heads);
   zsum_kernel<D><<<dim3(g.S * parts, heads), 256, 0, stream>>>(k, ws.dz, g.L, g.N, g.S, parts);
-  zprefix_kernel<<<heads, D, 0, stream>>>(z, ws.dz, ws.z_pre, g.S, D, parts);
+  zprefix_kernel<<<heads, kZThreads, 0, stream>>>(z, ws.dz, ws.z_pre, g.S, D, parts);
   if (delta) {
-    gh_kernel<D, true><<<dim3(g.S * csplit, heads), 256, 0, stream>>>(
-        k, v, ws.z_pre, ws.gh, g.L, g.N, g.S, g.eps, csplit);
-    seq_kernel<D, true><<<dim3(D / 32, heads), 64 * (D / 32), 0, stream>>>(ws.gh, M,
-                                                                          ws.mt_pre_bf16, g.S);
+    if (split)
+      gh_kernel<D, true, 2><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, g.L, g.N, g.S,
+                                                        g.eps);
+    else
+      gh_kernel<D, true, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, g.L, g.N, g.S,
+                                                        g.eps);
+    seq_kernel<D, true><<<seqgrid, 64 * (D / 32), 0, stream>>>(ws.gh, M, ws.mt_pre_bf16, g.S);
   } else {
-    gh_kernel<D, false><<<dim3(g.S * csplit, heads), 256, 0, stream>>>(
-        k, v, ws.z_pre, ws.gh, g.L, g.N, g.S, g.eps, csplit);
-    seq_kernel<D, false><<<dim3(D / 32, heads), 64 * (D / 32), 0, stream>>>(ws.gh, M,
-                                                                           ws.mt_pre_bf16, g.S);
+    if (split)
+      gh_kernel<D, false, 2><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, g.L, g.N, g.S,
+                                                         g.eps);
+    else
+      gh_kernel<D, false, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, g.L, g.N, g.S,
+                                                         g.eps);
+    seq_kernel<D, false><<<seqgrid, 64 * (D / 32), 0, stream>>>(ws.gh, M, ws.mt_pre_bf16, g.S);
   }
   return hipGetLastError();
 }
