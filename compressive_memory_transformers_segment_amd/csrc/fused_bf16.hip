@@ -26,8 +26,10 @@
 //   * Q stays in registers for the whole key loop (its d-contiguous rows are
 //     exactly the B operand of S^T = K Q^T).
 //   * K tiles are staged row-major in LDS (A operand of S^T, d-contiguous).
-//     V tiles are staged transposed in LDS, [d][key], so the A operand of
-//     O^T = V^T P^T is two 8-byte LDS reads per lane. Two LDS buffers: the next
+//     V tiles are staged transposed in LDS, [d][key], with the keys of each
+//     16-key step permuted so that the 8 keys a lane contributes to one
+//     O^T = V^T P^T MFMA (two runs of 4 in the S^T result layout) are
+//     adjacent: the A operand is one 16-byte LDS read. Two LDS buffers: the next
 //     tile's global loads are issued before the current tile's MFMAs and it is
 //     written into the idle buffer afterwards, one barrier per key tile.
 //   * Causal skipping: a workgroup visits key tiles up to its last query row;
@@ -67,7 +69,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast
 template <int D>
 struct Tile {
   static constexpr int KSTR = D + 8;    // sK row stride in bf16 (16-byte pad)
-  static constexpr int VSTR = kBN + 4;  // sVt row stride in bf16 (8-byte pad)
+  static constexpr int VSTR = kBN + 8;  // sVt row stride in bf16: 36 dwords, 16 rows hit distinct banks
   static constexpr int MSTR = D + 8;    // staged M^T row stride in bf16
   static constexpr int KCHUNKS = kBN * D / 8;                 // 16-byte K chunks per tile
   static constexpr int KCH = (KCHUNKS + kThreads - 1) / kThreads;  // per thread
@@ -205,6 +207,11 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     }
   };
 
+  // Key group kg (keys 4 kg .. 4 kg + 3 of the tile) = 16-key step kg / 4,
+  // run h = (kg / 2) % 2, lane group g = kg % 2 of the S^T layout; it is
+  // stored at 4-key position (kg / 4, g, h), i.e. bits 0 and 1 swapped.
+  const int v_pos = 4 * ((v_kg & ~3) | ((v_kg & 1) << 1) | ((v_kg >> 1) & 1));
+
   auto store_tile = [&](uint16_t *sK, uint16_t *sVt) {
 #pragma unroll
     for (int r = 0; r < TL::KCH; ++r) {
@@ -225,8 +232,8 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
         const u32x2 hi = {__builtin_amdgcn_perm(r1, r0, 0x07060302u),
                           __builtin_amdgcn_perm(r3, r2, 0x07060302u)};
         const int col = v_cc * TL::VC + 2 * i;
-        *reinterpret_cast<u32x2 *>(sVt + col * TL::VSTR + 4 * v_kg) = lo;
-        *reinterpret_cast<u32x2 *>(sVt + (col + 1) * TL::VSTR + 4 * v_kg) = hi;
+        *reinterpret_cast<u32x2 *>(sVt + col * TL::VSTR + v_pos) = lo;
+        *reinterpret_cast<u32x2 *>(sVt + (col + 1) * TL::VSTR + v_pos) = hi;
       }
     }
   };
@@ -288,9 +295,10 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
       // 16-key group of P is packed: pair idx holds elements 2 (idx % 8), +1
       // of the 32-key half idx / 8, and group tu = idx / 4 is the P operand of
       // key step tu (slot j of lane group g is key 16 tu + 8 (j / 4) + 4 g +
-      // j % 4, matching the S^T result layout).
+      // j % 4, matching the S^T result layout; sVt holds it at position
+      // 16 tu + 8 g + j).
       const float neg_m = -m;
-      const uint16_t *vrow = sVt + l32 * TL::VSTR + 4 * g;
+      const uint16_t *vrow = sVt + l32 * TL::VSTR + 8 * g;
       uint32_t pw[4];
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
@@ -305,10 +313,8 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
           const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
 #pragma unroll
           for (int dt = 0; dt < ND; ++dt) {
-            const uint16_t *vr = vrow + 32 * dt * TL::VSTR + 16 * tu;
-            const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vr);
-            const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vr + 8);
-            const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+            const u32x4 va =
+                *reinterpret_cast<const u32x4 *>(vrow + 32 * dt * TL::VSTR + 16 * tu);
             o[dt] = mfma32(as_bf16x8(va), as_bf16x8(pb), o[dt]);
           }
         }
