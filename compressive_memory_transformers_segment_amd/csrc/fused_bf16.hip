@@ -66,6 +66,21 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
+// Combine a lane's value with that of the lane 32 away. v_permlane32_swap
+// exchanges the two 32-lane halves between its two operands, so with both
+// operands equal to x the pair it returns is {x, x of lane ^ 32} in some
+// order in every lane; max and sum are order-independent.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
 struct Tile {
   static constexpr int KSTR = D + 8;    // sK row stride in bf16 (16-byte pad)
@@ -278,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
       float mx = fmaxf(st[0][0], st[1][0]);
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(st[0][i], st[1][i]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;  // finite: key a is always visible
+      mx = max_xor32(mx) * scale_log2;  // finite: key a is always visible
       const bool grow = mx > m + kLazy;
       if (__any(grow)) {
         __asm__ volatile("" ::: "memory");  // keep this a branch (rarely taken)
@@ -299,25 +314,29 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
       // 16 tu + 8 g + j).
       const float neg_m = -m;
       const uint16_t *vrow = sVt + l32 * TL::VSTR + 8 * g;
-      uint32_t pw[4];
 #pragma unroll
-      for (int idx = 0; idx < 16; ++idx) {
-        const int T = idx >> 3, i = 2 * (idx & 7);
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][i], scale_log2, neg_m));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][i + 1], scale_log2, neg_m));
-        pw[idx & 3] = pack_bf16x2(p0, p1);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[idx & 3]), ones,
-                                               lsum, false);
-        if ((idx & 3) == 3) {
-          const int tu = idx >> 2;
-          const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
+      for (int tu = 0; tu < 4; ++tu) {
+        // The V fragments of this key step are read first, so their LDS
+        // latency overlaps the exponentials.
+        u32x4 va[ND];
 #pragma unroll
-          for (int dt = 0; dt < ND; ++dt) {
-            const u32x4 va =
-                *reinterpret_cast<const u32x4 *>(vrow + 32 * dt * TL::VSTR + 16 * tu);
-            o[dt] = mfma32(as_bf16x8(va), as_bf16x8(pb), o[dt]);
-          }
+        for (int dt = 0; dt < ND; ++dt)
+          va[dt] = *reinterpret_cast<const u32x4 *>(vrow + 32 * dt * TL::VSTR + 16 * tu);
+        uint32_t pw[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int idx = 4 * tu + jj;
+          const int T = idx >> 3, i = 2 * (idx & 7);
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][i], scale_log2, neg_m));
+          const float p1 =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][i + 1], scale_log2, neg_m));
+          pw[jj] = pack_bf16x2(p0, p1);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[jj]), ones, lsum,
+                                                 false);
         }
+        const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) o[dt] = mfma32(as_bf16x8(va[dt]), as_bf16x8(pb), o[dt]);
       }
     }
     if (has_next) {
@@ -358,10 +377,9 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     }
     sq[t] = u32x4{wv[0], wv[1], wv[2], wv[3]};
   }
-  den += __shfl_xor(den, 32);
-  den += eps;
+  den = sum_xor32(den) + eps;
   const float inv_den = 1.f / den;
-  const float inv_l = 1.f / (lsum + __shfl_xor(lsum, 32));  // both halves' key slots
+  const float inv_l = 1.f / sum_xor32(lsum);  // both halves' key slots
   const float gam = 1.f / (1.f + __expf(-beta[h]));
   const float w_mem = gam * inv_den;
   const float w_dot = (1.f - gam) * inv_l;
