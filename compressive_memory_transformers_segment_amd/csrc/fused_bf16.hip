@@ -25,13 +25,17 @@
 //     long as both operands agree).
 //   * Q stays in registers for the whole key loop (its d-contiguous rows are
 //     exactly the B operand of S^T = K Q^T).
-//   * K tiles are staged row-major in LDS (A operand of S^T, d-contiguous).
-//     V tiles are staged transposed in LDS, [d][key], with the keys of each
-//     16-key step permuted so that the 8 keys a lane contributes to one
-//     O^T = V^T P^T MFMA (two runs of 4 in the S^T result layout) are
-//     adjacent: the A operand is one 16-byte LDS read. Two LDS buffers: the next
-//     tile's global loads are issued before the current tile's MFMAs and it is
-//     written into the idle buffer afterwards, one barrier per key tile.
+//   * Tiles move from HBM to LDS by direct loads (global_load_lds: no
+//     register staging, no LDS store instructions) through a ring of three
+//     buffers: tile t + 2 is in flight while tile t is consumed, and each
+//     wave waits only for its own loads of tile t + 1 before the one barrier
+//     per key tile. K tiles are row-major with a 16-byte-unit XOR swizzle so
+//     that the 32 rows an MFMA operand reads hit distinct banks. V arrives
+//     already transposed, [d][key], from the segment scan, which writes it per
+//     64-key tile with the keys of each 16-key step permuted so that the 8
+//     keys a lane contributes to one O^T = V^T P^T MFMA (two runs of 4 in the
+//     S^T result layout) are adjacent and bank-swizzled: every MFMA operand
+//     read from LDS is one 16-byte read.
 //   * Causal skipping: a workgroup visits key tiles up to its last query row;
 //     a wave skips tiles entirely in its future and masks only diagonal tiles.
 //   * Online softmax with a lazy rescale: the running max m of a row moves
@@ -43,10 +47,13 @@
 //   * Block order is remapped so that consecutive work items share an XCD
 //     (blocks are dealt round-robin to the 8 XCDs): the query heads that read
 //     one kv head land on one XCD and share its L2.
-//   * Epilogue: the pre-segment snapshot M^T (bf16, [d_v][d_k]) is staged in
-//     LDS once for all heads of the workgroup and multiplied with sigma(Q)
+//   * Epilogue: the pre-segment snapshot M^T (bf16, [d_v][d_k]) arrives in its
+//     own LDS buffer by direct loads ahead of the first key tile, once for all
+//     heads of the workgroup, and is multiplied with sigma(Q)
 //     (computed from the Q registers) on MFMA; the denominator sigma(Q).z is a
 //     per-lane dot product plus one exchange.
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -81,38 +88,46 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wait until at most VM vector-memory operations of this wave are in flight
+// and all of its LDS operations are done (s_waitcnt, gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+
+#define IA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
 template <int D>
 struct Tile {
-  static constexpr int KSTR = D + 8;    // sK row stride in bf16 (16-byte pad)
-  static constexpr int VSTR = kBN + 8;  // sVt row stride in bf16: 36 dwords, 16 rows hit distinct banks
-  static constexpr int MSTR = D + 8;    // staged M^T row stride in bf16
-  static constexpr int KCHUNKS = kBN * D / 8;                 // 16-byte K chunks per tile
-  static constexpr int KCH = (KCHUNKS + kThreads - 1) / kThreads;  // per thread
-  static constexpr int VC = (D / 32) > 2 ? (D / 32) : 2;      // V columns per item (x 4 rows)
-  static constexpr int VITEMS = 16 * (D / VC);                // 4-row x VC-column items
-  static constexpr int BUF = kBN * KSTR + D * VSTR;           // one K tile + one V^T tile
-  static constexpr int LDS_ATT = 2 * BUF;
-  static constexpr int LDS_MEM = D * MSTR;
-  static constexpr int LDS = LDS_ATT > LDS_MEM ? LDS_ATT : LDS_MEM;
-  static_assert(VITEMS <= kThreads, "one V staging item per thread");
+  static constexpr int CPR = D / 8;          // 16-byte units per K (and M^T) row
+  static constexpr int RP = 16 / CPR;        // K rows per 256-byte bank line
+  static constexpr int KU = kBN * CPR;       // K units per tile
+  static constexpr int VU = D * 8;           // V^T units per tile (64 keys per row)
+  static constexpr int BUFU = KU + VU;       // units per ring buffer
+  static constexpr int BUF = BUFU * 8;       // bf16 per ring buffer
+  static constexpr int IPW = BUFU / kThreads;  // direct loads per wave per tile
+  static constexpr int MU = D * CPR;         // M^T units
+  static constexpr int MPW = (MU + kThreads - 1) / kThreads;  // direct loads per wave for M^T
+  static_assert(BUFU % kThreads == 0, "whole direct loads per wave");
+  static_assert(KU % 64 == 0, "a direct load never straddles K and V^T");
+
 };
 
-// Load VC consecutive bf16 (VC in {2, 4}) as VC/2 packed words.
-template <int VC>
-__device__ __forceinline__ void load_cols(const uint16_t *p, uint32_t (&w)[VC / 2]) {
-  if constexpr (VC == 4) {
-    const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
-    w[0] = x[0];
-    w[1] = x[1];
-  } else {
-    w[0] = *reinterpret_cast<const uint32_t *>(p);
-  }
+// 16-byte unit of (row r, unit c) in a swizzled row-major tile of D columns
+// (K tiles and M^T): 16 consecutive rows read at one unit index land on
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_unit(int r, int c) {
+  using TL = Tile<D>;
+  return r * TL::CPR + (c ^ ((r / TL::RP) % TL::CPR));
 }
 
 template <int D, int HPW>
 __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const float *__restrict__ beta,
+    const uint16_t *__restrict__ vt, int vt_tiles, const float *__restrict__ beta,
     const float *__restrict__ z_pre, const uint16_t *__restrict__ mt_pre,
     uint16_t *__restrict__ out, int Hq, int Hkv, int L, int N, int S, int n_qt, float eps,
     float scale_log2, int xcd_chunk) {
@@ -121,7 +136,12 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   constexpr int ND = D / 32;          // 32-row d tiles of O^T
   constexpr int RW = kWaves / HPW;    // waves (32-row strips) per head
   constexpr int BM = 32 * RW;         // query rows per workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t smem[TL::LDS];
+  // Three separate arrays, so that the compiler can tell the buffers apart
+  // when it orders LDS reads after direct loads into another buffer.
+  __shared__ __attribute__((aligned(16))) uint16_t sB0[TL::BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sB1[TL::BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[TL::BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sM[TL::MU * 8];
   __shared__ float sZ[D];
   const int tid = threadIdx.x;
   // The wave index is uniform across the wave; readfirstlane puts it (and all
@@ -155,9 +175,12 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   const bool wave_live = qw < e;
 
   const uint16_t *qp = q + static_cast<size_t>(bhq) * L * D;
-  const size_t kvoff = (static_cast<size_t>(b) * Hkv + hk) * L * D;
-  const uint16_t *kp = k + kvoff;
-  const uint16_t *vp = v + kvoff;
+  const size_t head = static_cast<size_t>(b) * Hkv + hk;
+  const uint16_t *kp = k + head * L * D;
+  const uint16_t *vtp = vt + (head * S + s) * vt_tiles * (D * 64);  // this segment's V^T tiles
+  const uint16_t *mt = mt_pre + (head * S + s) * D * D;
+  const float *zs = z_pre + (head * (S + 1) + s) * D;
+  const float zreg = tid < D ? zs[tid] : 0.f;
 
   // Q^T operand: k-step t covers d in [16t, 16t+16); lane holds d = 16t + 8g + 0..7.
   u32x4 qf[NT];
@@ -176,189 +199,168 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
 
   const int kv_end = min(q0 + BM, e);
 
-  // Register staging of the next K / V tile.
-  u32x4 kreg[TL::KCH];
-  uint32_t vreg[4][TL::VC / 2];
-  const int v_kg = tid & 15;  // 4-row key group
-  const int v_cc = tid >> 4;  // VC-column chunk
-  const bool v_has = tid < TL::VITEMS;
-  // K chunk r of this thread: chunk tid + kThreads * r = row c / (D/8), col (c % (D/8)) * 8.
-  constexpr int KROWS = kThreads / (D / 8);
-  const int koff = (tid / (D / 8)) * D + (tid % (D / 8)) * 8;
-  const int voff = 4 * v_kg * D + v_cc * TL::VC;
+  const int n_tiles = (kv_end - a + kBN - 1) / kBN;
 
-  auto load_tile = [&](int kv0) {
-    const uint16_t *kt = kp + static_cast<size_t>(kv0) * D;
-    const uint16_t *vt = vp + static_cast<size_t>(kv0) * D + voff;
-    if (kv0 + kBN <= e) {  // whole tile inside the segment: no per-row guards
+  // Direct loads: load i of wave w moves units [(8 i + w) 64, +64) of a ring
+  // buffer, one 16-byte unit per lane, into consecutive LDS (the hardware
+  // writes lane l's unit at the wave's LDS base + 16 l). Units below KU are K
+  // (lane picks its source through the swizzle; rows past the segment end
+  // read its last row, whose scores are masked anyway), the rest V^T, copied
+  // verbatim from the scan's tile.
+  auto dma_tile = [&](int t, uint16_t *buf) {
+    const int kv0 = a + t * kBN;
+    const uint16_t *vsrc = vtp + static_cast<size_t>(t) * (D * 64);
 #pragma unroll
-      for (int r = 0; r < TL::KCH; ++r)
-        if (tid + kThreads * r < TL::KCHUNKS)
-          kreg[r] = *reinterpret_cast<const u32x4 *>(kt + koff + r * KROWS * D);
-      if (v_has) {
+    for (int i = 0; i < TL::IPW; ++i) {
+      const int u0 = (8 * i + w) * 64;  // wave-uniform
+      const int U = u0 + lane;
+      const int r = U / TL::CPR, cp = U % TL::CPR;
+      const uint16_t *ksrc =
+          kp + static_cast<size_t>(min(kv0 + r, e - 1)) * D + 8 * (cp ^ ((r / TL::RP) % TL::CPR));
+      const uint16_t *vsrc_u = vsrc + 8 * (U - TL::KU);
+      // For D >= 64 the first KU / 512 loads of every wave are K; for D = 32
+      // the first load is K in waves 0..3 and V^T in waves 4..7. A select, not
+      // a branch, so the loads form straight-line code.
+      const bool is_k = (TL::KU % kThreads == 0) ? (i < TL::KU / kThreads) : (u0 < TL::KU);
+      __builtin_amdgcn_global_load_lds(is_k ? ksrc : vsrc_u, IA_LDS(buf + 8 * u0), 16, 0, 0);
+    }
+  };
+  // M^T of the segment, swizzled like a K tile.
+  auto dma_mem = [&]() {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) load_cols<TL::VC>(vt + r * D, vreg[r]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < TL::KCH; ++r) {
-        const int row = (tid + kThreads * r) / (D / 8);
-        if (tid + kThreads * r < TL::KCHUNKS)
-          kreg[r] = (kv0 + row < e)
-                        ? *reinterpret_cast<const u32x4 *>(kt + koff + r * KROWS * D)
-                        : u32x4{0u, 0u, 0u, 0u};
-      }
-      if (v_has) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (kv0 + 4 * v_kg + r < e) {
-            load_cols<TL::VC>(vt + r * D, vreg[r]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < TL::VC / 2; ++i) vreg[r][i] = 0u;
-          }
-        }
+    for (int i = 0; i < TL::MPW; ++i) {
+      const int u0 = (8 * i + w) * 64;
+      if (u0 < TL::MU) {
+        const int U = u0 + lane;
+        const int r = U / TL::CPR, cp = U % TL::CPR;
+        const int c = cp ^ ((r / TL::RP) % TL::CPR);
+        __builtin_amdgcn_global_load_lds(mt + static_cast<size_t>(r) * D + 8 * c,
+                                         IA_LDS(sM + 8 * u0), 16, 0, 0);
       }
     }
   };
 
-  // Key group kg (keys 4 kg .. 4 kg + 3 of the tile) = 16-key step kg / 4,
-  // run h = (kg / 2) % 2, lane group g = kg % 2 of the S^T layout; it is
-  // stored at 4-key position (kg / 4, g, h), i.e. bits 0 and 1 swapped.
-  const int v_pos = 4 * ((v_kg & ~3) | ((v_kg & 1) << 1) | ((v_kg >> 1) & 1));
-
-  auto store_tile = [&](uint16_t *sK, uint16_t *sVt) {
+  // Per-lane LDS offsets (bf16 elements) of the MFMA operands: K row l32 (+32
+  // for the second key half), unit 2 t + g; V^T row l32 (+32 dt), unit 2 tu + g.
+  int koff[NT];
 #pragma unroll
-    for (int r = 0; r < TL::KCH; ++r) {
-      const int c = tid + kThreads * r;
-      if (c < TL::KCHUNKS) {
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        *reinterpret_cast<u32x4 *>(sK + row * TL::KSTR + col8 * 8) = kreg[r];
-      }
-    }
-    if (v_has) {
-      // Transpose 4 rows x VC columns: one 8-byte write of 4 keys per column.
-      // v_perm picks the low (resp. high) bf16 of two rows into one word.
+  for (int t = 0; t < NT; ++t) koff[t] = 8 * swz_unit<D>(l32, 2 * t + g);
+  int voff[4];
 #pragma unroll
-      for (int i = 0; i < TL::VC / 2; ++i) {
-        const uint32_t r0 = vreg[0][i], r1 = vreg[1][i], r2 = vreg[2][i], r3 = vreg[3][i];
-        const u32x2 lo = {__builtin_amdgcn_perm(r1, r0, 0x05040100u),
-                          __builtin_amdgcn_perm(r3, r2, 0x05040100u)};
-        const u32x2 hi = {__builtin_amdgcn_perm(r1, r0, 0x07060302u),
-                          __builtin_amdgcn_perm(r3, r2, 0x07060302u)};
-        const int col = v_cc * TL::VC + 2 * i;
-        *reinterpret_cast<u32x2 *>(sVt + col * TL::VSTR + v_pos) = lo;
-        *reinterpret_cast<u32x2 *>(sVt + (col + 1) * TL::VSTR + v_pos) = hi;
-      }
-    }
-  };
+  for (int tu = 0; tu < 4; ++tu) voff[tu] = 8 * (TL::KU + l32 * 8 + vt_unit_pos(l32, 2 * tu + g));
 
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
-  load_tile(a);
-  store_tile(smem, smem + kBN * TL::KSTR);
-  __syncthreads();
-  int buf = 0;
-  for (int kv0 = a; kv0 < kv_end; kv0 += kBN) {
-    const uint16_t *sK = smem + buf * TL::BUF;
-    const uint16_t *sVt = sK + kBN * TL::KSTR;
-    const bool has_next = kv0 + kBN < kv_end;
-    if (has_next) load_tile(kv0 + kBN);  // global loads in flight during the MFMAs
+  auto compute = [&](int kv0, const uint16_t *buf) {
+    // S^T tile pair: rows = keys kv0 + 32T + ..., columns = this wave's
+    // queries; two independent accumulation chains, interleaved.
+    f32x16 st[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 ka0 = *reinterpret_cast<const u32x4 *>(buf + koff[t]);
+      const u32x4 ka1 = *reinterpret_cast<const u32x4 *>(buf + koff[t] + 32 * D);
+      st[0] = mfma32(as_bf16x8(ka0), as_bf16x8(qf[t]), st[0]);
+      st[1] = mfma32(as_bf16x8(ka1), as_bf16x8(qf[t]), st[1]);
+    }
+    // Mask future keys and keys past the segment end (diagonal tiles only).
+    if ((kv0 + kBN - 1 > qw) || (kv0 + kBN > e)) {
+      __asm__ volatile("" ::: "memory");  // keep this a branch (diagonal tiles only)
+      const int lim = min(qrow, e - 1) - kv0 - 4 * g;  // key offsets above lim are masked
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (32 * T + (i >> 2) * 8 + (i & 3) > lim) st[T][i] = -INFINITY;
+        }
+      }
+    }
+    float mx = fmaxf(st[0][0], st[1][0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(st[0][i], st[1][i]));
+    mx = max_xor32(mx) * scale_log2;  // finite: key a is always visible
+    const bool grow = mx > m + kLazy;
+    if (__any(grow)) {
+      __asm__ volatile("" ::: "memory");  // keep this a branch (rarely taken)
+      const float m_new = grow ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 1 where m stays
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+    }
+    // p = 2^(s c - m) rounded to bf16; the row sum is taken over the same
+    // rounded values (bf16 dot2 with ones), so numerator and denominator
+    // of the softmax see identical weights. O^T += V^T P^T as soon as each
+    // 16-key group of P is packed: pair idx holds elements 2 (idx % 8), +1
+    // of the 32-key half idx / 8, and group tu = idx / 4 is the P operand of
+    // key step tu (slot j of lane group g is key 16 tu + 8 (j / 4) + 4 g +
+    // j % 4, matching the S^T result layout and the V^T tile's unit order).
+    const float neg_m = -m;
+#pragma unroll
+    for (int tu = 0; tu < 4; ++tu) {
+      u32x4 va[ND];
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+        va[dt] = *reinterpret_cast<const u32x4 *>(buf + voff[tu] + 32 * dt * 64);
+      uint32_t pw[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int idx = 4 * tu + jj;
+        const int T = idx >> 3, i = 2 * (idx & 7);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][i], scale_log2, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][i + 1], scale_log2, neg_m));
+        pw[jj] = pack_bf16x2(p0, p1);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[jj]), ones, lsum,
+                                               false);
+      }
+      const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) o[dt] = mfma32(as_bf16x8(va[dt]), as_bf16x8(pb), o[dt]);
+    }
+  };
 
-    if (wave_live && kv0 <= qw + 31) {
-      // S^T tile pair: rows = keys kv0 + 32T + ..., columns = this wave's
-      // queries; two independent accumulation chains, interleaved.
-      f32x16 st[2] = {f32x16{}, f32x16{}};
-      const uint16_t *krow = sK + l32 * TL::KSTR + 8 * g;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x4 ka0 = *reinterpret_cast<const u32x4 *>(krow + 16 * t);
-        const u32x4 ka1 = *reinterpret_cast<const u32x4 *>(krow + 32 * TL::KSTR + 16 * t);
-        st[0] = mfma32(as_bf16x8(ka0), as_bf16x8(qf[t]), st[0]);
-        st[1] = mfma32(as_bf16x8(ka1), as_bf16x8(qf[t]), st[1]);
-      }
-      // Mask future keys and keys past the segment end (diagonal tiles only).
-      if ((kv0 + kBN - 1 > qw) || (kv0 + kBN > e)) {
-        __asm__ volatile("" ::: "memory");  // keep this a branch (diagonal tiles only)
-        const int lim = min(qrow, e - 1) - kv0 - 4 * g;  // key offsets above lim are masked
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            if (32 * T + (i >> 2) * 8 + (i & 3) > lim) st[T][i] = -INFINITY;
-          }
-        }
-      }
-      float mx = fmaxf(st[0][0], st[1][0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(st[0][i], st[1][i]));
-      mx = max_xor32(mx) * scale_log2;  // finite: key a is always visible
-      const bool grow = mx > m + kLazy;
-      if (__any(grow)) {
-        __asm__ volatile("" ::: "memory");  // keep this a branch (rarely taken)
-        const float m_new = grow ? mx : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 1 where m stays
-        m = m_new;
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
-      }
-      // p = 2^(s c - m) rounded to bf16; the row sum is taken over the same
-      // rounded values (bf16 dot2 with ones), so numerator and denominator
-      // of the softmax see identical weights. O^T += V^T P^T as soon as each
-      // 16-key group of P is packed: pair idx holds elements 2 (idx % 8), +1
-      // of the 32-key half idx / 8, and group tu = idx / 4 is the P operand of
-      // key step tu (slot j of lane group g is key 16 tu + 8 (j / 4) + 4 g +
-      // j % 4, matching the S^T result layout; sVt holds it at position
-      // 16 tu + 8 g + j).
-      const float neg_m = -m;
-      const uint16_t *vrow = sVt + l32 * TL::VSTR + 8 * g;
-#pragma unroll
-      for (int tu = 0; tu < 4; ++tu) {
-        // The V fragments of this key step are read first, so their LDS
-        // latency overlaps the exponentials.
-        u32x4 va[ND];
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-          va[dt] = *reinterpret_cast<const u32x4 *>(vrow + 32 * dt * TL::VSTR + 16 * tu);
-        uint32_t pw[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int idx = 4 * tu + jj;
-          const int T = idx >> 3, i = 2 * (idx & 7);
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][i], scale_log2, neg_m));
-          const float p1 =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][i + 1], scale_log2, neg_m));
-          pw[jj] = pack_bf16x2(p0, p1);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[jj]), ones, lsum,
-                                                 false);
-        }
-        const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) o[dt] = mfma32(as_bf16x8(va[dt]), as_bf16x8(pb), o[dt]);
-      }
-    }
-    if (has_next) {
-      // The idle buffer was last read before the previous barrier.
-      uint16_t *nK = smem + (buf ^ 1) * TL::BUF;
-      store_tile(nK, nK + kBN * TL::KSTR);
-    }
-    __syncthreads();
-    buf ^= 1;
+  // Iteration t: direct loads of tile t + 2 into the buffer tile t - 1 left
+  // (past the end, the last tile again: every iteration issues the same
+  // loads, so issue and wait form one pattern whose count the compiler's own
+  // wait analysis can follow; nothing reads that buffer before it is
+  // reloaded); the tile's MFMAs; then this wave's loads of tile t + 1 are
+  // awaited and the workgroup meets at the barrier that publishes them.
+  //
+  // The compiler's wait analysis loses track of which buffer a direct load
+  // targets where control flow merges (the loop head) and waits for all of
+  // them before the next LDS read; the first iteration after the loop head
+  // therefore issues its loads after its MFMAs (LATE), so that this wait
+  // covers only tile t + 1, issued a whole tile earlier.
+  auto step = [&](auto late, int t, const uint16_t *cur, uint16_t *nx2) {
+    if (!late.value) dma_tile(min(t + 2, n_tiles - 1), nx2);
+    const int kv0 = a + t * kBN;
+    if (wave_live && kv0 <= qw + 31) compute(kv0, cur);
+    if (late.value) dma_tile(min(t + 2, n_tiles - 1), nx2);
+    wait_vm_lgkm0<TL::IPW>();
+    __builtin_amdgcn_s_barrier();
+  };
+  using LATE = std::true_type;
+  using EARLY = std::false_type;
+
+  // M^T first (its own buffer, needed only after the loop), then tiles 0, 1.
+  dma_mem();
+  dma_tile(0, sB0);
+  dma_tile(min(1, n_tiles - 1), sB1);
+  wait_vm_lgkm0<TL::IPW>();
+  __builtin_amdgcn_s_barrier();
+  for (int t = 0;;) {
+    step(LATE{}, t, sB0, sB2);
+    if (++t >= n_tiles) break;
+    step(EARLY{}, t, sB1, sB0);
+    if (++t >= n_tiles) break;
+    step(EARLY{}, t, sB2, sB1);
+    if (++t >= n_tiles) break;
   }
 
   // ---- retrieval from the pre-segment snapshot and the gate ----
-  const size_t head = static_cast<size_t>(b) * Hkv + hk;
-  const uint16_t *mt = mt_pre + (head * S + s) * D * D;
-  const float *zs = z_pre + (head * (S + 1) + s) * D;
-  // (the loop ended with a barrier: smem is free for M^T)
-  for (int c = tid; c < D * D / 8; c += kThreads) {
-    const int row = c / (D / 8), col8 = c % (D / 8);
-    *reinterpret_cast<u32x4 *>(smem + row * TL::MSTR + col8 * 8) =
-        *reinterpret_cast<const u32x4 *>(mt + static_cast<size_t>(row) * D + col8 * 8);
-  }
-  if (tid < D) sZ[tid] = zs[tid];
+  if (tid < D) sZ[tid] = zreg;
+  wait_vm_lgkm0<0>();
   __syncthreads();
 
   if (!wave_live) return;
@@ -390,8 +392,8 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     f32x16 am = f32x16{};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const u32x4 ma = *reinterpret_cast<const u32x4 *>(smem + (32 * dt + l32) * TL::MSTR +
-                                                       16 * t + 8 * g);
+      const u32x4 ma =
+          *reinterpret_cast<const u32x4 *>(sM + 8 * swz_unit<D>(32 * dt + l32, 2 * t + g));
       am = mfma32(as_bf16x8(ma), as_bf16x8(sq[t]), am);
     }
     if (qrow < e) {
@@ -422,8 +424,8 @@ hipError_t launch_t(const Geometry &g, const uint16_t *q, const uint16_t *k, con
   const int xcd_chunk = (nblk % kXcds == 0) ? static_cast<int>(nblk / kXcds) : 0;
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   fused_bf16_kernel<D, HPW><<<dim3(static_cast<unsigned>(nblk)), kThreads, 0, stream>>>(
-      q, k, v, beta, ws.z_pre, ws.mt_pre_bf16, out, g.Hq, g.Hkv, g.L, g.N, g.S, n_qt, g.eps,
-      scale_log2, xcd_chunk);
+      q, k, ws.vt, ws.vt_tiles, beta, ws.z_pre, ws.mt_pre_bf16, out, g.Hq, g.Hkv, g.L, g.N, g.S,
+      n_qt, g.eps, scale_log2, xcd_chunk);
   return hipGetLastError();
 }
 

@@ -59,9 +59,13 @@ int n_segments(int L, int N) { return L == 0 ? 0 : (L + N - 1) / N; }
 //   mt_pre [B*Hkv][S][D][D]       fp32 or bf16 by storage type
 //   dz     [B*Hkv][S][P][D] fp32  (bf16 storage only; P = z_parts(N) row ranges)
 //   gh     [B*Hkv][S][2][D][D] fp32 (bf16 storage only)
+//   vt     [B*Hkv][S][T][D][64] bf16 (bf16 storage only; T = ceil(N / 64)
+//          64-key tiles per segment, V^T in the fused kernel's LDS layout)
 struct WsLayout {
-  size_t z, mt, dz, gh, total;
+  size_t z, mt, dz, gh, vt, total;
 };
+
+int vt_tiles(int N) { return (N + 63) / 64; }
 
 // Row ranges per segment for the sigma(k) column sums: about 512 rows each.
 int z_parts(int N) {
@@ -78,7 +82,8 @@ WsLayout ws_layout(const infini_attn_desc *d, int S, int N) {
   w.mt = round_up(heads * S * D * D * (bf16 ? sizeof(uint16_t) : sizeof(float)));
   w.dz = bf16 ? round_up(heads * S * z_parts(N) * D * sizeof(float)) : 0;
   w.gh = bf16 ? round_up(heads * S * 2 * D * D * sizeof(float)) : 0;
-  w.total = w.z + w.mt + w.dz + w.gh;
+  w.vt = bf16 ? round_up(heads * S * vt_tiles(N) * D * 64 * sizeof(uint16_t)) : 0;
+  w.total = w.z + w.mt + w.dz + w.gh + w.vt;
   return w;
 }
 
@@ -198,6 +203,8 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
   ws.dz = bf16 ? reinterpret_cast<float *>(base + lay.z + lay.mt) : nullptr;
   ws.z_parts = z_parts(g.N);
   ws.gh = bf16 ? reinterpret_cast<float *>(base + lay.z + lay.mt + lay.dz) : nullptr;
+  ws.vt = bf16 ? reinterpret_cast<uint16_t *>(base + lay.z + lay.mt + lay.dz + lay.gh) : nullptr;
+  ws.vt_tiles = vt_tiles(g.N);
 
   TimedCall tc{};
   if (h->timing) {

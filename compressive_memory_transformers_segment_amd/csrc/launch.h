@@ -25,7 +25,18 @@ struct Workspace {
   float *dz;              // [B*Hkv][S][z_parts][D] partial sums of sigma(k) (bf16 path)
   int z_parts;            // row ranges per segment in dz
   float *gh;              // [B*Hkv][S][2][D*D] G_s, H_s in MFMA fragment order (bf16 path)
+  uint16_t *vt;           // [B*Hkv][S][vt_tiles][D*64] V^T per 64-key tile (bf16 path)
+  int vt_tiles;           // 64-key tiles per segment, ceil(N / 64)
 };
+
+// Layout of one 64-key V^T tile (bf16 path), written by the scan and copied
+// verbatim into LDS by the fused kernel. Row d (one per value column) holds
+// the tile's 64 keys as 8 units of 16 bytes. Unit q of the row holds the
+// keys of 16-key step q / 2 that lane group q % 2 of a 32x32x16 MFMA operand
+// contributes: keys 16 (q/2) + 4 (q%2) + {0..3} and 16 (q/2) + 8 + 4 (q%2) +
+// {0..3}. Unit q is stored at position q ^ ((d / 2) % 8) of the row, so that
+// 16 consecutive rows read at one unit index hit distinct LDS banks.
+__host__ __device__ inline int vt_unit_pos(int d, int q) { return q ^ ((d >> 1) & 7); }
 
 // Segment scan, fp32 storage: carries fp32 (M, z) across segments for every
 // (b, kv head) on VALU, writing the pre-segment snapshots (z_pre, mt_pre_f32)

@@ -16,7 +16,9 @@
 //   zprefix (head)              z_{s-1} for every s, and z_S                  [VALU]
 //   gh      (segment, head)     G_s (delta only) and H_s, contraction over    [MFMA bf16]
 //                               the segment's rows, stored in MFMA fragment
-//                               order: H_s as fp32, G_s as a bf16 hi/lo pair
+//                               order: H_s as fp32, G_s as a bf16 hi/lo pair;
+//                               also writes the segment's V^T in 64-key tiles
+//                               (the fused kernel's LDS layout)
 //   seq     (column tile, head) M_s = M_{s-1} - G_s M_{s-1} + H_s with the    [MFMA bf16 x3]
 //                               product as G_hi M_hi + G_hi M_lo + G_lo M_hi
 //                               (about 16 mantissa bits); fp32 state in
@@ -165,8 +167,9 @@ template <int D, bool DELTA, int CS>
 __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
                                                  const uint16_t *__restrict__ v,
                                                  const float *__restrict__ z_pre,
-                                                 float *__restrict__ gh, int L, int N, int S,
-                                                 float eps) {
+                                                 float *__restrict__ gh,
+                                                 uint16_t *__restrict__ vt, int vt_tiles, int L,
+                                                 int N, int S, float eps) {
   constexpr int ND = D / 32;
   constexpr int CCH = D / 8;            // 8-column chunks per row
   constexpr int ITEMS = 16 * CCH;       // staging items: 4 rows x 8 columns each
@@ -285,6 +288,20 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
     }
     __syncthreads();
     if (i0 + 128 < e) load_chunk(cur, i0 + 128);  // cur is free once staged
+    if (cs == 0) {
+      // V^T of this 64-key chunk (rows past the segment end are zero), in the
+      // unit order and bank swizzle of vt_unit_pos.
+      uint16_t *vtile =
+          vt + ((static_cast<size_t>(head) * S + s) * vt_tiles + (i0 - a) / 64) * (D * 64);
+      for (int u = tid; u < D * 8; u += 256) {
+        const int d = u >> 3;
+        const int q = vt_unit_pos(d, u & 7);  // the swizzle is its own inverse
+        const int k0 = 16 * (q >> 1) + 4 * (q & 1);
+        const u32x2 r0 = *reinterpret_cast<const u32x2 *>(sVt + d * kStr + k0);
+        const u32x2 r1 = *reinterpret_cast<const u32x2 *>(sVt + d * kStr + k0 + 8);
+        *reinterpret_cast<u32x4 *>(vtile + u * 8) = u32x4{r0[0], r0[1], r1[0], r1[1]};
+      }
+    }
 
     // Contraction over the 64 keys of the chunk, 16 per MFMA. Slot j of lane
     // group g is key kb + 8 (j / 4) + 4 g + j % 4 in both operands.
@@ -493,19 +510,19 @@ hipError_t launch_d(const Geometry &g, const uint16_t *k, const uint16_t *v, flo
   zprefix_kernel<<<heads, kZThreads, 0, stream>>>(z, ws.dz, ws.z_pre, g.S, D, parts);
   if (delta) {
     if (split)
-      gh_kernel<D, true, 2><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, g.L, g.N, g.S,
-                                                        g.eps);
+      gh_kernel<D, true, 2><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+                                                        ws.vt_tiles, g.L, g.N, g.S, g.eps);
     else
-      gh_kernel<D, true, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, g.L, g.N, g.S,
-                                                        g.eps);
+      gh_kernel<D, true, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+                                                        ws.vt_tiles, g.L, g.N, g.S, g.eps);
     seq_kernel<D, true><<<seqgrid, 64 * (D / 32), 0, stream>>>(ws.gh, M, ws.mt_pre_bf16, g.S);
   } else {
     if (split)
-      gh_kernel<D, false, 2><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, g.L, g.N, g.S,
-                                                         g.eps);
+      gh_kernel<D, false, 2><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+                                                         ws.vt_tiles, g.L, g.N, g.S, g.eps);
     else
-      gh_kernel<D, false, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, g.L, g.N, g.S,
-                                                         g.eps);
+      gh_kernel<D, false, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+                                                         ws.vt_tiles, g.L, g.N, g.S, g.eps);
     seq_kernel<D, false><<<seqgrid, 64 * (D / 32), 0, stream>>>(ws.gh, M, ws.mt_pre_bf16, g.S);
   }
   return hipGetLastError();

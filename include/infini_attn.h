@@ -87,7 +87,9 @@ int infini_attn_check(const infini_attn_desc *desc, int32_t seg_len, int32_t upd
  * Bytes of device workspace a handle with this descriptor allocates for a
  * forward call with this segment length: the per-segment state snapshots
  * (M_{s-1}, z_{s-1}) that the segment-scan kernel writes and the fused
- * attention kernel reads. Writes the size to *bytes. Host only.
+ * attention kernel reads, and for bf16 storage the scan's per-segment
+ * statistics and a transposed copy of V in 64-key tiles. Writes the size to
+ * *bytes. Host only.
  */
 int infini_attn_workspace_size(const infini_attn_desc *desc, int32_t seg_len, size_t *bytes);
 
