@@ -128,8 +128,8 @@ def cpu_baseline(w, inp, mode: str, budget_s: float) -> dict:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b_gqa")
     ap.add_argument("--mode", default="delta", choices=["linear", "delta"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -432,7 +432,9 @@ hipError_t launch_t(const Geometry &g, const uint16_t *q, const uint16_t *k, con
 template <int D>
 hipError_t launch_d(const Geometry &g, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                     const float *beta, const Workspace &ws, uint16_t *out, hipStream_t stream) {
-  // Share each K / V tile across two query heads when they read the same kv head.
+  // Share each K / V tile across up to four query heads that read the same kv
+  // head (64 rows each); otherwise two heads of 128 rows or one of 256.
+  if ((g.Hq / g.Hkv) % 4 == 0) return launch_t<D, 4>(g, q, k, v, beta, ws, out, stream);
   if ((g.Hq / g.Hkv) % 2 == 0) return launch_t<D, 2>(g, q, k, v, beta, ws, out, stream);
   return launch_t<D, 1>(g, q, k, v, beta, ws, out, stream);
 }

@@ -61,6 +61,20 @@ def test_ragged_multi_tile(dtype, d, mode):
               run_oracle(inp, dtype, 300, mode), dtype)
 
 
+# Query-head groups: 4 and 8 heads per kv head (four heads share each
+# workgroup's K / V tiles), 6 (two), 3 (one).
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 2), (6, 2), (3, 1)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_grouped_heads(hq, hkv, d):
+    betas = np.linspace(-2.0, 2.0, hq).astype(np.float32)
+    inp = synth.random_case(300 + 10 * hq + d, B=1, Hq=hq, Hkv=hkv, L=700, dk=d, dv=d,
+                            dtype="bf16", beta=betas, nonzero_state=True,
+                            scale=1.5 / np.sqrt(d) * 4)
+    log(f"grouped Hq={hq} Hkv={hkv} d={d}")
+    check_all(f"grouped {hq}/{hkv} d{d}", run_gpu(inp, "bf16", 300, "delta"),
+              run_oracle(inp, "bf16", 300, "delta"), "bf16")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_pure_branches(dtype):
     """beta = -inf isolates local attention; beta = +inf isolates retrieval."""
