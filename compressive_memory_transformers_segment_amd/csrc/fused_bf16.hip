@@ -256,13 +256,24 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     // S^T tile pair: rows = keys kv0 + 32T + ..., columns = this wave's
     // queries; two independent accumulation chains, interleaved.
     f32x16 st[2] = {f32x16{}, f32x16{}};
+    // K fragments are read two k-steps ahead of their MFMAs (two register
+    // sets); the scheduling fences keep the compiler from sinking the reads
+    // next to their uses.
+    u32x4 kf[2][2];
+    auto kread = [&](int t, u32x4 (&kk)[2]) __attribute__((always_inline)) {
+      kk[0] = *reinterpret_cast<const u32x4 *>(buf + koff[t]);
+      kk[1] = *reinterpret_cast<const u32x4 *>(buf + koff[t] + 32 * D);
+    };
+    kread(0, kf[0]);
+    if (NT > 1) kread(1, kf[1]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const u32x4 ka0 = *reinterpret_cast<const u32x4 *>(buf + koff[t]);
-      const u32x4 ka1 = *reinterpret_cast<const u32x4 *>(buf + koff[t] + 32 * D);
-      st[0] = mfma32(as_bf16x8(ka0), as_bf16x8(qf[t]), st[0]);
-      st[1] = mfma32(as_bf16x8(ka1), as_bf16x8(qf[t]), st[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      st[0] = mfma32(as_bf16x8(kf[t & 1][0]), as_bf16x8(qf[t]), st[0]);
+      st[1] = mfma32(as_bf16x8(kf[t & 1][1]), as_bf16x8(qf[t]), st[1]);
+      if (t + 2 < NT) kread(t + 2, kf[t & 1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // Mask future keys and keys past the segment end (diagonal tiles only).
     if ((kv0 + kBN - 1 > qw) || (kv0 + kBN > e)) {
       __asm__ volatile("" ::: "memory");  // keep this a branch (diagonal tiles only)
@@ -297,12 +308,15 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     // key step tu (slot j of lane group g is key 16 tu + 8 (j / 4) + 4 g +
     // j % 4, matching the S^T result layout and the V^T tile's unit order).
     const float neg_m = -m;
+    // V fragments of step tu + 1 are read right after the MFMAs of step tu,
+    // so their latency overlaps the exponentials of step tu + 1.
+    u32x4 vf[2][ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+      vf[0][dt] = *reinterpret_cast<const u32x4 *>(buf + voff[0] + 32 * dt * 64);
 #pragma unroll
     for (int tu = 0; tu < 4; ++tu) {
-      u32x4 va[ND];
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
-        va[dt] = *reinterpret_cast<const u32x4 *>(buf + voff[tu] + 32 * dt * 64);
+      u32x4 (&va)[ND] = vf[tu & 1];
       uint32_t pw[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -315,8 +329,16 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
                                                false);
       }
       const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) o[dt] = mfma32(as_bf16x8(va[dt]), as_bf16x8(pb), o[dt]);
+      if (tu + 1 < 4) {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+          vf[(tu + 1) & 1][dt] =
+              *reinterpret_cast<const u32x4 *>(buf + voff[tu + 1] + 32 * dt * 64);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
