@@ -225,7 +225,9 @@ def main(argv=None) -> int:
         "hbm_gbs_algorithmic": wc["bytes"] * args.steps / elapsed / 1e9,
         "kernels_ms": {"segment_scan": scan_avg_s * 1e3, "fused_attention": fused_avg_s * 1e3},
         "roofline": {
-            "kernel": "fused_bf16_kernel<128>" if w.d == 128 else f"fused kernel d={w.d}",
+            "kernel": (f"fused_bf16_kernel<{w.d}, "
+                       f"{4 if (w.n_q_heads // w.n_kv_heads) % 4 == 0 else 2 if (w.n_q_heads // w.n_kv_heads) % 2 == 0 else 1}>"
+                       if w.dtype == "bf16" else f"fused_f32_kernel<{w.d}>"),
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
