@@ -23,35 +23,46 @@
 //     layout of the second (the key index is the contraction index of P V, and
 //     the order in which the hardware walks a contraction does not matter as
 //     long as both operands agree).
-//   * Q stays in registers for the whole key loop (its d-contiguous rows are
-//     exactly the B operand of S^T = K Q^T).
-//   * Tiles move from HBM to LDS by direct loads (global_load_lds: no
-//     register staging, no LDS store instructions) through a ring of three
-//     buffers: tile t + 2 is in flight while tile t is consumed, and each
-//     wave waits only for its own loads of tile t + 1 before the one barrier
-//     per key tile. K tiles are row-major with a 16-byte-unit XOR swizzle so
+//   * Q stays in registers for the whole key loop of a work item (its
+//     d-contiguous rows are exactly the B operand of S^T = K Q^T).
+//   * Persistent workgroups (as many as fit on the chip at once) work through
+//     a static schedule of work items (query tile x head unit x segment) that
+//     alternates long and short query tiles, so every workgroup gets about
+//     the same number of key tiles. All data a workgroup needs moves from HBM
+//     to LDS by direct loads (global_load_lds: no register staging, no LDS
+//     store instructions) through a ring of three buffers, as one continuous
+//     stream of slots across items: per item its key tiles (padded to a
+//     multiple of three slots), M^T of the segment, then the next item's Q
+//     rows. The loads run two slots ahead of the work, so the next item's Q,
+//     tiles and snapshot are in flight while the current one finishes and no
+//     item waits for its inputs. Each wave waits only for its own loads of the
+//     next slot before the one barrier per slot.
+//   * K tiles (and M^T, Q) are row-major with a 16-byte-unit XOR swizzle so
 //     that the 32 rows an MFMA operand reads hit distinct banks. V arrives
 //     already transposed, [d][key], from the segment scan, which writes it per
 //     64-key tile with the keys of each 16-key step permuted so that the 8
 //     keys a lane contributes to one O^T = V^T P^T MFMA (two runs of 4 in the
 //     S^T result layout) are adjacent and bank-swizzled: every MFMA operand
 //     read from LDS is one 16-byte read.
-//   * Causal skipping: a workgroup visits key tiles up to its last query row;
-//     a wave skips tiles entirely in its future and masks only diagonal tiles.
+//   * Causal skipping: an item visits key tiles up to its last query row; a
+//     wave skips tiles entirely in its future and masks only diagonal tiles.
 //   * Online softmax with a lazy rescale: the running max m of a row moves
 //     (and O, l are rescaled) only when a tile's max exceeds m by more than
 //     kLazy (log2 units), so probabilities stay <= 2^kLazy and most tiles skip
 //     the rescale. The 1/sqrt(d) scale is folded into the exponent's FMA, and
 //     the row sum is a bf16 dot2 over the same rounded P the MFMA consumes.
 //     The kernel runs with the IEEE mode bit off (no NaN quieting on max).
-//   * Block order is remapped so that consecutive work items share an XCD
-//     (blocks are dealt round-robin to the 8 XCDs): the query heads that read
-//     one kv head land on one XCD and share its L2.
-//   * Epilogue: the pre-segment snapshot M^T (bf16, [d_v][d_k]) arrives in its
-//     own LDS buffer by direct loads ahead of the first key tile, once for all
-//     heads of the workgroup, and is multiplied with sigma(Q)
-//     (computed from the Q registers) on MFMA; the denominator sigma(Q).z is a
-//     per-lane dot product plus one exchange.
+//   * In every round the workgroups of one XCD (workgroups are dealt
+//     round-robin to the 8 XCDs) take consecutive items: the query tiles that
+//     read one kv head's segment share that XCD's L2.
+//   * Epilogue: the pre-segment snapshot M^T (bf16, [d_v][d_k]) arrives as a
+//     ring slot, once for all heads of the workgroup, and is multiplied with
+//     sigma(Q) (computed in place of the Q registers) on MFMA; the
+//     denominator sigma(Q).z is a per-lane dot product plus one exchange (z
+//     and the gate parameters travel in a side area of the snapshot's slot).
+//     Rows are stored through a buffer resource that ends at the segment end,
+//     so every wave issues the same stores and the hardware drops those past
+//     it.
 
 #include <type_traits>
 
@@ -101,18 +112,19 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 template <int D>
 struct Tile {
-  static constexpr int CPR = D / 8;          // 16-byte units per K (and M^T) row
+  static constexpr int CPR = D / 8;          // 16-byte units per K (and M^T, Q) row
   static constexpr int RP = 16 / CPR;        // K rows per 256-byte bank line
   static constexpr int KU = kBN * CPR;       // K units per tile
   static constexpr int VU = D * 8;           // V^T units per tile (64 keys per row)
-  static constexpr int BUFU = KU + VU;       // units per ring buffer
-  static constexpr int BUF = BUFU * 8;       // bf16 per ring buffer
-  static constexpr int IPW = BUFU / kThreads;  // direct loads per wave per tile
+  static constexpr int BUFU = KU + VU;       // 16-byte units per ring slot
+  static constexpr int SIDE = kWaves * 64;   // floats in a slot's side area (z, beta)
+  static constexpr int BUF = BUFU * 8 + 2 * SIDE;  // bf16 per ring slot
+  static constexpr int IPW = BUFU / kThreads;  // 16-byte direct loads per wave per slot
   static constexpr int MU = D * CPR;         // M^T units
-  static constexpr int MPW = (MU + kThreads - 1) / kThreads;  // direct loads per wave for M^T
   static_assert(BUFU % kThreads == 0, "whole direct loads per wave");
   static_assert(KU % 64 == 0, "a direct load never straddles K and V^T");
-
+  static_assert(4 * 32 * CPR == BUFU, "the Q rows of four waves fill one slot");
+  static_assert(MU <= BUFU, "M^T fits one slot");
 };
 
 // 16-byte unit of (row r, unit c) in a swizzled row-major tile of D columns
@@ -124,25 +136,77 @@ __device__ __forceinline__ int swz_unit(int r, int c) {
   return r * TL::CPR + (c ^ ((r / TL::RP) % TL::CPR));
 }
 
+// One work item of the persistent schedule: a query tile of one head unit
+// (HPW query heads of one kv head) in one segment. Uniform across the
+// workgroup.
+struct FusedItem {
+  int k;     // round of the item in its workgroup's schedule; -1 past the last item
+  int a, e;  // rows [a, e) of the segment
+  int q0;    // first query row of the tile
+  int T;     // key tiles under the causal mask
+  int bq;    // b * Hq + first query head of the head unit
+  int head;  // b * Hkv + kv head
+  int s;     // segment index
+};
+
+// Round k gives the workgroup in slot r item k G + r on even rounds and
+// k G + G - 1 - r on odd ones. Items are ordered with the query tile fastest
+// and longest first, so a workgroup alternates long and short query tiles;
+// items without rows (short last segment) are skipped.
+template <int HPW>
+__device__ __forceinline__ FusedItem fused_item(int k, int G, int r, int n_items, int n_qt, int S,
+                                                int N, int L, int Hq, int Hkv) {
+  constexpr int BM = 32 * kWaves / HPW;
+  const int grp = Hq / Hkv;
+  const int units = grp / HPW;
+  FusedItem it;
+  for (;; ++k) {
+    const long long jl = static_cast<long long>(k) * G + ((k & 1) ? G - 1 - r : r);
+    if (jl >= n_items) {
+      it.k = -1;
+      it.a = it.e = it.q0 = it.T = it.bq = it.head = it.s = 0;
+      return it;
+    }
+    const int j = static_cast<int>(jl);
+    const int qt = n_qt - 1 - j % n_qt;
+    const int s = (j / n_qt) % S;
+    const int unit = j / (n_qt * S);
+    const int a = s * N;
+    const int e = min(a + N, L);
+    const int q0 = a + qt * BM;
+    if (q0 >= e) continue;
+    const int b = unit / (Hkv * units);
+    const int hk = (unit / units) % Hkv;
+    // The fields are uniform by construction; readfirstlane states it, so
+    // that they live in scalar registers.
+    it.k = __builtin_amdgcn_readfirstlane(k);
+    it.a = __builtin_amdgcn_readfirstlane(a);
+    it.e = __builtin_amdgcn_readfirstlane(e);
+    it.q0 = __builtin_amdgcn_readfirstlane(q0);
+    it.T = __builtin_amdgcn_readfirstlane((min(q0 + BM, e) - a + kBN - 1) / kBN);
+    it.bq = __builtin_amdgcn_readfirstlane(b * Hq + hk * grp + (unit % units) * HPW);
+    it.head = __builtin_amdgcn_readfirstlane(b * Hkv + hk);
+    it.s = __builtin_amdgcn_readfirstlane(s);
+    return it;
+  }
+}
+
 template <int D, int HPW>
 __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ vt, int vt_tiles, const float *__restrict__ beta,
     const float *__restrict__ z_pre, const uint16_t *__restrict__ mt_pre,
-    uint16_t *__restrict__ out, int Hq, int Hkv, int L, int N, int S, int n_qt, float eps,
-    float scale_log2, int xcd_chunk) {
+    uint16_t *__restrict__ out, int Hq, int Hkv, int L, int N, int S, int n_qt, int n_items,
+    float eps, float scale_log2) {
   using TL = Tile<D>;
   constexpr int NT = D / 16;          // k-steps over d
   constexpr int ND = D / 32;          // 32-row d tiles of O^T
   constexpr int RW = kWaves / HPW;    // waves (32-row strips) per head
-  constexpr int BM = 32 * RW;         // query rows per workgroup
-  // Three separate arrays, so that the compiler can tell the buffers apart
-  // when it orders LDS reads after direct loads into another buffer.
+  // Three separate arrays, so that the compiler can tell the ring slots apart
+  // when it orders LDS reads after direct loads into another slot.
   __shared__ __attribute__((aligned(16))) uint16_t sB0[TL::BUF];
   __shared__ __attribute__((aligned(16))) uint16_t sB1[TL::BUF];
   __shared__ __attribute__((aligned(16))) uint16_t sB2[TL::BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sM[TL::MU * 8];
-  __shared__ float sZ[D];
   const int tid = threadIdx.x;
   // The wave index is uniform across the wave; readfirstlane puts it (and all
   // per-wave bounds derived from it) in scalar registers, so the mask and
@@ -151,92 +215,96 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   const int lane = tid & 63;
   const int g = lane >> 5, l32 = lane & 31;
 
-  // Work item: dispatch index -> XCD-contiguous order (when the grid divides
-  // evenly), then (query tile, segment, head unit) with the query tile fastest;
-  // longest query tiles (most key tiles under the mask) first. A head unit is
-  // HPW consecutive query heads of one kv head.
-  int wi = blockIdx.x;
-  if (xcd_chunk > 0) wi = (wi % kXcds) * xcd_chunk + wi / kXcds;
-  const int grp = Hq / Hkv;
-  const int units = grp / HPW;  // head units per kv head
-  const int qt = n_qt - 1 - wi % n_qt;
-  const int s = (wi / n_qt) % S;
-  const int unit = wi / (n_qt * S);
-  const int b = unit / (Hkv * units);
-  const int hk = (unit / units) % Hkv;
-  const int h = hk * grp + (unit % units) * HPW + w / RW;  // this wave's query head
-  const int bhq = b * Hq + h;
-  const int a = s * N;
-  const int e = min(a + N, L);
-  const int q0 = a + qt * BM;
-  if (q0 >= e) return;  // short last segment: whole workgroup idle
-  const int qw = q0 + (w % RW) * 32;  // first query row of this wave
-  const int qrow = qw + l32;          // query row owned by this lane
-  const bool wave_live = qw < e;
+  // Slot of this workgroup in the schedule. Workgroups are dealt round-robin
+  // to the 8 XCDs; when the grid divides evenly, the slots of one XCD are
+  // contiguous, so in every round an XCD works on consecutive items (the
+  // query tiles of one head unit and segment, which read the same K / V
+  // tiles and share that XCD's L2).
+  const int G = gridDim.x;
+  const int r = (G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
+                                 : static_cast<int>(blockIdx.x);
+  auto item = [&](int kk) __attribute__((always_inline)) {
+    return fused_item<HPW>(kk, G, r, n_items, n_qt, S, N, L, Hq, Hkv);
+  };
 
-  const uint16_t *qp = q + static_cast<size_t>(bhq) * L * D;
-  const size_t head = static_cast<size_t>(b) * Hkv + hk;
-  const uint16_t *kp = k + head * L * D;
-  const uint16_t *vtp = vt + (head * S + s) * vt_tiles * (D * 64);  // this segment's V^T tiles
-  const uint16_t *mt = mt_pre + (head * S + s) * D * D;
-  const float *zs = z_pre + (head * (S + 1) + s) * D;
-  const float zreg = tid < D ? zs[tid] : 0.f;
+  // The workgroup's items form one stream of ring slots. Item i with T key
+  // tiles occupies 3 n slots, n = ceil((T + 3) / 3), so that every item starts
+  // at ring buffer 0:
+  //   slots 0 .. T-1        key tiles (K swizzled, V^T as the scan wrote it)
+  //   slots T .. 3n-4       padding (no work; the last tile is loaded again)
+  //   slot 3n-3             M^T of the segment (swizzled like K)
+  //   slots 3n-2, 3n-1      Q rows of the next item for waves 0..3, 4..7
+  //                         (32 rows per wave, swizzled like K)
+  // (the first item's Q slots come before its first tile). Every slot also
+  // carries a side area of one float per lane of every wave: z of the item's
+  // segment (waves 0..6) and beta of its heads (wave 7). Loads run two slots
+  // ahead of the work.
+  FusedItem cur = item(0);
+  if (cur.k < 0) return;
 
-  // Q^T operand: k-step t covers d in [16t, 16t+16); lane holds d = 16t + 8g + 0..7.
-  u32x4 qf[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    qf[t] = (qrow < e) ? *reinterpret_cast<const u32x4 *>(qp + static_cast<size_t>(qrow) * D +
-                                                          16 * t + 8 * g)
-                       : u32x4{0u, 0u, 0u, 0u};
-  }
-
-  f32x16 o[ND];
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x16{};
-  float m = -INFINITY;  // running max of this row, log2 domain
-  float lsum = 0.f;     // running sum over this lane's key slots
-
-  const int kv_end = min(q0 + BM, e);
-
-  const int n_tiles = (kv_end - a + kBN - 1) / kBN;
-
-  // Direct loads: load i of wave w moves units [(8 i + w) 64, +64) of a ring
-  // buffer, one 16-byte unit per lane, into consecutive LDS (the hardware
-  // writes lane l's unit at the wave's LDS base + 16 l). Units below KU are K
-  // (lane picks its source through the swizzle; rows past the segment end
-  // read its last row, whose scores are masked anyway), the rest V^T, copied
-  // verbatim from the scan's tile.
-  auto dma_tile = [&](int t, uint16_t *buf) {
-    const int kv0 = a + t * kBN;
-    const uint16_t *vsrc = vtp + static_cast<size_t>(t) * (D * 64);
+  // Direct loads of one slot: load i of wave w moves units [(8 i + w) 64, +64)
+  // of the slot, one 16-byte unit per lane, into consecutive LDS (the hardware
+  // writes lane l's unit at the wave's LDS base + 16 l). The 64 units of a
+  // load are 512 / D consecutive rows of one 32-row block b_i = (8 i + w) 16 /
+  // D of the slot (uniform per wave); the lane's row within the block and its
+  // swizzled column are the same for every i (the rows a load covers advance
+  // by a multiple of 32, the swizzle period divides 32), so two per-lane
+  // values serve all loads. A source row is min(row0 + lr, rowmax): rows past
+  // the segment end read its last row, whose results are masked or dropped.
+  const int lr = ((w * 64 + lane) / TL::CPR) % 32;
+  const int lcol = 8 * ((lane % TL::CPR) ^ ((((w * 64 + lane) / TL::CPR) / TL::RP) % TL::CPR));
+  auto blk = [&](int i) __attribute__((always_inline)) { return (8 * i + w) * 16 / D; };
+  auto ld = [&](const uint16_t *src, uint16_t *buf, int i) __attribute__((always_inline)) {
+    __builtin_amdgcn_global_load_lds(src, IA_LDS(buf + 8 * (8 * i + w) * 64), 16, 0, 0);
+  };
+  // (The lane values pass through an empty asm statement at each use, so the
+  // compiler does not hoist per-lane addresses out of the loops and keep them
+  // in registers the MFMA work needs.)
+  auto rowsrc = [&](const uint16_t *base, int row0, int rowmax) __attribute__((always_inline)) {
+    int r = lr, c = lcol;
+    __asm__ volatile("" : "+v"(r), "+v"(c));
+    return base + static_cast<size_t>(min(row0 + r, rowmax)) * D + c;
+  };
+  auto linsrc = [&](const uint16_t *base) __attribute__((always_inline)) {
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    return base + 8 * ln;
+  };
+  // Key tile t of an item: K rows swizzled, then V^T copied verbatim.
+  auto dma_tile = [&](const FusedItem &it, int t, uint16_t *buf) __attribute__((always_inline)) {
+    const uint16_t *kp = k + static_cast<size_t>(it.head) * L * D;
+    const uint16_t *vsrc =
+        vt + ((static_cast<size_t>(it.head) * S + it.s) * vt_tiles + t) * (D * 64);
 #pragma unroll
     for (int i = 0; i < TL::IPW; ++i) {
       const int u0 = (8 * i + w) * 64;  // wave-uniform
-      const int U = u0 + lane;
-      const int r = U / TL::CPR, cp = U % TL::CPR;
-      const uint16_t *ksrc =
-          kp + static_cast<size_t>(min(kv0 + r, e - 1)) * D + 8 * (cp ^ ((r / TL::RP) % TL::CPR));
-      const uint16_t *vsrc_u = vsrc + 8 * (U - TL::KU);
       // For D >= 64 the first KU / 512 loads of every wave are K; for D = 32
-      // the first load is K in waves 0..3 and V^T in waves 4..7. A select, not
-      // a branch, so the loads form straight-line code.
+      // the first load is K in waves 0..3 and V^T in waves 4..7.
       const bool is_k = (TL::KU % kThreads == 0) ? (i < TL::KU / kThreads) : (u0 < TL::KU);
-      __builtin_amdgcn_global_load_lds(is_k ? ksrc : vsrc_u, IA_LDS(buf + 8 * u0), 16, 0, 0);
+      ld(is_k ? rowsrc(kp, it.a + t * kBN + 32 * blk(i), it.e - 1)
+              : linsrc(vsrc + 8 * (u0 - TL::KU)),
+         buf, i);
     }
   };
-  // M^T of the segment, swizzled like a K tile.
-  auto dma_mem = [&]() {
+  // M^T of an item's segment, swizzled like K, and the side area (one float
+  // per lane of every wave) with z of the segment (waves 0..6) and beta of the
+  // item's heads (wave 7).
+  auto dma_mem = [&](const FusedItem &it, uint16_t *buf) __attribute__((always_inline)) {
+    const uint16_t *mt = mt_pre + (static_cast<size_t>(it.head) * S + it.s) * D * D;
 #pragma unroll
-    for (int i = 0; i < TL::MPW; ++i) {
-      const int u0 = (8 * i + w) * 64;
-      if (u0 < TL::MU) {
-        const int U = u0 + lane;
-        const int r = U / TL::CPR, cp = U % TL::CPR;
-        const int c = cp ^ ((r / TL::RP) % TL::CPR);
-        __builtin_amdgcn_global_load_lds(mt + static_cast<size_t>(r) * D + 8 * c,
-                                         IA_LDS(sM + 8 * u0), 16, 0, 0);
-      }
+    for (int i = 0; i < TL::IPW; ++i) ld(rowsrc(mt, 32 * blk(i), D - 1), buf, i);  // rows past D (D < 128): unread copies
+    const float *zs = z_pre + (static_cast<size_t>(it.head) * (S + 1) + it.s) * D;
+    const float *side = (w == kWaves - 1) ? beta + it.bq % Hq + (lane < HPW ? lane : 0)
+                                          : zs + (64 * w + lane) % D;
+    __builtin_amdgcn_global_load_lds(side, IA_LDS(buf + TL::BUFU * 8 + 128 * w), 4, 0, 0);
+  };
+  // Q rows of an item for the waves of half `half` (waves 4 half .. 4 half + 3).
+  auto dma_q = [&](const FusedItem &it, int half, uint16_t *buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TL::IPW; ++i) {
+      const int wv = 4 * half + blk(i);  // the wave that reads this block
+      ld(rowsrc(q + static_cast<size_t>(it.bq + wv / RW) * L * D, it.q0 + (wv % RW) * 32, it.e - 1),
+         buf, i);
     }
   };
 
@@ -252,7 +320,14 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
-  auto compute = [&](int kv0, const uint16_t *buf) {
+  // Q^T operand: k-step t covers d in [16t, 16t+16); lane holds d = 16t + 8g + 0..7.
+  u32x4 qf[NT];
+  f32x16 o[ND];
+  float m = -INFINITY;  // running max of this row, log2 domain
+  float lsum = 0.f;     // running sum over this lane's key slots
+
+  auto compute = [&](int kv0, const uint16_t *buf, int qw, int qrow, int e)
+                     __attribute__((always_inline)) {
     // S^T tile pair: rows = keys kv0 + 32T + ..., columns = this wave's
     // queries; two independent accumulation chains, interleaved.
     f32x16 st[2] = {f32x16{}, f32x16{}};
@@ -342,83 +417,64 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     }
   };
 
-  // Iteration t: direct loads of tile t + 2 into the buffer tile t - 1 left
-  // (past the end, the last tile again: every iteration issues the same
-  // loads, so issue and wait form one pattern whose count the compiler's own
-  // wait analysis can follow; nothing reads that buffer before it is
-  // reloaded); the tile's MFMAs; then this wave's loads of tile t + 1 are
-  // awaited and the workgroup meets at the barrier that publishes them.
-  //
-  // The compiler's wait analysis loses track of which buffer a direct load
-  // targets where control flow merges (the loop head) and waits for all of
-  // them before the next LDS read; the first iteration after the loop head
-  // therefore issues its loads after its MFMAs (LATE), so that this wait
-  // covers only tile t + 1, issued a whole tile earlier.
-  auto step = [&](auto late, int t, const uint16_t *cur, uint16_t *nx2) {
-    if (!late.value) dma_tile(min(t + 2, n_tiles - 1), nx2);
-    const int kv0 = a + t * kBN;
-    if (wave_live && kv0 <= qw + 31) compute(kv0, cur);
-    if (late.value) dma_tile(min(t + 2, n_tiles - 1), nx2);
-    wait_vm_lgkm0<TL::IPW>();
-    __builtin_amdgcn_s_barrier();
-  };
-  using LATE = std::true_type;
-  using EARLY = std::false_type;
-
-  // M^T first (its own buffer, needed only after the loop), then tiles 0, 1.
-  dma_mem();
-  dma_tile(0, sB0);
-  dma_tile(min(1, n_tiles - 1), sB1);
-  wait_vm_lgkm0<TL::IPW>();
-  __builtin_amdgcn_s_barrier();
-  for (int t = 0;;) {
-    step(LATE{}, t, sB0, sB2);
-    if (++t >= n_tiles) break;
-    step(EARLY{}, t, sB1, sB0);
-    if (++t >= n_tiles) break;
-    step(EARLY{}, t, sB2, sB1);
-    if (++t >= n_tiles) break;
-  }
-
-  // ---- retrieval from the pre-segment snapshot and the gate ----
-  if (tid < D) sZ[tid] = zreg;
-  wait_vm_lgkm0<0>();
-  __syncthreads();
-
-  if (!wave_live) return;
-  // sigma(Q) as the B operand, and this lane's part of sigma(q).z.
-  float den = 0.f;
-  u32x4 sq[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    uint32_t wv[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float x0 = elu1(lo_bf16(qf[t][jj]));
-      const float x1 = elu1(hi_bf16(qf[t][jj]));
-      den += x0 * sZ[16 * t + 8 * g + 2 * jj] + x1 * sZ[16 * t + 8 * g + 2 * jj + 1];
-      wv[jj] = pack_bf16x2(x0, x1);
-    }
-    sq[t] = u32x4{wv[0], wv[1], wv[2], wv[3]};
-  }
-  den = sum_xor32(den) + eps;
-  const float inv_den = 1.f / den;
-  const float inv_l = 1.f / sum_xor32(lsum);  // both halves' key slots
-  const float gam = 1.f / (1.f + __expf(-beta[h]));
-  const float w_mem = gam * inv_den;
-  const float w_dot = (1.f - gam) * inv_l;
-
-  uint16_t *op = out + (static_cast<size_t>(bhq) * L + qrow) * D;
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt) {
-    f32x16 am = f32x16{};
+  // Retrieval from the pre-segment snapshot M^T (this slot), the gate and the
+  // store of this wave's 32 rows. Every wave runs it (waves past the segment
+  // end included) and issues the same stores: the buffer range ends at the
+  // segment end, and the hardware drops stores beyond it.
+  auto epilogue = [&](const uint16_t *buf, int qw) __attribute__((always_inline)) {
+    const float *side = reinterpret_cast<const float *>(buf + TL::BUFU * 8);
+    // sigma(Q) as the B operand, computed in place of Q (the next item's Q
+    // slots reload every wave's registers before its first key tile), and
+    // this lane's part of sigma(q).z.
+    float den = 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const u32x4 ma =
-          *reinterpret_cast<const u32x4 *>(sM + 8 * swz_unit<D>(32 * dt + l32, 2 * t + g));
-      am = mfma32(as_bf16x8(ma), as_bf16x8(sq[t]), am);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float x0 = elu1(lo_bf16(qf[t][jj]));
+        const float x1 = elu1(hi_bf16(qf[t][jj]));
+        den += x0 * side[16 * t + 8 * g + 2 * jj] + x1 * side[16 * t + 8 * g + 2 * jj + 1];
+        qf[t][jj] = pack_bf16x2(x0, x1);
+      }
     }
-    if (qrow < e) {
+    den = sum_xor32(den) + eps;
+    const float inv_den = 1.f / den;
+    const float inv_l = 1.f / sum_xor32(lsum);  // both halves' key slots
+    const float gam = 1.f / (1.f + __expf(-side[(kWaves - 1) * 64 + w / RW]));
+    const float w_mem = gam * inv_den;
+    const float w_dot = (1.f - gam) * inv_l;
+
+    // The buffer's base and size are wave-uniform (readfirstlane states it;
+    // a buffer resource must be in scalar registers).
+    const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(32, cur.e - qw)));
+    const size_t obase = (static_cast<size_t>(cur.bq + w / RW) * L + qw) * D;
+    const uint32_t ob_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(obase));
+    const uint32_t ob_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(obase >> 32));
+    uint16_t *ob = out + ((static_cast<size_t>(ob_hi) << 32) | ob_lo);
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(ob, 0, nrows * D * 2, 0x00020000);
+    const int lane_off = (l32 < nrows ? l32 : nrows) * D * 2;
+    // One 32-row block of A_mem^T at a time (the fences keep the four
+    // accumulation chains from being interleaved, which would hold four
+    // accumulators at once). Row 32 dt + l32 of M^T has the swizzle of row
+    // l32 (the pattern repeats every 16 rows), so the K operand offsets serve
+    // here too. The fragments of block dt + 1 are read as soon as the MFMAs of
+    // block dt have been issued, so their latency hides behind the output
+    // work of block dt.
+    u32x4 ma[NT];
+    auto mread = [&](int dt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        ma[t] = *reinterpret_cast<const u32x4 *>(buf + koff[t] + 32 * dt * D);
+    };
+    mread(0);
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 am = f32x16{};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) am = mfma32(as_bf16x8(ma[t]), as_bf16x8(qf[t]), am);
+      if (dt + 1 < ND) mread(dt + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         uint32_t pk[2];
@@ -428,10 +484,132 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
           pk[jj] = pack_bf16x2(w_mem * am[i0] + w_dot * o[dt][i0],
                                w_mem * am[i0 + 1] + w_dot * o[dt][i0 + 1]);
         }
-        *reinterpret_cast<u32x2 *>(op + 32 * dt + 8 * gi + 4 * g) = u32x2{pk[0], pk[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pk[0], pk[1]}, rsrc,
+                                              lane_off + (32 * dt + 8 * gi + 4 * g) * 2, 0, 0);
       }
     }
+  };
+
+  // Q rows of this item for the waves of half `half` (0: waves 0..3, 1:
+  // waves 4..7); the online-softmax state starts over with the first half.
+  auto take_q = [&](int half, const uint16_t *buf) __attribute__((always_inline)) {
+    if (half == 0) {
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) o[dt] = f32x16{};
+      m = -INFINITY;
+      lsum = 0.f;
+    }
+    if ((w >> 2) == half) {
+      // Row l32 of this wave's 32-row block, swizzled like K row l32. (The
+      // block offset passes through an empty asm statement, so that the eight
+      // addresses are formed here rather than hoisted and kept.)
+      int qo = (w & 3) * 32 * D;
+      __asm__ volatile("" : "+v"(qo));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) qf[t] = *reinterpret_cast<const u32x4 *>(buf + qo + koff[t]);
+    }
+  };
+
+  // One step: the direct loads of the slot two ahead (EARLY: before the work;
+  // LATE: after it), the work on this slot, then this wave's loads of the next
+  // slot are awaited and the workgroup meets at the barrier that publishes
+  // them. Direct loads complete in issue order, so allowing only this step's
+  // own loads (NLD of them) to be outstanding means the next slot has landed.
+  //
+  // The compiler's wait analysis loses track of which buffer a direct load
+  // targets where the paths into a loop head merge, and waits for all of them
+  // before the next LDS read; the first step after a loop head therefore
+  // issues its loads LATE, so that this wait covers only the next slot, issued
+  // a whole step earlier. Elsewhere the steps are straight-line code after a
+  // single predecessor and issue EARLY.
+  auto step = [&](auto late, auto nld, auto &&load, auto &&work) __attribute__((always_inline)) {
+    if (!late.value) load();
+    work();
+    if (late.value) load();
+    wait_vm_lgkm0<decltype(nld)::value>();
+    __builtin_amdgcn_s_barrier();
+  };
+  using LATE = std::true_type;
+  using EARLY = std::false_type;
+  using NT_ = std::integral_constant<int, TL::IPW>;      // key tile or Q slot
+  using NM_ = std::integral_constant<int, TL::IPW + 1>;  // M^T slot with its side area
+#define IA_DO(...) [&]() __attribute__((always_inline)) { __VA_ARGS__; }
+
+  // The first item's Q slots (as if a previous item had ended).
+  dma_q(cur, 0, sB1);
+  dma_q(cur, 1, sB2);
+  wait_vm_lgkm0<TL::IPW>();
+  __builtin_amdgcn_s_barrier();
+  step(EARLY{}, NT_{}, IA_DO(dma_tile(cur, 0, sB0)), IA_DO(take_q(0, sB1)));
+  step(EARLY{}, NT_{}, IA_DO(dma_tile(cur, min(1, cur.T - 1), sB1)), IA_DO(take_q(1, sB2)));
+  for (;;) {
+    const FusedItem nxt = item(cur.k + 1);
+    const int n3 = (cur.T + 5) / 3 * 3;  // slots of this item
+    const int qw = cur.q0 + (w % RW) * 32;  // first query row of this wave
+    const bool live = qw < cur.e;
+    const int tlast = cur.T - 1;
+    auto tile = [&](int pos, const uint16_t *buf) __attribute__((always_inline)) {
+      const int kv0 = cur.a + pos * kBN;
+      if (pos < cur.T && live && kv0 <= qw + 31) compute(kv0, buf, qw, qw + l32, cur.e);
+    };
+    // Slots 0 .. n3 - 7, three per iteration; every slot loaded from here on
+    // is a key tile (padding: the last tile again).
+    int pos = 0;
+    while (pos < n3 - 6) {
+      step(LATE{}, NT_{}, IA_DO(dma_tile(cur, min(pos + 2, tlast), sB2)), IA_DO(tile(pos, sB0)));
+      step(EARLY{}, NT_{}, IA_DO(dma_tile(cur, min(pos + 3, tlast), sB0)),
+           IA_DO(tile(pos + 1, sB1)));
+      step(EARLY{}, NT_{}, IA_DO(dma_tile(cur, min(pos + 4, tlast), sB1)),
+           IA_DO(tile(pos + 2, sB2)));
+      pos += 3;
+    }
+    // The last three tile slots load M^T and the next item's Q; then the
+    // retrieval and output of this item, and the next item's Q. Past the last
+    // item, the Q slots load M^T again (any valid source; nobody reads it).
+    step(LATE{}, NT_{}, IA_DO(dma_tile(cur, min(n3 - 4, tlast), sB2)), IA_DO(tile(n3 - 6, sB0)));
+    step(EARLY{}, NM_{}, IA_DO(dma_mem(cur, sB0)), IA_DO(tile(n3 - 5, sB1)));
+    if (nxt.k >= 0) {
+      step(EARLY{}, NT_{}, IA_DO(dma_q(nxt, 0, sB1)), IA_DO(tile(n3 - 4, sB2)));
+      step(EARLY{}, NT_{}, IA_DO(dma_q(nxt, 1, sB2)), IA_DO(epilogue(sB0, qw)));
+    } else {
+      step(EARLY{}, NT_{}, IA_DO(dma_tile(cur, tlast, sB1)), IA_DO(tile(n3 - 4, sB2)));
+      step(EARLY{}, NT_{}, IA_DO(dma_tile(cur, tlast, sB2)), IA_DO(epilogue(sB0, qw)));
+      break;
+    }
+    cur = nxt;
+    step(EARLY{}, NT_{}, IA_DO(dma_tile(cur, 0, sB0)), IA_DO(take_q(0, sB1)));
+    step(EARLY{}, NT_{}, IA_DO(dma_tile(cur, min(1, cur.T - 1), sB1)), IA_DO(take_q(1, sB2)));
   }
+#undef IA_DO
+  // Loads of slots past the end are still in flight; they must land before
+  // the workgroup's LDS is handed to another workgroup.
+  wait_vm_lgkm0<0>();
+}
+
+// Compute units of a device and resident workgroups per compute unit of a
+// kernel, cached per device (the values do not change for a process).
+int device_cus(int dev) {
+  static int cached[64] = {};
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 1;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
+
+template <int D, int HPW>
+int fused_per_cu(int dev) {
+  static int cached[64] = {};  // per template instance
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void *>(&fused_bf16_kernel<D, HPW>), kThreads, 0) !=
+          hipSuccess ||
+      n < 1)
+    n = 1;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
 }
 
 template <int D, int HPW>
@@ -441,13 +619,21 @@ hipError_t launch_t(const Geometry &g, const uint16_t *q, const uint16_t *k, con
   const int rows = g.N < g.L ? g.N : g.L;
   const int n_qt = (rows + BM - 1) / BM;
   const long long units = static_cast<long long>(g.B) * g.Hkv * (g.Hq / g.Hkv / HPW);
-  const long long nblk = static_cast<long long>(n_qt) * g.S * units;
-  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const int xcd_chunk = (nblk % kXcds == 0) ? static_cast<int>(nblk / kXcds) : 0;
+  const long long n_items = static_cast<long long>(n_qt) * g.S * units;
+  if (n_items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (n_items == 0) return hipSuccess;
+  // Persistent workgroups: as many as can be resident at once (one per
+  // compute unit at d = 128, where the ring fills most of a CU's LDS), each
+  // working through its items in one stream of ring slots.
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const long long slots = static_cast<long long>(fused_per_cu<D, HPW>(dev)) * device_cus(dev);
+  const long long grid = n_items < slots ? n_items : slots;
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
-  fused_bf16_kernel<D, HPW><<<dim3(static_cast<unsigned>(nblk)), kThreads, 0, stream>>>(
+  fused_bf16_kernel<D, HPW><<<dim3(static_cast<unsigned>(grid)), kThreads, 0, stream>>>(
       q, k, ws.vt, ws.vt_tiles, beta, ws.z_pre, ws.mt_pre_bf16, out, g.Hq, g.Hkv, g.L, g.N, g.S,
-      n_qt, g.eps, scale_log2, xcd_chunk);
+      n_qt, static_cast<int>(n_items), g.eps, scale_log2);
   return hipGetLastError();
 }
 
