@@ -163,26 +163,33 @@ __global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restr
 // ---------------------------------------------------------------------------
 // gh: [G_s | H_s] = sigma(K_s)^T [diag(1/den) sigma(K_s) | V_s], den_i = sigma(k_i).z_{s-1} + eps
 // ---------------------------------------------------------------------------
-template <int D, bool DELTA, int CS>
-__global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
-                                                 const uint16_t *__restrict__ v,
-                                                 const float *__restrict__ z_pre,
-                                                 float *__restrict__ gh,
-                                                 uint16_t *__restrict__ vt, int vt_tiles, int L,
-                                                 int N, int S, float eps) {
+// RG row groups of four waves share a workgroup: group q takes the chunks
+// q, q + RG, ... of the segment with its own staging buffers, and the groups'
+// partial sums are added through LDS at the end (fixed order, so the result
+// does not depend on timing). Two groups fill a CU's wave slots when the grid
+// alone would leave one workgroup per CU.
+template <int D, bool DELTA, int CS, int RG>
+__global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict__ k,
+                                                      const uint16_t *__restrict__ v,
+                                                      const float *__restrict__ z_pre,
+                                                      float *__restrict__ gh,
+                                                      uint16_t *__restrict__ vt, int vt_tiles,
+                                                      int L, int N, int S, float eps) {
   constexpr int ND = D / 32;
   constexpr int CCH = D / 8;            // 8-column chunks per row
   constexpr int ITEMS = 16 * CCH;       // staging items: 4 rows x 8 columns each
   constexpr int NPAIR = DELTA ? 2 * ND : ND;  // (matrix, column tile) pairs
   constexpr int PPW = (NPAIR + 4 * CS - 1) / (4 * CS);  // pairs per wave
-  static_assert(ITEMS <= 256, "one staging item per thread");
+  constexpr int NB = DELTA ? 3 : 2;     // staging buffers per group: sigma(K)^T, V^T, (W^T)
+  static_assert(ITEMS <= 256, "one staging item per thread of a group");
+  static_assert(RG == 1 || 4 * PPW * ND * 16 * 64 * 4 <= RG * NB * D * kStr * 2,
+                "the partial sums of a group fit in the staging buffers");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * kStr];  // sigma(K)^T  [col][key]
-  __shared__ __attribute__((aligned(16))) uint16_t sWt[DELTA ? D * kStr : 8];  // (sigma(K)/den)^T
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * kStr];  // V^T
+  // Per group: sigma(K)^T, V^T and (delta) (sigma(K)/den)^T, [col][key].
+  __shared__ __attribute__((aligned(16))) uint16_t sStage[RG][NB][D * kStr];
   __shared__ float sZ[D];
-  __shared__ float sDenPart[CCH][64];
-  __shared__ float sRden[64];
+  __shared__ float sDenPart[RG][CCH][64];
+  __shared__ float sRden[RG][64];
 
   // Work item wi = (head * S + s) * CS + cs. When the launch divides evenly,
   // consecutive work items go to one XCD (hardware hands out workgroups
@@ -195,8 +202,17 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
   const int cs = wi % CS, s = (wi / CS) % S, head = wi / CS / S;
   const int p_lo = cs * NPAIR / CS, p_hi = (cs + 1) * NPAIR / CS;
   const int a = s * N, e = min(a + N, L);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Wave within the group and thread within the group (written without a
+  // mask when there is one group: the compiler then keeps the wave index
+  // scalar and the accumulators in place).
+  const int w = RG > 1 ? (__builtin_amdgcn_readfirstlane(tid >> 6) & 3) : (tid >> 6);
+  const int grp = RG > 1 ? (tid >> 8) : 0;  // row group
+  const int tg = RG > 1 ? (tid & 255) : tid;
   const int g = lane >> 5, l32 = lane & 31;
+  uint16_t *sKt = sStage[grp][0];
+  uint16_t *sVt = sStage[grp][1];
+  uint16_t *sWt = sStage[grp][NB - 1];  // delta only
   const uint16_t *kp = k + static_cast<size_t>(head) * L * D;
   const uint16_t *vp = v + static_cast<size_t>(head) * L * D;
   if (tid < D) sZ[tid] = z_pre[(static_cast<size_t>(head) * (S + 1) + s) * D + tid];
@@ -207,8 +223,10 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
 #pragma unroll
     for (int rt = 0; rt < ND; ++rt) acc[pi][rt] = f32x16{};
 
-  const bool has = tid < ITEMS;
-  const int kg = tid & 15, cc = tid >> 4;  // rows 4 kg .. 4 kg + 3, columns 8 cc .. 8 cc + 7
+  // Chunk iterations of every group (the groups take chunks grp, grp + RG, ...).
+  const int iters = ((e - a + 63) / 64 + RG - 1) / RG;
+  const bool has = tg < ITEMS;
+  const int kg = tg & 15, cc = tg >> 4;  // rows 4 kg .. 4 kg + 3, columns 8 cc .. 8 cc + 7
 
   // Register staging of 64-row chunks (4 rows x 8 columns per item), two
   // register sets: a chunk's loads are issued two chunks before it is staged.
@@ -251,7 +269,7 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
           float p = 0.f;
 #pragma unroll
           for (int j = 0; j < 8; ++j) p += kf[r][j] * sZ[cc * 8 + j];
-          sDenPart[cc][4 * kg + r] = p;
+          sDenPart[grp][cc][4 * kg + r] = p;
         }
       }
       // transposed stores: one 8-byte write of 4 keys per column
@@ -271,29 +289,32 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
     }
     if constexpr (DELTA) {
       __syncthreads();
-      if (tid < 64) {
+      if (tg < 64) {
         float den = eps;
-        for (int c = 0; c < CCH; ++c) den += sDenPart[c][tid];
-        sRden[tid] = 1.f / den;
+        for (int c = 0; c < CCH; ++c) den += sDenPart[grp][c][tg];
+        sRden[grp][tg] = 1.f / den;
       }
       __syncthreads();
       if (has) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const u32x2 w2 = {pack_bf16x2(kf[0][j] * sRden[4 * kg], kf[1][j] * sRden[4 * kg + 1]),
-                            pack_bf16x2(kf[2][j] * sRden[4 * kg + 2], kf[3][j] * sRden[4 * kg + 3])};
+          const float *rd = sRden[grp];
+          const u32x2 w2 = {pack_bf16x2(kf[0][j] * rd[4 * kg], kf[1][j] * rd[4 * kg + 1]),
+                            pack_bf16x2(kf[2][j] * rd[4 * kg + 2], kf[3][j] * rd[4 * kg + 3])};
           *reinterpret_cast<u32x2 *>(sWt + (cc * 8 + j) * kStr + 4 * kg) = w2;
         }
       }
     }
     __syncthreads();
-    if (i0 + 128 < e) load_chunk(cur, i0 + 128);  // cur is free once staged
-    if (cs == 0) {
+    // cur is free once staged: load the chunk this set takes next (zeros past
+    // the segment end, for a chunk the loop visits without one).
+    if (i0 + 128 * RG < a + 64 * RG * iters) load_chunk(cur, i0 + 128 * RG);
+    if (cs == 0 && i0 < e) {
       // V^T of this 64-key chunk (rows past the segment end are zero), in the
       // unit order and bank swizzle of vt_unit_pos.
       uint16_t *vtile =
           vt + ((static_cast<size_t>(head) * S + s) * vt_tiles + (i0 - a) / 64) * (D * 64);
-      for (int u = tid; u < D * 8; u += 256) {
+      for (int u = tg; u < D * 8; u += 256) {
         const int d = u >> 3;
         const int q = vt_unit_pos(d, u & 7);  // the swizzle is its own inverse
         const int k0 = 16 * (q >> 1) + 4 * (q & 1);
@@ -332,16 +353,45 @@ __global__ __launch_bounds__(256) void gh_kernel(const uint16_t *__restrict__ k,
       }
     }
   };
+  // Group grp takes chunks grp, grp + RG, ...; every group runs the same
+  // number of iterations (the barriers are workgroup-wide), a chunk past the
+  // segment end contributing nothing.
   Stage sa, sb;
-  load_chunk(sa, a);
-  if (a + 64 < e) load_chunk(sb, a + 64);
-  for (int i0 = a;;) {
-    chunk(i0, sa);
-    i0 += 64;
-    if (i0 >= e) break;
-    chunk(i0, sb);
-    i0 += 64;
-    if (i0 >= e) break;
+  load_chunk(sa, a + 64 * grp);
+  if (iters > 1) load_chunk(sb, a + 64 * (RG + grp));
+  for (int j = 0;;) {
+    chunk(a + 64 * (RG * j + grp), sa);
+    if (++j >= iters) break;
+    chunk(a + 64 * (RG * j + grp), sb);
+    if (++j >= iters) break;
+  }
+  if constexpr (RG > 1) {
+    // Add the other groups' partial sums into group 0 (staging buffers reused).
+    float *sAcc = reinterpret_cast<float *>(&sStage[0][0][0]);
+    __syncthreads();
+    for (int q = 1; q < RG; ++q) {
+      if (grp == q) {
+#pragma unroll
+        for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+          for (int rt = 0; rt < ND; ++rt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              sAcc[(((w * PPW + pi) * ND + rt) * 16 + r) * 64 + lane] = acc[pi][rt][r];
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int pi = 0; pi < PPW; ++pi)
+#pragma unroll
+          for (int rt = 0; rt < ND; ++rt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              acc[pi][rt][r] += sAcc[(((w * PPW + pi) * ND + rt) * 16 + r) * 64 + lane];
+      }
+      __syncthreads();
+    }
+    if (grp != 0) return;
   }
 
   // Store in fragment order: matrix 0 = G as bf16 hi/lo operand words
@@ -506,22 +556,24 @@ hipError_t launch_d(const Geometry &g, const uint16_t *k, const uint16_t *v, flo
   // workgroups so that the launch still covers the chip.
   const bool split = g.S * heads < 512;
   const dim3 ghgrid(g.S * (split ? 2 : 1), heads), seqgrid(D / 32, heads);
+  // With the column split, two row groups per workgroup (512 threads) fill
+  // the CU's wave slots; without it the accumulators leave room for one.
   zsum_kernel<D><<<dim3(g.S * parts, heads), 256, 0, stream>>>(k, ws.dz, g.L, g.N, g.S, parts);
   zprefix_kernel<<<heads, kZThreads, 0, stream>>>(z, ws.dz, ws.z_pre, g.S, D, parts);
   if (delta) {
     if (split)
-      gh_kernel<D, true, 2><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+      gh_kernel<D, true, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
                                                         ws.vt_tiles, g.L, g.N, g.S, g.eps);
     else
-      gh_kernel<D, true, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+      gh_kernel<D, true, 1, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
                                                         ws.vt_tiles, g.L, g.N, g.S, g.eps);
     seq_kernel<D, true><<<seqgrid, 64 * (D / 32), 0, stream>>>(ws.gh, M, ws.mt_pre_bf16, g.S);
   } else {
     if (split)
-      gh_kernel<D, false, 2><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+      gh_kernel<D, false, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
                                                          ws.vt_tiles, g.L, g.N, g.S, g.eps);
     else
-      gh_kernel<D, false, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+      gh_kernel<D, false, 1, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
                                                          ws.vt_tiles, g.L, g.N, g.S, g.eps);
     seq_kernel<D, false><<<seqgrid, 64 * (D / 32), 0, stream>>>(ws.gh, M, ws.mt_pre_bf16, g.S);
   }
