@@ -29,7 +29,8 @@
 // (rt, ct) holds, for MFMA-result register r and lane l, the element at row
 // 32 rt + kappa(r, l / 32), column 32 ct + l % 32, where
 // kappa(r, g) = 8 (r / 4) + 4 g + r % 4 is the 32x32 MFMA result row map.
-//   H_s (fp32): element index ((rt * (D/32) + ct) * 16 + r) * 64 + l.
+//   H_s (fp32): element index ((rt * (D/32) + ct) * 64 + l) * 16 + r (a lane's
+//     16 values contiguous: four 16-byte loads).
 //   G_s (bf16 hi/lo): 32-bit word ((rt * (D/32) + ct) * 64 + l) * 16 + w, where
 //     word 4 h + p (h, p < 2, 4) packs the hi parts of registers 8 h + 2 p
 //     (low half) and 8 h + 2 p + 1 (high half), and word 8 + 4 h + p the lo
@@ -51,6 +52,26 @@ __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 __device__ __forceinline__ int kappa(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// Sum of x over the lanes l, l ^ 16, l ^ 32 and l ^ 48 (the same value in all
+// four). v_permlane16_swap / v_permlane32_swap with both operands equal to x
+// return, in every lane, x of the lane and of its partner 16 / 32 away.
+__device__ __forceinline__ float sum_lanes_16_32(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup barrier that orders LDS only. __syncthreads() also waits for every
+// outstanding global load and store of the wave, which would drain the
+// prefetches the loops below keep in flight across their barriers; these
+// barriers only ever guard LDS buffers.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ---------------------------------------------------------------------------
 // zsum: dz[head][s][part][c] = sum over rows of part `part` of segment s of
@@ -169,8 +190,8 @@ __global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restr
 // does not depend on timing). Two groups fill a CU's wave slots when the grid
 // alone would leave one workgroup per CU.
 template <int D, bool DELTA, int CS, int RG>
-__global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict__ k,
-                                                      const uint16_t *__restrict__ v,
+__global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not restrict:
+                                                      const uint16_t *v,  // see load_chunk
                                                       const float *__restrict__ z_pre,
                                                       float *__restrict__ gh,
                                                       uint16_t *__restrict__ vt, int vt_tiles,
@@ -188,8 +209,10 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict
   // Per group: sigma(K)^T, V^T and (delta) (sigma(K)/den)^T, [col][key].
   __shared__ __attribute__((aligned(16))) uint16_t sStage[RG][NB][D * kStr];
   __shared__ float sZ[D];
-  __shared__ float sDenPart[RG][CCH][64];
-  __shared__ float sRden[RG][64];
+  // Partial denominators: per row of the chunk, one sum over each wave's 32
+  // columns (the waves holding staging items: CCH / 4 of them).
+  constexpr int NWD = CCH / 4;
+  __shared__ __attribute__((aligned(16))) float sDenPart[RG][NWD][64];
 
   // Work item wi = (head * S + s) * CS + cs. When the launch divides evenly,
   // consecutive work items go to one XCD (hardware hands out workgroups
@@ -230,23 +253,29 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict
 
   // Register staging of 64-row chunks (4 rows x 8 columns per item), two
   // register sets: a chunk's loads are issued two chunks before it is staged.
+  // Every item issues all its loads (rows past the segment end read its last
+  // row, and staging masks them), so the compiler's count of loads in flight
+  // is the same on every path and its waits cover exactly the chunk being
+  // staged. The empty asm statements keep the loads where they are issued
+  // (k and v are not restrict, so they cannot be moved across them).
   struct Stage {
     u32x4 k[4], v[4];
   };
-  auto load_chunk = [&](Stage &st, int i0) {
+  auto load_chunk = [&](Stage &st, int i0) __attribute__((always_inline)) {
+    if (has) {
+      __asm__ volatile("" ::: "memory");
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = i0 + 4 * kg + r;
-      st.k[r] = st.v[r] = u32x4{0u, 0u, 0u, 0u};
-      if (has && row < e) {
-        st.k[r] = *reinterpret_cast<const u32x4 *>(kp + static_cast<size_t>(row) * D + cc * 8);
-        st.v[r] = *reinterpret_cast<const u32x4 *>(vp + static_cast<size_t>(row) * D + cc * 8);
+      for (int r = 0; r < 4; ++r) {
+        const size_t row = min(i0 + 4 * kg + r, e - 1);
+        st.k[r] = *reinterpret_cast<const u32x4 *>(kp + row * D + cc * 8);
+        st.v[r] = *reinterpret_cast<const u32x4 *>(vp + row * D + cc * 8);
       }
+      __asm__ volatile("" ::: "memory");
     }
   };
 
   auto chunk = [&](int i0, Stage &cur) {
-    __syncthreads();  // previous chunk consumed; sZ visible
+    lds_barrier();  // previous chunk consumed; sZ visible
     const u32x4 *kw = cur.k;
     const u32x4 *vv = cur.v;
     float kf[4][8];
@@ -260,17 +289,22 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict
           // rows past the segment end contribute nothing: sigma forced to 0
           kf[r][2 * jj] = in ? elu1(lo_bf16(kw[r][jj])) : 0.f;
           kf[r][2 * jj + 1] = in ? elu1(hi_bf16(kw[r][jj])) : 0.f;
-          vw[r][jj] = vv[r][jj];
+          vw[r][jj] = in ? vv[r][jj] : 0u;
         }
       }
-      if (DELTA) {
+      if constexpr (DELTA) {
+        // sigma(k_i).z over this thread's 8 columns, then over the 32 columns
+        // of its wave (the lanes 16 apart hold the same rows), written once
+        // per wave and row.
+        f32x4 p;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float p = 0.f;
+          float x = 0.f;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) p += kf[r][j] * sZ[cc * 8 + j];
-          sDenPart[grp][cc][4 * kg + r] = p;
+          for (int j = 0; j < 8; ++j) x += kf[r][j] * sZ[cc * 8 + j];
+          p[r] = sum_lanes_16_32(x);
         }
+        if ((cc & 3) == 0) *reinterpret_cast<f32x4 *>(&sDenPart[grp][cc >> 2][4 * kg]) = p;
       }
       // transposed stores: one 8-byte write of 4 keys per column
 #pragma unroll
@@ -287,34 +321,16 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict
         *reinterpret_cast<u32x2 *>(sVt + (cc * 8 + 2 * jj + 1) * kStr + 4 * kg) = hi;
       }
     }
-    if constexpr (DELTA) {
-      __syncthreads();
-      if (tg < 64) {
-        float den = eps;
-        for (int c = 0; c < CCH; ++c) den += sDenPart[grp][c][tg];
-        sRden[grp][tg] = 1.f / den;
-      }
-      __syncthreads();
-      if (has) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float *rd = sRden[grp];
-          const u32x2 w2 = {pack_bf16x2(kf[0][j] * rd[4 * kg], kf[1][j] * rd[4 * kg + 1]),
-                            pack_bf16x2(kf[2][j] * rd[4 * kg + 2], kf[3][j] * rd[4 * kg + 3])};
-          *reinterpret_cast<u32x2 *>(sWt + (cc * 8 + j) * kStr + 4 * kg) = w2;
-        }
-      }
-    }
-    __syncthreads();
-    // cur is free once staged: load the chunk this set takes next (zeros past
-    // the segment end, for a chunk the loop visits without one).
-    if (i0 + 128 * RG < a + 64 * RG * iters) load_chunk(cur, i0 + 128 * RG);
+    lds_barrier();
     if (cs == 0 && i0 < e) {
       // V^T of this 64-key chunk (rows past the segment end are zero), in the
-      // unit order and bank swizzle of vt_unit_pos.
+      // unit order and bank swizzle of vt_unit_pos. Stored before the next
+      // loads are issued, so that waiting for those never waits for these.
       uint16_t *vtile =
           vt + ((static_cast<size_t>(head) * S + s) * vt_tiles + (i0 - a) / 64) * (D * 64);
-      for (int u = tg; u < D * 8; u += 256) {
+#pragma unroll
+      for (int uu = 0; uu < D * 8 / 256; ++uu) {
+        const int u = tg + 256 * uu;
         const int d = u >> 3;
         const int q = vt_unit_pos(d, u & 7);  // the swizzle is its own inverse
         const int k0 = 16 * (q >> 1) + 4 * (q & 1);
@@ -322,6 +338,29 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict
         const u32x2 r1 = *reinterpret_cast<const u32x2 *>(sVt + d * kStr + k0 + 8);
         *reinterpret_cast<u32x4 *>(vtile + u * 8) = u32x4{r0[0], r0[1], r1[0], r1[1]};
       }
+    }
+    // cur is free once staged: load the chunk this set takes next (copies of
+    // the last row, for a chunk the loop never stages).
+    load_chunk(cur, i0 + 128 * RG);
+    if constexpr (DELTA) {
+      // (sigma(K) / den)^T: den of this thread's rows from the waves' partial
+      // sums (added in a fixed order), then one 8-byte write per column.
+      if (has) {
+        f32x4 den = {eps, eps, eps, eps};
+#pragma unroll
+        for (int q = 0; q < NWD; ++q) den += *reinterpret_cast<const f32x4 *>(&sDenPart[grp][q][4 * kg]);
+        // (v_rcp_f32, within 1 ulp: W is rounded to bf16 right after.)
+        float rd[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rd[r] = __builtin_amdgcn_rcpf(den[r]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x2 w2 = {pack_bf16x2(kf[0][j] * rd[0], kf[1][j] * rd[1]),
+                            pack_bf16x2(kf[2][j] * rd[2], kf[3][j] * rd[3])};
+          *reinterpret_cast<u32x2 *>(sWt + (cc * 8 + j) * kStr + 4 * kg) = w2;
+        }
+      }
+      lds_barrier();
     }
 
     // Contraction over the 64 keys of the chunk, 16 per MFMA. Slot j of lane
@@ -358,17 +397,19 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict
   // segment end contributing nothing.
   Stage sa, sb;
   load_chunk(sa, a + 64 * grp);
-  if (iters > 1) load_chunk(sb, a + 64 * (RG + grp));
-  for (int j = 0;;) {
+  load_chunk(sb, a + 64 * (RG + grp));
+  // Whole pairs of chunks, then an odd last one: a loop with a single exit,
+  // so that the loop head is reached only after both sets' loads were issued.
+  int j = 0;
+  for (; j + 2 <= iters; j += 2) {
     chunk(a + 64 * (RG * j + grp), sa);
-    if (++j >= iters) break;
-    chunk(a + 64 * (RG * j + grp), sb);
-    if (++j >= iters) break;
+    chunk(a + 64 * (RG * (j + 1) + grp), sb);
   }
+  if (j < iters) chunk(a + 64 * (RG * j + grp), sa);
   if constexpr (RG > 1) {
     // Add the other groups' partial sums into group 0 (staging buffers reused).
     float *sAcc = reinterpret_cast<float *>(&sStage[0][0][0]);
-    __syncthreads();
+    lds_barrier();
     for (int q = 1; q < RG; ++q) {
       if (grp == q) {
 #pragma unroll
@@ -379,7 +420,7 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict
             for (int r = 0; r < 16; ++r)
               sAcc[(((w * PPW + pi) * ND + rt) * 16 + r) * 64 + lane] = acc[pi][rt][r];
       }
-      __syncthreads();
+      lds_barrier();
       if (grp == 0) {
 #pragma unroll
         for (int pi = 0; pi < PPW; ++pi)
@@ -389,7 +430,7 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict
             for (int r = 0; r < 16; ++r)
               acc[pi][rt][r] += sAcc[(((w * PPW + pi) * ND + rt) * 16 + r) * 64 + lane];
       }
-      __syncthreads();
+      lds_barrier();
     }
     if (grp != 0) return;
   }
@@ -419,9 +460,12 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict
           for (int q = 0; q < 4; ++q)
             f[q] = u32x4{wd[4 * q], wd[4 * q + 1], wd[4 * q + 2], wd[4 * q + 3]};
         } else {
-          float *f = base + static_cast<size_t>(D) * D + ((rt * ND + ct) * 16) * 64 + lane;
+          f32x4 *f = reinterpret_cast<f32x4 *>(base + static_cast<size_t>(D) * D) +
+                     ((rt * ND + ct) * 64 + lane) * 4;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) f[r * 64] = acc[pi][rt][r];
+          for (int q = 0; q < 4; ++q)
+            f[q] = f32x4{acc[pi][rt][4 * q], acc[pi][rt][4 * q + 1], acc[pi][rt][4 * q + 2],
+                         acc[pi][rt][4 * q + 3]};
         }
       }
     }
@@ -437,7 +481,7 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *__restrict
 // B operand of G_s M_{s-1}. Its hi part is the bf16 snapshot M_{s-1}^T.
 // ---------------------------------------------------------------------------
 template <int D, bool DELTA>
-__global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *__restrict__ gh,
+__global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *gh,  // not restrict: see step()
                                                            float *__restrict__ M,
                                                            uint16_t *__restrict__ mt_pre,
                                                            int S) {
@@ -455,55 +499,70 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *__restr
 #pragma unroll
   for (int r = 0; r < 16; ++r) m[r] = Mh[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j];
 
-  // Publish the state before segment st: global bf16 snapshot (if st < S) and,
-  // for the delta rule, the hi/lo operand copy in LDS. This lane's rows
+  // The state before segment st: the global bf16 snapshot M_{st-1}^T (st < S)
+  // and, for the delta rule, the hi/lo operand copy in LDS. This lane's rows
   // 32 ct + 8 q4 + 4 g + 0..3 are contiguous in the transposed layouts.
-  auto publish = [&](int st) {
+  auto snapshot = [&](int st) __attribute__((always_inline)) {
     uint16_t *mt = mt_pre + (static_cast<size_t>(head) * S + st) * D * D +
                    static_cast<size_t>(j) * D + 32 * ct + 4 * g;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<u32x2 *>(mt + 8 * q4) =
+          u32x2{pack_bf16x2(m[4 * q4], m[4 * q4 + 1]), pack_bf16x2(m[4 * q4 + 2], m[4 * q4 + 3])};
+  };
+  auto operand = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const uint32_t h0 = pack_bf16x2(m[4 * q4], m[4 * q4 + 1]);
       const uint32_t h1 = pack_bf16x2(m[4 * q4 + 2], m[4 * q4 + 3]);
-      if (st < S) *reinterpret_cast<u32x2 *>(mt + 8 * q4) = u32x2{h0, h1};
-      if constexpr (DELTA) {
-        const int off = l32 * MS + 32 * ct + 8 * q4 + 4 * g;
-        *reinterpret_cast<u32x2 *>(sMh + off) = u32x2{h0, h1};
-        *reinterpret_cast<u32x2 *>(sMl + off) =
-            u32x2{pack_bf16x2(m[4 * q4] - lo_bf16(h0), m[4 * q4 + 1] - hi_bf16(h0)),
-                  pack_bf16x2(m[4 * q4 + 2] - lo_bf16(h1), m[4 * q4 + 3] - hi_bf16(h1))};
-      }
+      const int off = l32 * MS + 32 * ct + 8 * q4 + 4 * g;
+      *reinterpret_cast<u32x2 *>(sMh + off) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2 *>(sMl + off) =
+          u32x2{pack_bf16x2(m[4 * q4] - lo_bf16(h0), m[4 * q4 + 1] - hi_bf16(h0)),
+                pack_bf16x2(m[4 * q4 + 2] - lo_bf16(h1), m[4 * q4 + 3] - hi_bf16(h1))};
     }
   };
 
-  // Fragments of step s are loaded one step ahead, so their latency overlaps
-  // the previous step's MFMAs. G: 4 operand vectors (hi h=0,1, lo h=0,1) per
-  // 32-row tile kt of the contraction.
+  // G_s / H_s fragments of a step, loaded R - 1 steps ahead through a ring of
+  // R register sets (the loop is unrolled R times, so the sets do not move):
+  // 3 for the delta rule (80 registers a set), 8 for the linear rule (16). G: 4
+  // operand vectors (hi h = 0, 1, lo h = 0, 1) per 32-row tile kt of the
+  // contraction; H: this lane's 16 values. Every step issues its loads (past
+  // the last segment it reloads the last one), so that the wait before a
+  // step's work covers exactly the loads R - 1 steps old.
   constexpr int NG = DELTA ? ND : 1;
-  u32x4 gcur[NG][4];
-  float hcur[16];
-  auto load_step = [&](int st, u32x4 (&gd)[NG][4], float (&hd)[16]) {
+  constexpr int R = DELTA ? 3 : 8;
+  struct Frags {
+    u32x4 g[NG][4];
+    f32x4 h[4];
+  };
+  auto load_step = [&](int st, Frags &f) __attribute__((always_inline)) {
+    st = min(st, S - 1);
     const float *ghs = gh + (static_cast<size_t>(head) * S + st) * 2 * D * D;
-    const float *hf = ghs + static_cast<size_t>(D) * D + ((ct * ND + jt) * 16) * 64 + lane;
+    const f32x4 *hf = reinterpret_cast<const f32x4 *>(ghs + static_cast<size_t>(D) * D) +
+                      ((ct * ND + jt) * 64 + lane) * 4;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) hd[r] = hf[r * 64];
+    for (int q = 0; q < 4; ++q) f.h[q] = hf[q];
     if constexpr (DELTA) {
 #pragma unroll
       for (int kt = 0; kt < ND; ++kt) {
         const u32x4 *gf = reinterpret_cast<const u32x4 *>(ghs) + ((kt * ND + ct) * 64 + lane) * 4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) gd[kt][q] = gf[q];
+        for (int q = 0; q < 4; ++q) f.g[kt][q] = gf[q];
       }
     }
   };
-  if (S > 0) load_step(0, gcur, hcur);
-  publish(0);
-  if constexpr (DELTA) __syncthreads();
-
-  for (int s = 0; s < S; ++s) {
-    u32x4 gnext[NG][4];
-    float hnext[16];
-    if (s + 1 < S) load_step(s + 1, gnext, hnext);
+  // One segment: store the snapshot of the state before it, start the loads
+  // of the segment R - 1 ahead, then M += H_s (- G_s M for the delta rule).
+  auto step = [&](int s, const Frags &cur, Frags &ahead) __attribute__((always_inline)) {
+    // (The empty asm statements keep the snapshot stores and the loads at the
+    // top of their step: the compiler would otherwise sink loads whose values
+    // are needed two steps later past the loop exits toward their use. They
+    // can only do so because gh is not declared restrict.)
+    __asm__ volatile("" ::: "memory");
+    snapshot(s);
+    load_step(s + R - 1, ahead);
+    __asm__ volatile("" ::: "memory");
     if constexpr (DELTA) {
       // (G M)[32 ct + m][j] = sum_c G[c][32 ct + m] M[c][j] over c = 32 kt +
       // 16 h + 8 (slot / 4) + 4 g + slot % 4 in both operands.
@@ -519,32 +578,47 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *__restr
           const u32x2 l1 = *reinterpret_cast<const u32x2 *>(sMl + off + 8);
           const u32x4 bh = {h0[0], h0[1], h1[0], h1[1]};
           const u32x4 bl = {l0[0], l0[1], l1[0], l1[1]};
-          acc = mfma_bf16(gcur[kt][h], bh, acc);
-          acc = mfma_bf16(gcur[kt][h], bl, acc);
-          acc = mfma_bf16(gcur[kt][2 + h], bh, acc);
+          acc = mfma_bf16(cur.g[kt][h], bh, acc);
+          acc = mfma_bf16(cur.g[kt][h], bl, acc);
+          acc = mfma_bf16(cur.g[kt][2 + h], bh, acc);
         }
       }
-      __syncthreads();  // every wave has read M_{s-1} from LDS
+      lds_barrier();  // every wave has read M_{s-1} from LDS
 #pragma unroll
-      for (int r = 0; r < 16; ++r) m[r] = m[r] - acc[r] + hcur[r];
-      publish(s + 1);
-      __syncthreads();
+      for (int r = 0; r < 16; ++r) m[r] = m[r] - acc[r] + cur.h[r / 4][r % 4];
+      operand();
+      lds_barrier();
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) m[r] += hcur[r];
-      publish(s + 1);
+      for (int r = 0; r < 16; ++r) m[r] += cur.h[r / 4][r % 4];
     }
-    if (s + 1 < S) {
+  };
+
+  Frags f[R];
+  if (S > 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) hcur[r] = hnext[r];
-#pragma unroll
-      for (int kt = 0; kt < NG; ++kt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) gcur[kt][q] = gnext[kt][q];
+    for (int r = 0; r + 1 < R; ++r) load_step(r, f[r]);
+    if constexpr (DELTA) {
+      operand();
+      lds_barrier();
     }
+    // Whole rounds of R steps, then the rest (fewer than R). The rounds have
+    // no exits inside, so every path into the loop head has the same loads in
+    // flight and the waits stay exact.
+    int s = 0;
+    for (; s + R <= S; s += R) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) step(s + r, f[r], f[(r + R - 1) % R]);
+    }
+#pragma unroll
+    for (int r = 0; r + 1 < R; ++r)
+      if (s + r < S) step(s + r, f[r], f[(r + R - 1) % R]);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) Mh[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j] = m[r];
+  // The loads issued past the last segment land before the wave ends (vmcnt 0,
+  // lgkmcnt 0, expcnt at its maximum; gfx9 s_waitcnt encoding).
+  __builtin_amdgcn_s_waitcnt(7 << 4);
 }
 
 template <int D>
