@@ -123,6 +123,19 @@ def test_bitwise_deterministic():
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("S", [7, 8, 9, 11, 17])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode", ["linear", "delta"])
+def test_segment_counts_around_the_scan_ring(S, d, mode):
+    """Segment counts below, at and past the scan's register ring (3 steps for
+    the delta rule, 8 for the linear rule): whole rounds, a remainder, both."""
+    inp = synth.random_case(400 + 7 * S + d, B=1, Hq=2, Hkv=1, L=64 * S - 10, dk=d, dv=d,
+                            dtype="bf16", nonzero_state=True, scale=1.5 / np.sqrt(d) * 4)
+    log(f"S={S} d={d} {mode}")
+    check_all(f"S={S} d{d} {mode}", run_gpu(inp, "bf16", 64, mode),
+              run_oracle(inp, "bf16", 64, mode), "bf16")
+
+
 @pytest.mark.parametrize("seg_len", [1, 5, 2000])
 def test_segment_length_extremes(seg_len):
     """N = 1 (every row its own segment), an odd N, and N > L (one short segment)."""
