@@ -29,14 +29,17 @@
 // (rt, ct) holds, for MFMA-result register r and lane l, the element at row
 // 32 rt + kappa(r, l / 32), column 32 ct + l % 32, where
 // kappa(r, g) = 8 (r / 4) + 4 g + r % 4 is the 32x32 MFMA result row map.
-//   H_s (fp32): element index ((rt * (D/32) + ct) * 64 + l) * 16 + r (a lane's
-//     16 values contiguous: four 16-byte loads).
-//   G_s (bf16 hi/lo): 32-bit word ((rt * (D/32) + ct) * 64 + l) * 16 + w, where
-//     word 4 h + p (h, p < 2, 4) packs the hi parts of registers 8 h + 2 p
+// A lane's 16 values (words) of a tile are kept as four 16-byte quarters, and
+// quarter q of all 64 lanes is contiguous, so that every 16-byte load or store
+// of a wave covers one contiguous kilobyte:
+//   H_s (fp32): element index (((rt * (D/32) + ct) * 4 + r / 4) * 64 + l) * 4 + r % 4.
+//   G_s (bf16 hi/lo): 32-bit word (((rt * (D/32) + ct) * 4 + w / 4) * 64 + l) * 4 + w % 4,
+//     where word 4 h + p (h, p < 2, 4) packs the hi parts of registers 8 h + 2 p
 //     (low half) and 8 h + 2 p + 1 (high half), and word 8 + 4 h + p the lo
-//     parts; so words 4 h .. 4 h + 3 are directly the 8-slot bf16 A operand of
-//     a 32x32x16 MFMA over rows 32 rt + 16 h .. + 15. G_s is symmetric, so
-//     tile (kt, ct) read this way is the A operand for output rows of tile ct.
+//     parts; so quarter h (hi) and quarter 2 + h (lo) are directly the 8-slot
+//     bf16 A operands of a 32x32x16 MFMA over rows 32 rt + 16 h .. + 15. G_s is
+//     symmetric, so tile (kt, ct) read this way is the A operand for output
+//     rows of tile ct.
 
 #include "common.h"
 #include "launch.h"
@@ -455,16 +458,16 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
             wd[q] = hw;
             wd[8 + q] = pack_bf16x2(x0 - lo_bf16(hw), x1 - hi_bf16(hw));
           }
-          u32x4 *f = reinterpret_cast<u32x4 *>(base) + ((rt * ND + ct) * 64 + lane) * 4;
+          u32x4 *f = reinterpret_cast<u32x4 *>(base) + (rt * ND + ct) * 256 + lane;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            f[q] = u32x4{wd[4 * q], wd[4 * q + 1], wd[4 * q + 2], wd[4 * q + 3]};
+            f[64 * q] = u32x4{wd[4 * q], wd[4 * q + 1], wd[4 * q + 2], wd[4 * q + 3]};
         } else {
           f32x4 *f = reinterpret_cast<f32x4 *>(base + static_cast<size_t>(D) * D) +
-                     ((rt * ND + ct) * 64 + lane) * 4;
+                     (rt * ND + ct) * 256 + lane;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            f[q] = f32x4{acc[pi][rt][4 * q], acc[pi][rt][4 * q + 1], acc[pi][rt][4 * q + 2],
+            f[64 * q] = f32x4{acc[pi][rt][4 * q], acc[pi][rt][4 * q + 1], acc[pi][rt][4 * q + 2],
                          acc[pi][rt][4 * q + 3]};
         }
       }
@@ -540,15 +543,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *gh,  //
     st = min(st, S - 1);
     const float *ghs = gh + (static_cast<size_t>(head) * S + st) * 2 * D * D;
     const f32x4 *hf = reinterpret_cast<const f32x4 *>(ghs + static_cast<size_t>(D) * D) +
-                      ((ct * ND + jt) * 64 + lane) * 4;
+                      (ct * ND + jt) * 256 + lane;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) f.h[q] = hf[q];
+    for (int q = 0; q < 4; ++q) f.h[q] = hf[64 * q];
     if constexpr (DELTA) {
 #pragma unroll
       for (int kt = 0; kt < ND; ++kt) {
-        const u32x4 *gf = reinterpret_cast<const u32x4 *>(ghs) + ((kt * ND + ct) * 64 + lane) * 4;
+        const u32x4 *gf = reinterpret_cast<const u32x4 *>(ghs) + (kt * ND + ct) * 256 + lane;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) f.g[kt][q] = gf[q];
+        for (int q = 0; q < 4; ++q) f.g[kt][q] = gf[64 * q];
       }
     }
   };
