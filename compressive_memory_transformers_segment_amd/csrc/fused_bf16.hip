@@ -62,7 +62,8 @@
 //     and the gate parameters travel in a side area of the snapshot's slot).
 //     Rows are stored through a buffer resource that ends at the segment end,
 //     so every wave issues the same stores and the hardware drops those past
-//     it.
+//     it. The two lanes that hold one row exchange halves first, so that each
+//     store writes 16 contiguous bytes per lane (32 per row and instruction).
 
 #include <type_traits>
 
@@ -475,17 +476,32 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
       for (int t = 0; t < NT; ++t) am = mfma32(as_bf16x8(ma[t]), as_bf16x8(qf[t]), am);
       if (dt + 1 < ND) mread(dt + 1);
       __builtin_amdgcn_sched_barrier(0);
+      uint32_t pk[4][2];
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
-        uint32_t pk[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int i0 = 4 * gi + 2 * jj;
-          pk[jj] = pack_bf16x2(w_mem * am[i0] + w_dot * o[dt][i0],
-                               w_mem * am[i0 + 1] + w_dot * o[dt][i0 + 1]);
+          pk[gi][jj] = pack_bf16x2(w_mem * am[i0] + w_dot * o[dt][i0],
+                                   w_mem * am[i0 + 1] + w_dot * o[dt][i0 + 1]);
         }
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pk[0], pk[1]}, rsrc,
-                                              lane_off + (32 * dt + 8 * gi + 4 * g) * 2, 0, 0);
+      }
+      // Lane group g holds values 8 gi + 4 g + 0..3 of the block; swapping the
+      // words of chunks 2p, 2p + 1 with the lane 32 away (upper half of the
+      // first operand with the lower half of the second) leaves values
+      // 16 p + 8 g + 0..7 in the lane: one 16-byte store per p.
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        uint32_t a[2], b[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const auto r = __builtin_amdgcn_permlane32_swap(pk[2 * p][jj], pk[2 * p + 1][jj], false,
+                                                          false);
+          a[jj] = r[0];
+          b[jj] = r[1];
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{a[0], a[1], b[0], b[1]}, rsrc,
+                                               lane_off + (32 * dt + 16 * p + 8 * g) * 2, 0, 0);
       }
     }
   };
