@@ -503,15 +503,34 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *gh,  //
   for (int r = 0; r < 16; ++r) m[r] = Mh[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j];
 
   // The state before segment st: the global bf16 snapshot M_{st-1}^T (st < S)
-  // and, for the delta rule, the hi/lo operand copy in LDS. This lane's rows
-  // 32 ct + 8 q4 + 4 g + 0..3 are contiguous in the transposed layouts.
+  // and, for the delta rule, the hi/lo operand copy in LDS. This lane holds
+  // rows 32 ct + 8 q4 + 4 g + 0..3, which are contiguous in the transposed
+  // layouts.
+  // The two lanes holding one row of the snapshot (32 apart) swap halves
+  // first (upper half of the first operand with the lower half of the
+  // second), so that each lane stores 8 contiguous values: rows
+  // 32 ct + 16 p + 8 g + 0..7, one 16-byte store per p.
   auto snapshot = [&](int st) __attribute__((always_inline)) {
     uint16_t *mt = mt_pre + (static_cast<size_t>(head) * S + st) * D * D +
-                   static_cast<size_t>(j) * D + 32 * ct + 4 * g;
+                   static_cast<size_t>(j) * D + 32 * ct + 8 * g;
+    uint32_t wd[4][2];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<u32x2 *>(mt + 8 * q4) =
-          u32x2{pack_bf16x2(m[4 * q4], m[4 * q4 + 1]), pack_bf16x2(m[4 * q4 + 2], m[4 * q4 + 3])};
+    for (int q4 = 0; q4 < 4; ++q4) {
+      wd[q4][0] = pack_bf16x2(m[4 * q4], m[4 * q4 + 1]);
+      wd[q4][1] = pack_bf16x2(m[4 * q4 + 2], m[4 * q4 + 3]);
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      uint32_t x[2], y[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const auto r = __builtin_amdgcn_permlane32_swap(wd[2 * p][jj], wd[2 * p + 1][jj], false,
+                                                        false);
+        x[jj] = r[0];
+        y[jj] = r[1];
+      }
+      *reinterpret_cast<u32x4 *>(mt + 16 * p) = u32x4{x[0], x[1], y[0], y[1]};
+    }
   };
   auto operand = [&]() __attribute__((always_inline)) {
 #pragma unroll
