@@ -56,14 +56,12 @@ __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
 
 __device__ __forceinline__ int kappa(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
-// Sum of x over the lanes l, l ^ 16, l ^ 32 and l ^ 48 (the same value in all
-// four). v_permlane16_swap / v_permlane32_swap with both operands equal to x
-// return, in every lane, x of the lane and of its partner 16 / 32 away.
-__device__ __forceinline__ float sum_lanes_16_32(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+// x of another lane of the same 16-lane row, by DPP control CTRL (all lanes
+// active): quad_perm 0xB1 = lane ^ 1, 0x4E = lane ^ 2; row_half_mirror 0x141
+// = lane 7 - i within 8; row_mirror 0x140 = lane 15 - i within 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Workgroup barrier that orders LDS only. __syncthreads() also waits for every
@@ -212,10 +210,6 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
   // Per group: sigma(K)^T, V^T and (delta) (sigma(K)/den)^T, [col][key].
   __shared__ __attribute__((aligned(16))) uint16_t sStage[RG][NB][D * kStr];
   __shared__ float sZ[D];
-  // Partial denominators: per row of the chunk, one sum over each wave's 32
-  // columns (the waves holding staging items: CCH / 4 of them).
-  constexpr int NWD = CCH / 4;
-  __shared__ __attribute__((aligned(16))) float sDenPart[RG][NWD][64];
 
   // Work item wi = (head * S + s) * CS + cs. When the launch divides evenly,
   // consecutive work items go to one XCD (hardware hands out workgroups
@@ -252,7 +246,20 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
   // Chunk iterations of every group (the groups take chunks grp, grp + RG, ...).
   const int iters = ((e - a + 63) / 64 + RG - 1) / RG;
   const bool has = tg < ITEMS;
-  const int kg = tg & 15, cc = tg >> 4;  // rows 4 kg .. 4 kg + 3, columns 8 cc .. 8 cc + 7
+  // Rows 4 kg .. 4 kg + 3, columns 8 cc .. 8 cc + 7. The column chunks of a row
+  // lie in consecutive lanes, so that each load of a wave reads whole rows.
+  const int kg = tg / CCH, cc = tg % CCH;
+  // The staging buffers hold [column][key], with key unit (4 keys, 8 bytes) u
+  // of column c at position u ^ kswz(c): the transposed writes of a wave then
+  // spread over all banks (the lanes of one write cover 16 columns 8 apart
+  // and four key units), while the operand reads, which take one unit of 32
+  // consecutive columns at a time, keep their pattern.
+  auto kswz = [](int col) __attribute__((always_inline)) {
+    return ((col >> 5) & (CCH / 4 - 1)) * (64 / CCH);
+  };
+  auto kpos = [&](int col, int unit) __attribute__((always_inline)) {
+    return col * kStr + 4 * (unit ^ kswz(col));
+  };
 
   // Register staging of 64-row chunks (4 rows x 8 columns per item), two
   // register sets: a chunk's loads are issued two chunks before it is staged.
@@ -295,33 +302,44 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
           vw[r][jj] = in ? vv[r][jj] : 0u;
         }
       }
-      if constexpr (DELTA) {
-        // sigma(k_i).z over this thread's 8 columns, then over the 32 columns
-        // of its wave (the lanes 16 apart hold the same rows), written once
-        // per wave and row.
-        f32x4 p;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = 0.f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x += kf[r][j] * sZ[cc * 8 + j];
-          p[r] = sum_lanes_16_32(x);
-        }
-        if ((cc & 3) == 0) *reinterpret_cast<f32x4 *>(&sDenPart[grp][cc >> 2][4 * kg]) = p;
-      }
       // transposed stores: one 8-byte write of 4 keys per column
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const u32x2 kk2 = {pack_bf16x2(kf[0][j], kf[1][j]), pack_bf16x2(kf[2][j], kf[3][j])};
-        *reinterpret_cast<u32x2 *>(sKt + (cc * 8 + j) * kStr + 4 * kg) = kk2;
+        *reinterpret_cast<u32x2 *>(sKt + kpos(cc * 8 + j, kg)) = kk2;
       }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const uint32_t r0 = vw[0][jj], r1 = vw[1][jj], r2 = vw[2][jj], r3 = vw[3][jj];
         const u32x2 lo = {(r0 & 0xffffu) | (r1 << 16), (r2 & 0xffffu) | (r3 << 16)};
         const u32x2 hi = {(r0 >> 16) | (r1 & 0xffff0000u), (r2 >> 16) | (r3 & 0xffff0000u)};
-        *reinterpret_cast<u32x2 *>(sVt + (cc * 8 + 2 * jj) * kStr + 4 * kg) = lo;
-        *reinterpret_cast<u32x2 *>(sVt + (cc * 8 + 2 * jj + 1) * kStr + 4 * kg) = hi;
+        *reinterpret_cast<u32x2 *>(sVt + kpos(cc * 8 + 2 * jj, kg)) = lo;
+        *reinterpret_cast<u32x2 *>(sVt + kpos(cc * 8 + 2 * jj + 1, kg)) = hi;
+      }
+      if constexpr (DELTA) {
+        // den_i = sigma(k_i).z + eps: this thread's 8 columns, then the
+        // row's CCH chunks, which sit in consecutive lanes (DPP: lane pairs,
+        // quads, mirrored halves of 8 and of 16 lanes; every lane ends with
+        // the same sum). Then (sigma(K) / den)^T, one 8-byte write per column.
+        float rd[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x += kf[r][j] * sZ[cc * 8 + j];
+          x += dpp_f32<0xB1>(x);  // lane ^ 1
+          x += dpp_f32<0x4E>(x);  // lane ^ 2
+          if constexpr (CCH >= 8) x += dpp_f32<0x141>(x);  // lane i <-> 7 - i
+          if constexpr (CCH >= 16) x += dpp_f32<0x140>(x);  // lane i <-> 15 - i
+          // (v_rcp_f32, within 1 ulp: W is rounded to bf16 right after.)
+          rd[r] = __builtin_amdgcn_rcpf(x + eps);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x2 w2 = {pack_bf16x2(kf[0][j] * rd[0], kf[1][j] * rd[1]),
+                            pack_bf16x2(kf[2][j] * rd[2], kf[3][j] * rd[3])};
+          *reinterpret_cast<u32x2 *>(sWt + kpos(cc * 8 + j, kg)) = w2;
+        }
       }
     }
     lds_barrier();
@@ -336,35 +354,15 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
         const int u = tg + 256 * uu;
         const int d = u >> 3;
         const int q = vt_unit_pos(d, u & 7);  // the swizzle is its own inverse
-        const int k0 = 16 * (q >> 1) + 4 * (q & 1);
-        const u32x2 r0 = *reinterpret_cast<const u32x2 *>(sVt + d * kStr + k0);
-        const u32x2 r1 = *reinterpret_cast<const u32x2 *>(sVt + d * kStr + k0 + 8);
+        const int u0 = 4 * (q >> 1) + (q & 1);  // key units u0 and u0 + 2
+        const u32x2 r0 = *reinterpret_cast<const u32x2 *>(sVt + kpos(d, u0));
+        const u32x2 r1 = *reinterpret_cast<const u32x2 *>(sVt + kpos(d, u0 + 2));
         *reinterpret_cast<u32x4 *>(vtile + u * 8) = u32x4{r0[0], r0[1], r1[0], r1[1]};
       }
     }
     // cur is free once staged: load the chunk this set takes next (copies of
     // the last row, for a chunk the loop never stages).
     load_chunk(cur, i0 + 128 * RG);
-    if constexpr (DELTA) {
-      // (sigma(K) / den)^T: den of this thread's rows from the waves' partial
-      // sums (added in a fixed order), then one 8-byte write per column.
-      if (has) {
-        f32x4 den = {eps, eps, eps, eps};
-#pragma unroll
-        for (int q = 0; q < NWD; ++q) den += *reinterpret_cast<const f32x4 *>(&sDenPart[grp][q][4 * kg]);
-        // (v_rcp_f32, within 1 ulp: W is rounded to bf16 right after.)
-        float rd[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rd[r] = __builtin_amdgcn_rcpf(den[r]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const u32x2 w2 = {pack_bf16x2(kf[0][j] * rd[0], kf[1][j] * rd[1]),
-                            pack_bf16x2(kf[2][j] * rd[2], kf[3][j] * rd[3])};
-          *reinterpret_cast<u32x2 *>(sWt + (cc * 8 + j) * kStr + 4 * kg) = w2;
-        }
-      }
-      lds_barrier();
-    }
 
     // Contraction over the 64 keys of the chunk, 16 per MFMA. Slot j of lane
     // group g is key kb + 8 (j / 4) + 4 g + j % 4 in both operands.
@@ -373,9 +371,9 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
       u32x4 av[ND];
 #pragma unroll
       for (int rt = 0; rt < ND; ++rt) {
-        const uint16_t *p = sKt + (32 * rt + l32) * kStr + kb + 4 * g;
-        const u32x2 x0 = *reinterpret_cast<const u32x2 *>(p);
-        const u32x2 x1 = *reinterpret_cast<const u32x2 *>(p + 8);
+        const int col = 32 * rt + l32;
+        const u32x2 x0 = *reinterpret_cast<const u32x2 *>(sKt + kpos(col, kb / 4 + g));
+        const u32x2 x1 = *reinterpret_cast<const u32x2 *>(sKt + kpos(col, kb / 4 + 2 + g));
         av[rt] = u32x4{x0[0], x0[1], x1[0], x1[1]};
       }
 #pragma unroll
@@ -385,9 +383,9 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
           const bool is_g = DELTA && pr < ND;
           const int ct = pr % ND;
           const uint16_t *src = is_g ? sWt : sVt;
-          const uint16_t *p = src + (32 * ct + l32) * kStr + kb + 4 * g;
-          const u32x2 x0 = *reinterpret_cast<const u32x2 *>(p);
-          const u32x2 x1 = *reinterpret_cast<const u32x2 *>(p + 8);
+          const int col = 32 * ct + l32;
+          const u32x2 x0 = *reinterpret_cast<const u32x2 *>(src + kpos(col, kb / 4 + g));
+          const u32x2 x1 = *reinterpret_cast<const u32x2 *>(src + kpos(col, kb / 4 + 2 + g));
           const u32x4 bv = {x0[0], x0[1], x1[0], x1[1]};
 #pragma unroll
           for (int rt = 0; rt < ND; ++rt) acc[pi][rt] = mfma_bf16(av[rt], bv, acc[pi][rt]);
