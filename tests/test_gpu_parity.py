@@ -181,3 +181,14 @@ def test_invalid_arguments_are_rejected_before_launch():
                                M.data_ptr(), z.data_ptr(), 64, 3, q.data_ptr())
     assert ei.value.status == -1
     assert inp["q"].shape == (1, 2, 64, 64)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_one_long_segment_is_full_causal_attention(d):
+    """N = L: one segment of 3000 rows (47 key tiles, a ragged tail), the
+    full-causal case the scaling sweep uses as its quadratic reference."""
+    inp = synth.random_case(500 + d, B=1, Hq=2, Hkv=1, L=3000, dk=d, dv=d, dtype="bf16",
+                            nonzero_state=True, scale=1.5 / np.sqrt(d) * 4)
+    log(f"one segment L=N=3000 d={d}")
+    check_all(f"N=L d{d}", run_gpu(inp, "bf16", 3000, "delta"),
+              run_oracle(inp, "bf16", 3000, "delta"), "bf16")
