@@ -30,4 +30,5 @@ from .infini_ref import (  # noqa: F401
     memory_update,
     infini_attention,
     memory_chain,
+    streaming_decode,
 )

@@ -205,3 +205,59 @@ def memory_chain(k: np.ndarray, v: np.ndarray, M0: np.ndarray, z0: np.ndarray, s
         vs = v[a:e] if upcast is None else upcast(v[a:e])
         M, z = memory_update(ks, vs, M, z, mode, eps)
     return M, z, states
+
+
+def streaming_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: np.ndarray,
+                     M0: np.ndarray, z0: np.ndarray, seg_len: int, mode: str, chunk: int = 1,
+                     eps: float = 1e-6) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Streaming inference: the tokens arrive in chunks of ``chunk`` rows (a
+    chunk never crosses a segment boundary), and only the current segment's
+    K/V rows plus (M, z) are kept.
+
+    For each arriving row at position p of its segment: local causal attention
+    over the cached rows 0..p of the segment, retrieval from the state before
+    the segment, the gate mix. When the segment's last row has arrived (or the
+    stream ends inside a segment), the cached rows are written into (M, z) and
+    the cache is emptied. Same shapes and return values as ``infini_attention``.
+
+    [HF-repro] "Infini-Attention メカニズム", steps Memory Update and State
+    Transfer (only the memory is handed on, the past segment's K/V is not
+    kept); [LNCB-review] "実装上の流れ" (attend and retrieve, then update the
+    memory with the current K/V and move to the next segment).
+    """
+    B, Hq, L, dk = q.shape
+    Hkv = k.shape[1]
+    dv = v.shape[3]
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    gamma = gate_value(beta)
+    M = np.array(M0, dtype=np.float64, copy=True)
+    z = np.array(z0, dtype=np.float64, copy=True)
+    out = np.empty((B, Hq, L, dv), dtype=np.float64)
+    cache_k = np.zeros((B, Hkv, seg_len, dk), dtype=np.float64)
+    cache_v = np.zeros((B, Hkv, seg_len, dv), dtype=np.float64)
+    n_cached = 0
+    t = 0
+    while t < L:
+        n_new = min(chunk, seg_len - n_cached, L - t)
+        # the new rows join the cache before they attend (each sees itself)
+        cache_k[:, :, n_cached:n_cached + n_new] = k[:, :, t:t + n_new]
+        cache_v[:, :, n_cached:n_cached + n_new] = v[:, :, t:t + n_new]
+        pos = np.arange(n_cached, n_cached + n_new)
+        for b in range(B):
+            for h in range(Hq):
+                j = kv_head_of(h, Hq, Hkv)
+                rows = q[b, h, t:t + n_new]
+                a_dot = local_causal_attention_rows(rows, pos, cache_k[b, j], cache_v[b, j])
+                a_mem = memory_retrieval(rows, M[b, j], z[b, j], eps)
+                out[b, h, t:t + n_new] = gamma[h] * a_mem + (1.0 - gamma[h]) * a_dot
+        n_cached += n_new
+        t += n_new
+        if n_cached == seg_len or t == L:
+            for b in range(B):
+                for j in range(Hkv):
+                    M[b, j], z[b, j] = memory_update(cache_k[b, j, :n_cached],
+                                                     cache_v[b, j, :n_cached], M[b, j], z[b, j],
+                                                     mode, eps)
+            n_cached = 0
+    return out, M, z

@@ -284,9 +284,27 @@ def pin_p12_delta_affine(ora):
         close(M2, (np.eye(dk) - G) @ M + H, rtol=1e-11, atol=1e-12, what="P-12")
 
 
+def pin_p13_streaming(ora):
+    """Streaming decode (chunks of 1, 2 or 3 rows, and whole segments) equals
+    the token-by-token brute force: outputs, and the state after the stream
+    (the last, unfinished segment written at the end)."""
+    for shp, N, mode, chunk in [(dict(B=2, Hq=4, Hkv=2, L=7, dk=3, dv=2), 3, m, c)
+                                for m in ("linear", "delta") for c in (1, 2, 3)] + [
+            (dict(B=1, Hq=2, Hkv=1, L=5, dk=3, dv=3), 2, "delta", 2)]:
+        c = case64(131 + N + chunk, scale=1.4, nonzero_state=True, **shp)
+        out, M, z = ora.streaming_decode(c["q"], c["k"], c["v"], c["beta"], c["M0"], c["z0"], N,
+                                         mode, chunk, c["eps"])
+        bo, bM, bz = ind.brute_force(c["q"], c["k"], c["v"], c["beta"], c["M0"], c["z0"], N,
+                                     mode, c["eps"])
+        tag = f"P-13 {mode} N={N} chunk={chunk}"
+        close(out, bo, rtol=1e-11, atol=1e-12, what=f"{tag} out")
+        close(M, bM, rtol=1e-11, atol=1e-12, what=f"{tag} M")
+        close(z, bz, rtol=1e-13, atol=1e-13, what=f"{tag} z")
+
+
 ALL_PINS = [
     pin_sigma_library, pin_gate_library, pin_golden, pin_p1_sdpa, pin_p2_dense_linear,
     pin_p3_linear_closed_form, pin_p4_zero_start, pin_p5_delta_fixed_point, pin_p6_exact,
     pin_p7_brute_force, pin_p8_gqa, pin_p9_split_calls, pin_p10_structure,
-    pin_p11_unit_segments, pin_p12_delta_affine,
+    pin_p11_unit_segments, pin_p12_delta_affine, pin_p13_streaming,
 ]

@@ -20,7 +20,8 @@ def test_oracle_pin(pin):
 
 _orig = {n: getattr(ref, n) for n in ("elu_plus_one", "gate_value", "kv_head_of",
                                        "local_causal_attention", "memory_retrieval",
-                                       "memory_update", "infini_attention")}
+                                       "memory_update", "infini_attention",
+                                       "streaming_decode")}
 
 
 def _retrieval_no_eps(qs, M, z, eps):
@@ -95,6 +96,46 @@ def _update_before_retrieval(q, k, v, beta, M0, z0, seg_len, mode, eps=1e-6):
     return out, M, z
 
 
+def _stream_factory(variant):
+    """streaming_decode with one step of the stream done wrong."""
+    def stream(q, k, v, beta, M0, z0, seg_len, mode, chunk=1, eps=1e-6):
+        B, Hq, L, dk = q.shape
+        Hkv = k.shape[1]
+        gamma = ref.gate_value(beta)
+        M, z = np.array(M0, dtype=np.float64), np.array(z0, dtype=np.float64)
+        out = np.empty((B, Hq, L, v.shape[3]))
+        ck, cv, n, t = [], [], 0, 0
+        while t < L:
+            m = min(chunk, seg_len - n, L - t)
+            for r in range(m):
+                for b in range(B):
+                    for h in range(Hq):
+                        j = ref.kv_head_of(h, Hq, Hkv)
+                        keys = np.array([x[b, j] for x in ck] + [k[b, j, t + r]])
+                        vals = np.array([x[b, j] for x in cv] + [v[b, j, t + r]])
+                        if variant == "exclusive" and len(keys) > 1:
+                            keys, vals = keys[:-1], vals[:-1]
+                        row = q[b, h, t + r][None]
+                        a_dot = ref.local_causal_attention_rows(row, np.array([len(keys) - 1]),
+                                                                keys, vals)
+                        a_mem = ref.memory_retrieval(row, M[b, j], z[b, j], eps)
+                        out[b, h, t + r] = gamma[h] * a_mem[0] + (1 - gamma[h]) * a_dot[0]
+                ck.append(k[:, :, t + r]); cv.append(v[:, :, t + r])
+            n += m
+            t += m
+            if n == seg_len or t == L or variant == "update_every_chunk":
+                start = len(ck) - (m if variant == "update_every_chunk" else n)
+                for b in range(B):
+                    for j in range(Hkv):
+                        ks = np.array([x[b, j] for x in ck[start:]])
+                        vs = np.array([x[b, j] for x in cv[start:]])
+                        M[b, j], z[b, j] = ref.memory_update(ks, vs, M[b, j], z[b, j], mode, eps)
+                if n == seg_len or t == L:
+                    ck, cv, n = [], [], 0
+        return out, M, z
+    return stream
+
+
 MUTANTS = {
     "no_eps_retrieval": ("memory_retrieval", _retrieval_no_eps),
     "sigma_on_scaled_q": ("memory_retrieval", _retrieval_scaled_q),
@@ -110,6 +151,8 @@ MUTANTS = {
     "elu_without_plus_one": ("elu_plus_one", lambda x: _orig["elu_plus_one"](x) - 1.0),
     "gqa_modulo": ("kv_head_of", lambda h, hq, hkv: h % hkv),
     "update_before_retrieval": ("infini_attention", _update_before_retrieval),
+    "stream_row_misses_itself": ("streaming_decode", _stream_factory("exclusive")),
+    "stream_updates_every_chunk": ("streaming_decode", _stream_factory("update_every_chunk")),
 }
 
 
