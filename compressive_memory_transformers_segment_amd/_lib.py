@@ -27,7 +27,8 @@ DELTA = 1
 
 EXPORTS = ("infini_attn_check", "infini_attn_workspace_size", "infini_attn_create",
            "infini_attn_forward", "infini_attn_destroy", "infini_attn_strerror",
-           "infini_attn_set_timing", "infini_attn_get_timing")
+           "infini_attn_set_timing", "infini_attn_get_timing", "infini_attn_decode",
+           "infini_attn_update")
 
 
 class InfiniAttnDesc(ctypes.Structure):
@@ -77,6 +78,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.infini_attn_create.restype = ctypes.c_int
         lib.infini_attn_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
         lib.infini_attn_forward.restype = ctypes.c_int
+        lib.infini_attn_decode.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp, vp]
+        lib.infini_attn_decode.restype = ctypes.c_int
+        lib.infini_attn_update.argtypes = [vp, vp, vp, vp, vp, i32]
+        lib.infini_attn_update.restype = ctypes.c_int
         lib.infini_attn_destroy.argtypes = [vp]
         lib.infini_attn_destroy.restype = ctypes.c_int
         lib.infini_attn_set_timing.argtypes = [vp, i32]
@@ -135,6 +140,20 @@ def infini_attn_forward(handle: int, q: int, k: int, v: int, beta: int, M: int, 
         raise InfiniAttnError(st, "infini_attn_forward")
 
 
+def infini_attn_decode(handle: int, q: int, n_new: int, k_cache: int, v_cache: int, n_past: int,
+                       beta: int, M: int, z: int, out: int) -> None:
+    st = load().infini_attn_decode(handle, q, int(n_new), k_cache, v_cache, int(n_past), beta, M,
+                                   z, out)
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_decode")
+
+
+def infini_attn_update(handle: int, k: int, v: int, M: int, z: int, update_mode: int) -> None:
+    st = load().infini_attn_update(handle, k, v, M, z, int(update_mode))
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_update")
+
+
 def infini_attn_destroy(handle: Optional[int]) -> None:
     st = load().infini_attn_destroy(handle)
     if st != OK:
@@ -169,11 +188,14 @@ def _mode(update_mode) -> int:
     return int(update_mode)
 
 
-def handle_for(q, k, eps: float = 1e-6, stream=None) -> int:
-    """Cached handle for this shape, dtype, eps, device and stream."""
+def handle_for(q, k, eps: float = 1e-6, stream=None, seq_len: Optional[int] = None) -> int:
+    """Cached handle for this shape, dtype, eps, device and stream (seq_len:
+    the rows per head of the handle, by default those of q)."""
     import torch
 
     B, Hq, L, D = q.shape
+    if seq_len is not None:
+        L = int(seq_len)
     Hkv = k.shape[1]
     dtype = {torch.float32: F32, torch.bfloat16: BF16}.get(q.dtype)
     if dtype is None:
@@ -222,6 +244,65 @@ def forward(q, k, v, beta, M, z, seg_len: int, update_mode="linear", out=None,
     infini_attn_forward(h, q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
                         M.data_ptr(), z.data_ptr(), seg_len, _mode(update_mode), out.data_ptr())
     return out
+
+
+def _check_device_tensors(**ts):
+    import torch
+
+    for name, t in ts.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name in ("beta", "M", "z"):
+        if name in ts and ts[name].dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+
+
+def decode(q, k_cache, v_cache, n_past: int, beta, M, z, out=None, eps: float = 1e-6):
+    """Streaming decode of q [B, Hq, C, d] (positions n_past .. n_past + C - 1
+    of the current segment) against k_cache / v_cache [B, Hkv, cap, d], whose
+    rows 0 .. n_past + C - 1 hold the segment (the new rows included). (M, z)
+    is the state before the segment and is not modified. Returns out
+    [B, Hq, C, d]."""
+    import torch
+
+    _check_device_tensors(q=q, k_cache=k_cache, v_cache=v_cache, beta=beta, M=M, z=z)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the cache must share one dtype")
+    B, Hq, C, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if (tuple(k_cache.shape) != (B, Hkv, cap, D) or tuple(v_cache.shape) != (B, Hkv, cap, D)
+            or tuple(beta.shape) != (Hq,) or tuple(M.shape) != (B, Hkv, D, D)
+            or tuple(z.shape) != (B, Hkv, D)):
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    h = handle_for(q, k_cache, eps, seq_len=cap)
+    infini_attn_decode(h, q.data_ptr(), C, k_cache.data_ptr(), v_cache.data_ptr(), n_past,
+                       beta.data_ptr(), M.data_ptr(), z.data_ptr(), out.data_ptr())
+    return out
+
+
+def update(k, v, M, z, update_mode="linear", eps: float = 1e-6, n_q_heads: Optional[int] = None):
+    """Write one finished segment k, v [B, Hkv, n, d] into (M, z) in place."""
+    _check_device_tensors(k=k, v=v, M=M, z=z)
+    if v.dtype != k.dtype:
+        raise TypeError("k and v must share one dtype")
+    B, Hkv, n, D = k.shape
+    if (tuple(v.shape) != (B, Hkv, n, D) or tuple(M.shape) != (B, Hkv, D, D)
+            or tuple(z.shape) != (B, Hkv, D)):
+        raise ValueError("inconsistent shapes")
+    # The update does not depend on the number of query heads; the handle
+    # records one (Hkv unless given) only because every handle has one.
+    hq = Hkv if n_q_heads is None else int(n_q_heads)
+    qlike = k.new_empty((B, hq, 0, D))
+    h = handle_for(qlike, k, eps, seq_len=n)
+    infini_attn_update(h, k.data_ptr(), v.data_ptr(), M.data_ptr(), z.data_ptr(),
+                       _mode(update_mode))
+    return M, z
 
 
 def release_handles() -> None:

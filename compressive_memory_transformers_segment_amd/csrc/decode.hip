@@ -1,0 +1,387 @@
+// Streaming decode for gfx950: a chunk of C new query rows per (batch, query
+// head) attends causally to the rows of the current segment held in a K/V
+// cache, retrieves from the memory state before that segment, and mixes the
+// two with the head's gate.
+//
+// [HF-repro] "Infini-Attention メカニズム": steps Local Attention (causal
+// attention inside the current segment), Memory Retrieval (sigma(q) M /
+// (sigma(q) z + eps) against the pre-segment state), Integration (gate), and
+// State Transfer (only (M, z) and the current segment's rows are kept).
+//
+// The work is a few query rows against at most one segment of keys, so it is
+// bound by reading the cache (and M) once, not by arithmetic: it runs on the
+// vector ALUs in fp32, in two kernels.
+//   * decode_partial: one workgroup per (split of 64 keys, batch x kv head,
+//     block of 16 queries), so a 2048-row cache of 8 kv heads already gives
+//     256 workgroups for one new row. Queries are (query head of the group,
+//     chunk row) pairs: the g heads that share a kv head share one read of
+//     its keys. The split's keys, values and the block's queries move to LDS
+//     with 16-byte loads (all issued before the first LDS write, widened to
+//     fp32); lane j of a wave scores key j against the wave's four queries,
+//     the split's max and sum come from DPP and lane-swap reductions, and P V
+//     accumulates with the lanes over value columns. Each split writes its
+//     unnormalised partial (acc, max m, sum l).
+//   * decode_combine: one workgroup per (batch x kv head, block of 4
+//     queries). Its four waves split the rows of M (each wave issues all its
+//     loads at once) and multiply them with the four queries' sigma(q) from
+//     LDS; the partial numerators meet in LDS. Wave w then merges the split
+//     partials of query w with the usual max-rescaling, adds the retrieval
+//     (denominator sigma(q).z by a wave reduction), applies the gate and
+//     stores the row.
+
+#include "common.h"
+#include "launch.h"
+
+namespace ia {
+namespace {
+
+constexpr int kDecKeys = 64;         // keys per workgroup (one split)
+constexpr int kDecQPW = 4;           // queries per wave
+constexpr int kDecQB = 4 * kDecQPW;  // queries per workgroup (4 waves)
+
+// x of another lane of the same 16-lane row, by DPP control CTRL: quad_perm
+// 0xB1 = lane ^ 1, 0x4E = lane ^ 2; row_half_mirror 0x141 = lane 7 - i within
+// 8; row_mirror 0x140 = lane 15 - i within 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Reductions over the 64 lanes; every lane ends with the same value (each
+// step combines a lane with its partner by a commutative operation).
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Value column of lane `lane` for its e-th accumulator (D = 32: lanes 32..63
+// mirror lanes 0..31 and store nothing).
+template <int D>
+__device__ __forceinline__ int dec_col(int lane, int e) {
+  return D >= 64 ? lane + 64 * e : (lane & (D - 1));
+}
+
+// 8 consecutive elements of a q/k/v tensor as fp32 (one 16-byte load for
+// bf16, two for fp32); the address is 16-byte aligned.
+__device__ __forceinline__ void load8(const uint16_t *p, float (&x)[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = lo_bf16(w[i]);
+    x[2 * i + 1] = hi_bf16(w[i]);
+  }
+}
+__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_partial_kernel(
+    const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
+    float *__restrict__ part, int Hq, int Hkv, int C, int cap, int n_past, int n_splits,
+    float scale) {
+  constexpr int KP = D + 4;                 // padded K row (floats)
+  constexpr int NE = D >= 64 ? D / 64 : 1;  // value columns per lane
+  constexpr int U = D / 8;                  // 8-element units per row
+  __shared__ __attribute__((aligned(16))) float sK[kDecKeys][KP];
+  __shared__ __attribute__((aligned(16))) float sV[kDecKeys][D];
+  __shared__ __attribute__((aligned(16))) float sQ[kDecQB][D];
+  __shared__ __attribute__((aligned(16))) float sP[4][kDecKeys][kDecQPW];
+
+  const int split = blockIdx.x, bh = blockIdx.y, qb = blockIdx.z;
+  const int g = Hq / Hkv, nq = g * C;
+  const int b = bh / Hkv, kvh = bh % Hkv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int k0 = split * kDecKeys;
+  const int k1 = min(k0 + kDecKeys, n_past + C);
+
+  // Stage the split's keys and values and the block's queries (8 elements per
+  // unit, all loads issued before the LDS writes).
+  constexpr int KVU = kDecKeys * U / 256;  // K (and V) units per thread
+  constexpr int QU = (kDecQB * U + 255) / 256;
+  float kx[KVU][8], vx[KVU][8], qx[QU][8];
+#pragma unroll
+  for (int it = 0; it < KVU; ++it) {
+    const int u = tid + 256 * it, r = u / U, c = 8 * (u % U);
+    const int row = min(k0 + r, k1 - 1);  // rows past the end: copies, zeroed below
+    const size_t off = (static_cast<size_t>(bh) * cap + row) * D + c;
+    load8(kc + off, kx[it]);
+    load8(vc + off, vx[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < QU; ++it) {
+    const int u = tid + 256 * it, r = u / U, c = 8 * (u % U);
+    const int qi = min(qb * kDecQB + r, nq - 1);
+    const int hh = qi / C, i = qi % C;
+    if (u < kDecQB * U)
+      load8(q + (static_cast<size_t>(b * Hq + kvh * g + hh) * C + i) * D + c, qx[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < KVU; ++it) {
+    const int u = tid + 256 * it, r = u / U, c = 8 * (u % U);
+    const bool in = k0 + r < k1;
+#pragma unroll
+    for (int j = 0; j < 8; j += 4) {
+      *reinterpret_cast<f32x4 *>(&sK[r][c + j]) =
+          in ? f32x4{kx[it][j], kx[it][j + 1], kx[it][j + 2], kx[it][j + 3]} : f32x4{};
+      *reinterpret_cast<f32x4 *>(&sV[r][c + j]) =
+          in ? f32x4{vx[it][j], vx[it][j + 1], vx[it][j + 2], vx[it][j + 3]} : f32x4{};
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < QU; ++it) {
+    const int u = tid + 256 * it, r = u / U, c = 8 * (u % U);
+    if (u < kDecQB * U) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 4)
+        *reinterpret_cast<f32x4 *>(&sQ[r][c + j]) =
+            f32x4{qx[it][j], qx[it][j + 1], qx[it][j + 2], qx[it][j + 3]};
+    }
+  }
+  __syncthreads();
+
+  // Scores: lane j takes key k0 + j against the wave's queries w, w + 4, ...
+  float s[kDecQPW];
+#pragma unroll
+  for (int r = 0; r < kDecQPW; ++r) s[r] = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < D; c += 4) {
+    const f32x4 kk = *reinterpret_cast<const f32x4 *>(&sK[lane][c]);
+#pragma unroll
+    for (int r = 0; r < kDecQPW; ++r) {
+      const f32x4 qq = *reinterpret_cast<const f32x4 *>(&sQ[w + 4 * r][c]);
+      s[r] += kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3];
+    }
+  }
+  const int key = k0 + lane;
+  float m[kDecQPW], l[kDecQPW];
+  f32x4 pv;
+#pragma unroll
+  for (int r = 0; r < kDecQPW; ++r) {
+    const int qi = qb * kDecQB + w + 4 * r;
+    const int lim = qi < nq ? n_past + qi % C : -1;  // last key the query sees
+    const float sc = key <= lim && key < k1 ? s[r] * scale : -INFINITY;
+    m[r] = wave_max(sc);  // -inf when the query sees no key of this split
+    const float p = m[r] == -INFINITY ? 0.f : __expf(sc - m[r]);
+    l[r] = wave_sum(p);
+    pv[r] = p;
+  }
+  *reinterpret_cast<f32x4 *>(&sP[w][lane][0]) = pv;
+  __syncthreads();
+  float acc[kDecQPW][NE];
+#pragma unroll
+  for (int r = 0; r < kDecQPW; ++r)
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[r][e] = 0.f;
+#pragma unroll 8
+  for (int j = 0; j < kDecKeys; ++j) {
+    const f32x4 pj = *reinterpret_cast<const f32x4 *>(&sP[w][j][0]);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const float vv = sV[j][dec_col<D>(lane, e)];
+#pragma unroll
+      for (int r = 0; r < kDecQPW; ++r) acc[r][e] += pj[r] * vv;
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < kDecQPW; ++r) {
+    const int qi = qb * kDecQB + w + 4 * r;
+    if (qi < nq) {
+      float *pp = part + ((static_cast<size_t>(bh) * n_splits + split) * nq + qi) * (D + 2);
+      if (D >= 64 || lane < 32) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) pp[dec_col<D>(lane, e)] = acc[r][e];
+      }
+      if (lane == 0) {
+        pp[D] = m[r];
+        pp[D + 1] = l[r];
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const T *__restrict__ q, const float *__restrict__ part, const float *__restrict__ beta,
+    const float *__restrict__ M, const float *__restrict__ z, T *__restrict__ out, int Hq,
+    int Hkv, int C, int n_splits, float eps) {
+  constexpr int NE = D >= 64 ? D / 64 : 1;
+  constexpr int RPW = D / 4;  // rows of M per wave
+  __shared__ __attribute__((aligned(16))) float sSq[4][D];      // sigma(q) of the 4 queries
+  __shared__ __attribute__((aligned(16))) float sNum[4][4][D];  // [wave][query][column]
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int g = Hq / Hkv, nq = g * C;
+  const int b = bh / Hkv, kvh = bh % Hkv;
+  const int q0 = blockIdx.x * 4;
+
+  // sigma(q) of the block's queries (empty slots: 0).
+  for (int x = tid; x < 4 * D; x += 256) {
+    const int r = x / D, c = x % D, qi = q0 + r;
+    float v = 0.f;
+    if (qi < nq) {
+      const size_t qrow = (static_cast<size_t>(b * Hq + kvh * g + qi / C) * C + qi % C) * D;
+      v = elu1(load_as_f32(q, qrow + c));
+    }
+    sSq[r][c] = v;
+  }
+  __syncthreads();
+
+  // Retrieval numerators: wave w multiplies rows [w RPW, (w + 1) RPW) of M
+  // (row-major [d_k][d_v]; every load of the wave issued before the FMAs)
+  // with the four queries' sigma(q).
+  const float *Mh = M + static_cast<size_t>(bh) * D * D;
+  float mv[RPW][NE];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      mv[rr][e] = Mh[static_cast<size_t>(w * RPW + rr) * D + dec_col<D>(lane, e)];
+  float num[4][NE];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int e = 0; e < NE; ++e) num[r][e] = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float sq = sSq[r][w * RPW + rr];  // same address in every lane
+#pragma unroll
+      for (int e = 0; e < NE; ++e) num[r][e] += sq * mv[rr][e];
+    }
+  }
+  if (D >= 64 || lane < 32) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < NE; ++e) sNum[w][r][dec_col<D>(lane, e)] = num[r][e];
+  }
+  __syncthreads();
+
+  // Wave w finishes query q0 + w.
+  const int qi = q0 + w;
+  if (qi >= nq) return;  // after the last barrier
+  const int hh = qi / C, i = qi % C;
+  const int h = kvh * g + hh;
+  const size_t qrow = (static_cast<size_t>(b * Hq + h) * C + i) * D;
+
+  // A_dot: merge the splits (every query sees key 0, so the merged max is
+  // finite). Lane s0 + lane reads split s0 + lane's max.
+  const size_t sstride = static_cast<size_t>(nq) * (D + 2);
+  const float *pp = part + static_cast<size_t>(bh) * n_splits * sstride + static_cast<size_t>(qi) * (D + 2);
+  float mt = -INFINITY;
+  for (int s0 = 0; s0 < n_splits; s0 += 64) {
+    const int sl = s0 + lane;
+    mt = fmaxf(mt, sl < n_splits ? pp[sl * sstride + D] : -INFINITY);
+  }
+  mt = wave_max(mt);
+  float lt = 0.f, a[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) a[e] = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < n_splits; ++s) {
+    const float *ps = pp + s * sstride;
+    const float wgt = __expf(ps[D] - mt);  // 0 for a split that saw no key
+    lt += wgt * ps[D + 1];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) a[e] += wgt * ps[dec_col<D>(lane, e)];
+  }
+
+  // A_mem = sigma(q) M / (sigma(q) z + eps).
+  const float *zh = z + static_cast<size_t>(bh) * D;
+  float den = 0.f;
+#pragma unroll
+  for (int t = 0; t < (D + 63) / 64; ++t) {
+    const int kk = lane + 64 * t;
+    den += kk < D ? sSq[w][kk] * zh[kk] : 0.f;
+  }
+  den = wave_sum(den);
+  const float gam = 1.f / (1.f + __expf(-beta[h]));
+  const float inv_den = 1.f / (den + eps), inv_l = 1.f / lt;
+  if (D >= 64 || lane < 32) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int c = dec_col<D>(lane, e);
+      const float nm = sNum[0][w][c] + sNum[1][w][c] + sNum[2][w][c] + sNum[3][w][c];
+      store_from_f32(out, qrow + c, gam * (nm * inv_den) + (1.f - gam) * (a[e] * inv_l));
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_decode_t(const DecodeGeometry &g, const T *q, const T *kc, const T *vc,
+                           const float *beta, const float *M, const float *z, float *part, T *out,
+                           hipStream_t stream) {
+  const int nq = (g.Hq / g.Hkv) * g.C;
+  const int bh = g.B * g.Hkv;
+  const dim3 grid1(decode_splits(g.n_past + g.C), bh, (nq + kDecQB - 1) / kDecQB);
+  decode_partial_kernel<T, D><<<grid1, 256, 0, stream>>>(
+      q, kc, vc, part, g.Hq, g.Hkv, g.C, g.cap, g.n_past, static_cast<int>(grid1.x),
+      1.f / sqrtf(static_cast<float>(D)));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid2((nq + 3) / 4, bh);
+  decode_combine_kernel<T, D><<<grid2, 256, 0, stream>>>(q, part, beta, M, z, out, g.Hq, g.Hkv,
+                                                         g.C, static_cast<int>(grid1.x), g.eps);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_decode_d(const DecodeGeometry &g, const T *q, const T *kc, const T *vc,
+                           const float *beta, const float *M, const float *z, float *part, T *out,
+                           hipStream_t stream) {
+  switch (g.D) {
+    case 32: return launch_decode_t<T, 32>(g, q, kc, vc, beta, M, z, part, out, stream);
+    case 64: return launch_decode_t<T, 64>(g, q, kc, vc, beta, M, z, part, out, stream);
+    case 128: return launch_decode_t<T, 128>(g, q, kc, vc, beta, M, z, part, out, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int decode_splits(int n_keys) { return (n_keys + kDecKeys - 1) / kDecKeys; }
+
+size_t decode_partial_floats(const DecodeGeometry &g) {
+  return static_cast<size_t>(g.B) * g.Hkv * decode_splits(g.n_past + g.C) *
+         (static_cast<size_t>(g.Hq / g.Hkv) * g.C) * (g.D + 2);
+}
+
+hipError_t launch_decode_bf16(const DecodeGeometry &g, const uint16_t *q, const uint16_t *kc,
+                              const uint16_t *vc, const float *beta, const float *M,
+                              const float *z, float *part, uint16_t *out, hipStream_t stream) {
+  return launch_decode_d<uint16_t>(g, q, kc, vc, beta, M, z, part, out, stream);
+}
+
+hipError_t launch_decode_f32(const DecodeGeometry &g, const float *q, const float *kc,
+                             const float *vc, const float *beta, const float *M, const float *z,
+                             float *part, float *out, hipStream_t stream) {
+  return launch_decode_d<float>(g, q, kc, vc, beta, M, z, part, out, stream);
+}
+
+}  // namespace ia

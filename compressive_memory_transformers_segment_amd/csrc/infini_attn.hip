@@ -1,6 +1,8 @@
 // Host side of the C ABI declared in include/infini_attn.h: argument
-// validation, the handle and its workspace, and the launch sequence
-//   segment scan  ->  fused per-segment attention  ->  copy of the final z
+// validation, the handle and its workspace, and the launch sequences
+//   forward:  segment scan  ->  fused per-segment attention  ->  copy of the final z
+//   update:   segment scan over one segment  ->  copy of the final z
+//   decode:   split partials of the local attention  ->  merge, retrieval, gate
 // enqueued on the handle's stream with no host synchronisation.
 
 #include "infini_attn.h"
@@ -22,6 +24,8 @@ struct infini_attn_handle {
   hipStream_t stream;
   void *ws;
   size_t ws_bytes;
+  void *dec_ws;  // split partials of the streaming decode
+  size_t dec_ws_bytes;
   bool timing;
   std::vector<TimedCall> recorded;  // calls timed since the last get
   std::vector<TimedCall> spare;     // event triples ready for reuse
@@ -108,6 +112,63 @@ struct DeviceGuard {
   }
 };
 
+// Grows *buf to at least `need` bytes (contents not kept).
+int ensure_buffer(void **buf, size_t *bytes, size_t need) {
+  if (need <= *bytes) return INFINI_ATTN_OK;
+  if (*buf) {
+    // hipFree waits for work still using the old buffer.
+    if (hipFree(*buf) != hipSuccess) return INFINI_ATTN_ERR_HIP;
+    *buf = nullptr;
+    *bytes = 0;
+  }
+  void *p = nullptr;
+  const hipError_t e = hipMalloc(&p, need);
+  if (e != hipSuccess) return e == hipErrorOutOfMemory ? INFINI_ATTN_ERR_OOM : INFINI_ATTN_ERR_HIP;
+  *buf = p;
+  *bytes = need;
+  return INFINI_ATTN_OK;
+}
+
+// The scan's and the fused kernel's workspace for geometry g, grown as needed.
+int bind_workspace(infini_attn_handle *h, const ia::Geometry &g, ia::Workspace *ws) {
+  const infini_attn_desc &d = h->desc;
+  const WsLayout lay = ws_layout(&d, g.S, g.N);
+  const int st = ensure_buffer(&h->ws, &h->ws_bytes, lay.total);
+  if (st != INFINI_ATTN_OK) return st;
+  char *base = static_cast<char *>(h->ws);
+  ws->z_pre = reinterpret_cast<float *>(base);
+  void *mt = base + lay.z;
+  const bool bf16 = d.dtype == INFINI_ATTN_BF16;
+  ws->mt_pre_f32 = bf16 ? nullptr : static_cast<float *>(mt);
+  ws->mt_pre_bf16 = bf16 ? static_cast<uint16_t *>(mt) : nullptr;
+  ws->dz = bf16 ? reinterpret_cast<float *>(base + lay.z + lay.mt) : nullptr;
+  ws->z_parts = z_parts(g.N);
+  ws->gh = bf16 ? reinterpret_cast<float *>(base + lay.z + lay.mt + lay.dz) : nullptr;
+  ws->vt = bf16 ? reinterpret_cast<uint16_t *>(base + lay.z + lay.mt + lay.dz + lay.gh) : nullptr;
+  ws->vt_tiles = vt_tiles(g.N);
+  return INFINI_ATTN_OK;
+}
+
+hipError_t launch_scan(const infini_attn_handle *h, const ia::Geometry &g, const void *k,
+                       const void *v, float *M, const float *z, int delta,
+                       const ia::Workspace &ws) {
+  return h->desc.dtype == INFINI_ATTN_BF16
+             ? ia::launch_segment_scan_bf16(g, static_cast<const uint16_t *>(k),
+                                            static_cast<const uint16_t *>(v), M, z, delta, ws,
+                                            h->stream)
+             : ia::launch_segment_scan_f32(g, static_cast<const float *>(k),
+                                           static_cast<const float *>(v), M, z, delta, ws,
+                                           h->stream);
+}
+
+// Final z: slot S of every head's snapshot row -> z [B*Hkv][D].
+hipError_t copy_final_z(const infini_attn_handle *h, const ia::Geometry &g, float *z,
+                        const ia::Workspace &ws) {
+  const size_t row = static_cast<size_t>(g.D) * sizeof(float);
+  return hipMemcpy2DAsync(z, row, ws.z_pre + static_cast<size_t>(g.S) * g.D, (g.S + 1) * row, row,
+                          static_cast<size_t>(g.B) * g.Hkv, hipMemcpyDeviceToDevice, h->stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,6 +208,8 @@ int infini_attn_create(infini_attn_t **h, const infini_attn_desc *desc) {
   p->stream = static_cast<hipStream_t>(desc->stream);
   p->ws = nullptr;
   p->ws_bytes = 0;
+  p->dec_ws = nullptr;
+  p->dec_ws_bytes = 0;
   p->timing = false;
   *h = p;
   return INFINI_ATTN_OK;
@@ -178,33 +241,10 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
   g.S = n_segments(d.seq_len, seg_len);
   g.eps = d.eps;
 
-  const WsLayout lay = ws_layout(&d, g.S, g.N);
-  const size_t need = lay.total;
-  if (need > h->ws_bytes) {
-    if (h->ws) {
-      // hipFree waits for work still using the old buffer.
-      if (hipFree(h->ws) != hipSuccess) return INFINI_ATTN_ERR_HIP;
-      h->ws = nullptr;
-      h->ws_bytes = 0;
-    }
-    void *p = nullptr;
-    const hipError_t e = hipMalloc(&p, need);
-    if (e != hipSuccess) return e == hipErrorOutOfMemory ? INFINI_ATTN_ERR_OOM : INFINI_ATTN_ERR_HIP;
-    h->ws = p;
-    h->ws_bytes = need;
-  }
   ia::Workspace ws;
-  char *base = static_cast<char *>(h->ws);
-  ws.z_pre = reinterpret_cast<float *>(base);
-  void *mt = base + lay.z;
+  st = bind_workspace(h, g, &ws);
+  if (st != INFINI_ATTN_OK) return st;
   const bool bf16 = d.dtype == INFINI_ATTN_BF16;
-  ws.mt_pre_f32 = bf16 ? nullptr : static_cast<float *>(mt);
-  ws.mt_pre_bf16 = bf16 ? static_cast<uint16_t *>(mt) : nullptr;
-  ws.dz = bf16 ? reinterpret_cast<float *>(base + lay.z + lay.mt) : nullptr;
-  ws.z_parts = z_parts(g.N);
-  ws.gh = bf16 ? reinterpret_cast<float *>(base + lay.z + lay.mt + lay.dz) : nullptr;
-  ws.vt = bf16 ? reinterpret_cast<uint16_t *>(base + lay.z + lay.mt + lay.dz + lay.gh) : nullptr;
-  ws.vt_tiles = vt_tiles(g.N);
 
   TimedCall tc{};
   if (h->timing) {
@@ -223,13 +263,7 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
     if (hipEventRecord(tc.ev[0], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
   }
   const int delta = update_mode == INFINI_ATTN_DELTA;
-  hipError_t e =
-      bf16 ? ia::launch_segment_scan_bf16(g, static_cast<const uint16_t *>(k),
-                                          static_cast<const uint16_t *>(v), M, z, delta, ws,
-                                          h->stream)
-           : ia::launch_segment_scan_f32(g, static_cast<const float *>(k),
-                                         static_cast<const float *>(v), M, z, delta, ws,
-                                         h->stream);
+  hipError_t e = launch_scan(h, g, k, v, M, z, delta, ws);
   if (e != hipSuccess) return hip_status(e);
   if (h->timing && hipEventRecord(tc.ev[1], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
   if (bf16) {
@@ -243,10 +277,79 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
   }
   if (e != hipSuccess) return hip_status(e);
   if (h->timing && hipEventRecord(tc.ev[2], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
-  // Final z: slot S of every head's snapshot row -> z [B*Hkv][D].
-  const size_t row = static_cast<size_t>(g.D) * sizeof(float);
-  e = hipMemcpy2DAsync(z, row, ws.z_pre + static_cast<size_t>(g.S) * g.D, (g.S + 1) * row, row,
-                       static_cast<size_t>(g.B) * g.Hkv, hipMemcpyDeviceToDevice, h->stream);
+  return hip_status(copy_final_z(h, g, z, ws));
+}
+
+int infini_attn_update(infini_attn_t *h, const void *k, const void *v, float *M, float *z,
+                       int32_t update_mode) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  const infini_attn_desc &d = h->desc;
+  const int32_t rows = d.seq_len;
+  int st = infini_attn_check(&d, rows > 0 ? rows : 1, update_mode);
+  if (st != INFINI_ATTN_OK) return st;
+  if (d.batch == 0 || rows == 0) return INFINI_ATTN_OK;  // nothing to write
+  if (!k || !v || !M || !z) return INFINI_ATTN_ERR_INVALID;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(M, 4) || !aligned(z, 4))
+    return INFINI_ATTN_ERR_INVALID;
+  DeviceGuard guard(d.device);
+  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  ia::Geometry g;
+  g.B = d.batch;
+  g.Hq = d.n_q_heads;
+  g.Hkv = d.n_kv_heads;
+  g.L = rows;
+  g.D = d.d_k;
+  g.N = rows;  // one segment
+  g.S = 1;
+  g.eps = d.eps;
+  ia::Workspace ws;
+  st = bind_workspace(h, g, &ws);
+  if (st != INFINI_ATTN_OK) return st;
+  hipError_t e = launch_scan(h, g, k, v, M, z, update_mode == INFINI_ATTN_DELTA, ws);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(copy_final_z(h, g, z, ws));
+}
+
+int infini_attn_decode(infini_attn_t *h, const void *q, int32_t n_new, const void *k_cache,
+                       const void *v_cache, int32_t n_past, const float *beta, const float *M,
+                       const float *z, void *out) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  const infini_attn_desc &d = h->desc;
+  int st = check_desc(&d);
+  if (st != INFINI_ATTN_OK) return st;
+  if (n_new < 1 || n_past < 0 || static_cast<int64_t>(n_past) + n_new > d.seq_len)
+    return INFINI_ATTN_ERR_INVALID;
+  const int64_t nq = static_cast<int64_t>(d.n_q_heads / d.n_kv_heads) * n_new;
+  if ((nq + 15) / 16 > 65535) return INFINI_ATTN_ERR_UNSUPPORTED;  // grid z of the split kernel
+  if (d.batch == 0) return INFINI_ATTN_OK;
+  if (!q || !k_cache || !v_cache || !beta || !M || !z || !out) return INFINI_ATTN_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return INFINI_ATTN_ERR_INVALID;
+  if (!aligned(beta, 4) || !aligned(M, 4) || !aligned(z, 4)) return INFINI_ATTN_ERR_INVALID;
+  DeviceGuard guard(d.device);
+  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  ia::DecodeGeometry g;
+  g.B = d.batch;
+  g.Hq = d.n_q_heads;
+  g.Hkv = d.n_kv_heads;
+  g.D = d.d_k;
+  g.C = n_new;
+  g.cap = d.seq_len;
+  g.n_past = n_past;
+  g.eps = d.eps;
+  st = ensure_buffer(&h->dec_ws, &h->dec_ws_bytes, ia::decode_partial_floats(g) * sizeof(float));
+  if (st != INFINI_ATTN_OK) return st;
+  float *part = static_cast<float *>(h->dec_ws);
+  const hipError_t e =
+      d.dtype == INFINI_ATTN_BF16
+          ? ia::launch_decode_bf16(g, static_cast<const uint16_t *>(q),
+                                   static_cast<const uint16_t *>(k_cache),
+                                   static_cast<const uint16_t *>(v_cache), beta, M, z, part,
+                                   static_cast<uint16_t *>(out), h->stream)
+          : ia::launch_decode_f32(g, static_cast<const float *>(q),
+                                  static_cast<const float *>(k_cache),
+                                  static_cast<const float *>(v_cache), beta, M, z, part,
+                                  static_cast<float *>(out), h->stream);
   return hip_status(e);
 }
 
@@ -289,9 +392,10 @@ int infini_attn_destroy(infini_attn_t *h) {
       for (TimedCall &tc : *list)
         for (hipEvent_t ev : tc.ev) (void)hipEventDestroy(ev);
   }
-  if (h->ws) {
+  for (void *buf : {h->ws, h->dec_ws}) {
+    if (!buf) continue;
     DeviceGuard guard(h->desc.device);
-    if (guard.err != hipSuccess || hipFree(h->ws) != hipSuccess) st = INFINI_ATTN_ERR_HIP;
+    if (guard.err != hipSuccess || hipFree(buf) != hipSuccess) st = INFINI_ATTN_ERR_HIP;
   }
   delete h;
   return st;

@@ -62,4 +62,28 @@ hipError_t launch_fused_f32(const Geometry &g, const float *q, const float *k, c
                             const float *beta, const Workspace &ws, float *out,
                             hipStream_t stream);
 
+// Geometry of one streaming-decode call: C new query rows per (batch, query
+// head) against rows [0, n_past + C) of a K/V cache of cap rows per kv head.
+struct DecodeGeometry {
+  int B, Hq, Hkv, D;
+  int C;       // new query rows per head
+  int cap;     // cache rows per (batch, kv head): the row stride of the cache
+  int n_past;  // cache rows before the new ones
+  float eps;
+};
+
+// Key splits (workgroups along the keys) for n_keys visible keys, and the
+// fp32 scratch the split partials need.
+int decode_splits(int n_keys);
+size_t decode_partial_floats(const DecodeGeometry &g);
+
+// Streaming decode: split partials of the local attention into `part`, then
+// merge, retrieval from (M, z), gate and store into out [B][Hq][C][D].
+hipError_t launch_decode_bf16(const DecodeGeometry &g, const uint16_t *q, const uint16_t *kc,
+                              const uint16_t *vc, const float *beta, const float *M,
+                              const float *z, float *part, uint16_t *out, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeGeometry &g, const float *q, const float *kc,
+                             const float *vc, const float *beta, const float *M, const float *z,
+                             float *part, float *out, hipStream_t stream);
+
 }  // namespace ia

@@ -125,6 +125,55 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
                         int32_t update_mode, void *out);
 
 /*
+ * Streaming decode: n_new new query rows per (batch, query head), at positions
+ * n_past .. n_past + n_new - 1 of the current segment, against the segment's
+ * rows held in a K/V cache. Per new row (position p): causal attention over
+ * cache rows 0 .. p, retrieval from the state before the segment, gate mix —
+ * the same rows infini_attn_forward produces for these positions
+ * ([HF-repro] "Infini-Attention メカニズム", steps Local Attention, Memory
+ * Retrieval, Integration and State Transfer: only (M, z) and the current
+ * segment's K/V are kept; [LNCB-review] "実装上の流れ").
+ * The handle's desc.seq_len is the cache capacity (rows per kv head).
+ *   q       [B, Hq,  n_new, d_k] dtype, contiguous, 16-byte aligned (device)
+ *   k_cache [B, Hkv, seq_len, d_k] dtype, 16-byte aligned (device); rows
+ *           0 .. n_past + n_new - 1 hold the segment's keys, the new rows'
+ *           own keys included (the caller appends them first)
+ *   v_cache [B, Hkv, seq_len, d_v] dtype, same rows as k_cache
+ *   n_past  >= 0 cached rows before the new ones; n_past + n_new <= seq_len
+ *   beta    [Hq] fp32 (device)
+ *   M, z    [B, Hkv, d_k, d_v], [B, Hkv, d_k] fp32 (device), the state before
+ *           the current segment; read only
+ *   out     [B, Hq, n_new, d_v] dtype (device), written
+ * The library keeps a scratch buffer for the key-split partials in the
+ * handle, grown on demand. The chunk must not cross a segment boundary: at
+ * the boundary, fold the finished segment into (M, z) with
+ * infini_attn_update and start the cache again at row 0.
+ * Errors: ERR_INVALID (null or misaligned pointer, n_new < 1, n_past < 0,
+ * n_past + n_new > seq_len), ERR_UNSUPPORTED (more than 1048560 query rows
+ * per kv head), ERR_OOM (scratch), ERR_HIP (launch failure).
+ */
+int infini_attn_decode(infini_attn_t *h, const void *q, int32_t n_new, const void *k_cache,
+                       const void *v_cache, int32_t n_past, const float *beta, const float *M,
+                       const float *z, void *out);
+
+/*
+ * Memory update of one finished segment: the desc.seq_len rows of k, v are
+ * written into (M, z) in place by the rule update_mode (step Memory Update;
+ * [LNCB-review] "メモリの更新"), exactly as infini_attn_forward writes a
+ * segment. Used with infini_attn_decode at segment boundaries; for a shorter
+ * last segment, use a handle whose seq_len is that segment's length.
+ *   k  [B, Hkv, seq_len, d_k] dtype, contiguous, 16-byte aligned (device)
+ *   v  [B, Hkv, seq_len, d_v] dtype, contiguous, 16-byte aligned (device)
+ *   M, z  fp32 in/out (device): the state before the segment on entry, after
+ *         it on exit
+ * seq_len = 0 or batch = 0 leaves (M, z) unchanged.
+ * Errors: ERR_INVALID (null or misaligned pointer, bad mode), ERR_OOM
+ * (workspace), ERR_HIP (launch failure).
+ */
+int infini_attn_update(infini_attn_t *h, const void *k, const void *v, float *M, float *z,
+                       int32_t update_mode);
+
+/*
  * Per-kernel timing for profiling. With timing enabled, every forward call
  * records HIP events on the handle's stream around its segment-scan kernel
  * and its fused attention kernel. infini_attn_get_timing waits for the
