@@ -31,4 +31,5 @@ from .infini_ref import (  # noqa: F401
     infini_attention,
     memory_chain,
     streaming_decode,
+    infini_block,
 )

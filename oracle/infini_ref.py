@@ -261,3 +261,29 @@ def streaming_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: np.ndarr
                                                      mode, eps)
             n_cached = 0
     return out, M, z
+
+
+def infini_block(x: np.ndarray, wq: np.ndarray, wk: np.ndarray, wv: np.ndarray, wo: np.ndarray,
+                 beta: np.ndarray, M0: np.ndarray, z0: np.ndarray, seg_len: int, mode: str,
+                 n_q_heads: int, n_kv_heads: int,
+                 eps: float = 1e-6) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The layer around the mechanism: query, key and value states are linear
+    projections of the layer input x [B, L, d_model] (head h takes columns
+    h*d .. h*d + d - 1 of x @ W), the Infini-attention forward runs on them,
+    and the heads of each row, side by side, go through the output projection.
+    Returns (y [B, L, d_model], M_S, z_S).
+
+    [HF-repro] "Infini-Attention メカニズム" (the mechanism consumes the
+    layer's own query / key / value states); [LNCB-review] "基本アイデア" (it
+    takes the place of the attention inside each layer's block).
+    """
+    B, L, dm = x.shape
+    d = wq.shape[1] // n_q_heads
+
+    def heads(w, n):
+        return (x @ w).reshape(B, L, n, d).transpose(0, 2, 1, 3)
+
+    q, k, v = heads(wq, n_q_heads), heads(wk, n_kv_heads), heads(wv, n_kv_heads)
+    out, M, z = infini_attention(q, k, v, beta, M0, z0, seg_len, mode, eps)
+    y = out.transpose(0, 2, 1, 3).reshape(B, L, n_q_heads * d) @ wo
+    return y, M, z

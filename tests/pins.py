@@ -302,9 +302,57 @@ def pin_p13_streaming(ora):
         close(z, bz, rtol=1e-13, atol=1e-13, what=f"{tag} z")
 
 
+def pin_p14_block(ora):
+    """The block equals scalar projections (explicit sums over d_model, head h
+    = columns h*d .. h*d + d - 1) around the token-by-token brute force, then
+    the scalar output projection over (head, column) pairs. d_model differs
+    from Hq * d, so a transposed weight or a wrong head split cannot pass."""
+    rng = np.random.default_rng(141)
+    for B, L, dm, Hq, Hkv, d, N, mode in [(2, 5, 4, 2, 1, 3, 3, "delta"),
+                                          (1, 6, 5, 2, 2, 2, 4, "linear")]:
+        x = rng.standard_normal((B, L, dm))
+        wq = rng.standard_normal((dm, Hq * d)) / math.sqrt(dm)
+        wk = rng.standard_normal((dm, Hkv * d)) / math.sqrt(dm)
+        wv = rng.standard_normal((dm, Hkv * d)) / math.sqrt(dm)
+        wo = rng.standard_normal((Hq * d, dm)) / math.sqrt(Hq * d)
+        beta = rng.standard_normal(Hq)
+        M0 = 0.1 * rng.standard_normal((B, Hkv, d, d))
+        z0 = rng.uniform(0.5, 2.0, (B, Hkv, d))
+        y, M, z = ora.infini_block(x, wq, wk, wv, wo, beta, M0, z0, N, mode, Hq, Hkv, 1e-6)
+
+        def proj(w, n):
+            out = np.zeros((B, n, L, d))
+            for b in range(B):
+                for h in range(n):
+                    for l in range(L):
+                        for c in range(d):
+                            acc = 0.0
+                            for i in range(dm):
+                                acc += x[b, l, i] * w[i, h * d + c]
+                            out[b, h, l, c] = acc
+            return out
+
+        q, k, v = proj(wq, Hq), proj(wk, Hkv), proj(wv, Hkv)
+        bo, bM, bz = ind.brute_force(q, k, v, beta, M0, z0, N, mode, 1e-6)
+        by = np.zeros((B, L, dm))
+        for b in range(B):
+            for l in range(L):
+                for j in range(dm):
+                    acc = 0.0
+                    for h in range(Hq):
+                        for c in range(d):
+                            acc += bo[b, h, l, c] * wo[h * d + c, j]
+                    by[b, l, j] = acc
+        tag = f"P-14 {mode} dm={dm} Hq={Hq} d={d}"
+        close(y, by, rtol=1e-10, atol=1e-12, what=f"{tag} y")
+        close(M, bM, rtol=1e-10, atol=1e-12, what=f"{tag} M")
+        close(z, bz, rtol=1e-12, atol=1e-12, what=f"{tag} z")
+
+
 ALL_PINS = [
     pin_sigma_library, pin_gate_library, pin_golden, pin_p1_sdpa, pin_p2_dense_linear,
     pin_p3_linear_closed_form, pin_p4_zero_start, pin_p5_delta_fixed_point, pin_p6_exact,
     pin_p7_brute_force, pin_p8_gqa, pin_p9_split_calls, pin_p10_structure,
     pin_p11_unit_segments, pin_p12_delta_affine, pin_p13_streaming,
+    pin_p14_block,
 ]

@@ -21,7 +21,7 @@ def test_oracle_pin(pin):
 _orig = {n: getattr(ref, n) for n in ("elu_plus_one", "gate_value", "kv_head_of",
                                        "local_causal_attention", "memory_retrieval",
                                        "memory_update", "infini_attention",
-                                       "streaming_decode")}
+                                       "streaming_decode", "infini_block")}
 
 
 def _retrieval_no_eps(qs, M, z, eps):
@@ -136,6 +136,27 @@ def _stream_factory(variant):
     return stream
 
 
+def _block_factory(variant):
+    """infini_block with its layout done wrong."""
+    def block(x, wq, wk, wv, wo, beta, M0, z0, seg_len, mode, n_q_heads, n_kv_heads, eps=1e-6):
+        B, L, dm = x.shape
+        d = wq.shape[1] // n_q_heads
+
+        def heads(w, n):
+            if variant == "column_major_heads":  # head h = columns h, h + n, h + 2n, ...
+                return (x @ w).reshape(B, L, d, n).transpose(0, 3, 1, 2)
+            return (x @ w).reshape(B, L, n, d).transpose(0, 2, 1, 3)
+
+        q, k, v = heads(wq, n_q_heads), heads(wk, n_kv_heads), heads(wv, n_kv_heads)
+        out, M, z = ref.infini_attention(q, k, v, beta, M0, z0, seg_len, mode, eps)
+        if variant == "heads_regrouped_wrong":
+            y = out.transpose(0, 2, 3, 1).reshape(B, L, n_q_heads * d) @ wo
+        else:
+            y = out.transpose(0, 2, 1, 3).reshape(B, L, n_q_heads * d) @ wo
+        return y, M, z
+    return block
+
+
 MUTANTS = {
     "no_eps_retrieval": ("memory_retrieval", _retrieval_no_eps),
     "sigma_on_scaled_q": ("memory_retrieval", _retrieval_scaled_q),
@@ -153,6 +174,8 @@ MUTANTS = {
     "update_before_retrieval": ("infini_attention", _update_before_retrieval),
     "stream_row_misses_itself": ("streaming_decode", _stream_factory("exclusive")),
     "stream_updates_every_chunk": ("streaming_decode", _stream_factory("update_every_chunk")),
+    "block_heads_interleaved": ("infini_block", _block_factory("column_major_heads")),
+    "block_output_regrouped_wrong": ("infini_block", _block_factory("heads_regrouped_wrong")),
 }
 
 
