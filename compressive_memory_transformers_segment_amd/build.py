@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libinfini_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["infini_attn.hip", "segment_scan.hip", "segment_scan_mfma.hip", "fused_bf16.hip",
-           "fused_f32.hip", "decode.hip"]
+           "fused_f32.hip", "decode.hip", "block.hip"]
 ARCH = "gfx950"
 
 # Extra flags per source. The fused attention kernel runs with the IEEE mode
@@ -71,7 +71,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
                 if verbose and out.strip():
                     print(out)
         tmp_lib = os.path.join(tmp, LIB_NAME)
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib])
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib,
+              "-lrocblas"])
         dst_tmp = LIB_PATH + ".tmp"
         shutil.copyfile(tmp_lib, dst_tmp)
         os.replace(dst_tmp, LIB_PATH)

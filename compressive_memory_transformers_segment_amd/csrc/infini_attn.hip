@@ -3,6 +3,8 @@
 //   forward:  segment scan  ->  fused per-segment attention  ->  copy of the final z
 //   update:   segment scan over one segment  ->  copy of the final z
 //   decode:   split partials of the local attention  ->  merge, retrieval, gate
+//   block:    Q/K/V projections (rocBLAS) and regrouping  ->  forward  ->  regroup
+//             ->  output projection
 // enqueued on the handle's stream with no host synchronisation.
 
 #include "infini_attn.h"
@@ -26,6 +28,9 @@ struct infini_attn_handle {
   size_t ws_bytes;
   void *dec_ws;  // split partials of the streaming decode
   size_t dec_ws_bytes;
+  void *blk_ws;  // the block's projections and regrouped attention output
+  size_t blk_ws_bytes;
+  void *blas;    // rocBLAS handle of the block's projections (created on first use)
   bool timing;
   std::vector<TimedCall> recorded;  // calls timed since the last get
   std::vector<TimedCall> spare;     // event triples ready for reuse
@@ -210,6 +215,9 @@ int infini_attn_create(infini_attn_t **h, const infini_attn_desc *desc) {
   p->ws_bytes = 0;
   p->dec_ws = nullptr;
   p->dec_ws_bytes = 0;
+  p->blk_ws = nullptr;
+  p->blk_ws_bytes = 0;
+  p->blas = nullptr;
   p->timing = false;
   *h = p;
   return INFINI_ATTN_OK;
@@ -353,6 +361,61 @@ int infini_attn_decode(infini_attn_t *h, const void *q, int32_t n_new, const voi
   return hip_status(e);
 }
 
+int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, const void *wq,
+                              const void *wk, const void *wv, const void *wo, const float *beta,
+                              float *M, float *z, int32_t seg_len, int32_t update_mode, void *y) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  const infini_attn_desc &d = h->desc;
+  int st = infini_attn_check(&d, seg_len, update_mode);
+  if (st != INFINI_ATTN_OK) return st;
+  if (d_model < 1) return INFINI_ATTN_ERR_INVALID;
+  if (d.batch == 0 || d.seq_len == 0) return INFINI_ATTN_OK;
+  if (!x || !wq || !wk || !wv || !wo || !beta || !M || !z || !y) return INFINI_ATTN_ERR_INVALID;
+  const int64_t rows = static_cast<int64_t>(d.batch) * d.seq_len;
+  if (rows > INT32_MAX) return INFINI_ATTN_ERR_UNSUPPORTED;
+  DeviceGuard guard(d.device);
+  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  if (!h->blas) {
+    st = ia::blas_create(&h->blas, h->stream);
+    if (st != INFINI_ATTN_OK) return st;
+  }
+  const size_t elt = d.dtype == INFINI_ATTN_BF16 ? 2 : 4;
+  const int D = d.d_k, L = d.seq_len;
+  const size_t per_head = static_cast<size_t>(L) * D * elt;
+  const size_t nq = static_cast<size_t>(d.batch) * d.n_q_heads * per_head;
+  const size_t nkv = static_cast<size_t>(d.batch) * d.n_kv_heads * per_head;
+  // Q, K, V head-major; O; O' regrouped by rows (each part 256-byte aligned).
+  const size_t oq = 0, ok = round_up(nq), ov = ok + round_up(nkv), oo = ov + round_up(nkv),
+               oo2 = oo + round_up(nq);
+  st = ensure_buffer(&h->blk_ws, &h->blk_ws_bytes, oo2 + round_up(nq));
+  if (st != INFINI_ATTN_OK) return st;
+  char *base = static_cast<char *>(h->blk_ws);
+  char *q = base + oq, *k = base + ok, *v = base + ov, *o = base + oo, *o2 = base + oo2;
+  // Each projection as one GEMM over all B * L rows into the O' area (large
+  // enough for any of them, Hq >= Hkv), then regrouped head-major.
+  const int row_bytes = D * static_cast<int>(elt);
+  const struct {
+    const void *w;
+    int heads;
+    char *dst;
+  } proj[3] = {{wq, d.n_q_heads, q}, {wk, d.n_kv_heads, k}, {wv, d.n_kv_heads, v}};
+  for (const auto &pj : proj) {
+    st = ia::blas_gemm_rowmajor(h->blas, d.dtype, static_cast<int>(rows), pj.heads * D, d_model,
+                                x, d_model, pj.w, pj.heads * D, o2, 1);
+    if (st != INFINI_ATTN_OK) return st;
+    const hipError_t e = ia::launch_rows_to_heads(o2, pj.dst, d.batch, pj.heads, L, row_bytes,
+                                                  h->stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  st = infini_attn_forward(h, q, k, v, beta, M, z, seg_len, update_mode, o);
+  if (st != INFINI_ATTN_OK) return st;
+  const hipError_t e = ia::launch_heads_to_rows(o, o2, d.batch, d.n_q_heads, L, row_bytes,
+                                                h->stream);
+  if (e != hipSuccess) return hip_status(e);
+  return ia::blas_gemm_rowmajor(h->blas, d.dtype, static_cast<int>(rows), d_model,
+                                d.n_q_heads * D, o2, d.n_q_heads * D, wo, d_model, y, 1);
+}
+
 int infini_attn_set_timing(infini_attn_t *h, int32_t enable) {
   if (!h) return INFINI_ATTN_ERR_INVALID;
   h->timing = enable != 0;
@@ -392,7 +455,11 @@ int infini_attn_destroy(infini_attn_t *h) {
       for (TimedCall &tc : *list)
         for (hipEvent_t ev : tc.ev) (void)hipEventDestroy(ev);
   }
-  for (void *buf : {h->ws, h->dec_ws}) {
+  if (h->blas) {
+    DeviceGuard guard(h->desc.device);
+    ia::blas_destroy(h->blas);
+  }
+  for (void *buf : {h->ws, h->dec_ws, h->blk_ws}) {
     if (!buf) continue;
     DeviceGuard guard(h->desc.device);
     if (guard.err != hipSuccess || hipFree(buf) != hipSuccess) st = INFINI_ATTN_ERR_HIP;

@@ -86,4 +86,16 @@ hipError_t launch_decode_f32(const DecodeGeometry &g, const float *q, const floa
                              const float *vc, const float *beta, const float *M, const float *z,
                              float *part, float *out, hipStream_t stream);
 
+// Infini-attention block: regrouping between [B][H][L][row] and [B][L][H][row]
+// (row_bytes 64, 128, 256 or 512), and the dense projections through rocBLAS
+// (statuses are INFINI_ATTN_* codes).
+hipError_t launch_heads_to_rows(const void *src, void *dst, int B, int H, int L, int row_bytes,
+                                hipStream_t stream);
+hipError_t launch_rows_to_heads(const void *src, void *dst, int B, int H, int L, int row_bytes,
+                                hipStream_t stream);
+int blas_create(void **blas, hipStream_t stream);
+void blas_destroy(void *blas);
+int blas_gemm_rowmajor(void *blas, int dtype, int rows, int n, int k, const void *x, int ldx,
+                       const void *w, int ldw, void *c, int batch);
+
 }  // namespace ia

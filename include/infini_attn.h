@@ -174,6 +174,33 @@ int infini_attn_update(infini_attn_t *h, const void *k, const void *v, float *M,
                        int32_t update_mode);
 
 /*
+ * The Infini-attention block: projections of the layer input, the forward
+ * pass above, and the output projection ([HF-repro] "Infini-Attention
+ * メカニズム": the mechanism takes the layer's own query, key and value
+ * states; [LNCB-review] "基本アイデア": it stands in for the attention of each
+ * layer's block):
+ *   Q = x Wq, K = x Wk, V = x Wv (head h takes columns h d .. h d + d - 1),
+ *   O = infini_attn_forward(Q, K, V, beta, M, z, seg_len, update_mode),
+ *   y = O' Wo, with O' the heads of each row side by side [B, L, Hq d].
+ *   d_model  >= 1 width of the layer input and output
+ *   x   [B, L, d_model]        dtype, contiguous (device)
+ *   wq  [d_model, Hq * d_k]    dtype, row-major (device)
+ *   wk  [d_model, Hkv * d_k]   dtype, row-major (device)
+ *   wv  [d_model, Hkv * d_v]   dtype, row-major (device)
+ *   wo  [Hq * d_v, d_model]    dtype, row-major (device)
+ *   beta, M, z, seg_len, update_mode as for infini_attn_forward (M, z in/out)
+ *   y   [B, L, d_model]        dtype (device), written
+ * The projections run on rocBLAS with fp32 accumulation, and Q, K, V, O are
+ * rounded to dtype. The handle keeps Q, K, V, O and O' in its own scratch,
+ * grown on demand, and a rocBLAS handle on its stream.
+ * Errors: as infini_attn_forward; ERR_INVALID also for d_model < 1;
+ * ERR_UNSUPPORTED for B * L > 2^31 - 1.
+ */
+int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, const void *wq,
+                              const void *wk, const void *wv, const void *wo, const float *beta,
+                              float *M, float *z, int32_t seg_len, int32_t update_mode, void *y);
+
+/*
  * Per-kernel timing for profiling. With timing enabled, every forward call
  * records HIP events on the handle's stream around its segment-scan kernel
  * and its fused attention kernel. infini_attn_get_timing waits for the
