@@ -32,4 +32,5 @@ from .infini_ref import (  # noqa: F401
     memory_chain,
     streaming_decode,
     infini_block,
+    infini_attention_backward,
 )

@@ -287,3 +287,110 @@ def infini_block(x: np.ndarray, wq: np.ndarray, wk: np.ndarray, wv: np.ndarray, 
     out, M, z = infini_attention(q, k, v, beta, M0, z0, seg_len, mode, eps)
     y = out.transpose(0, 2, 1, 3).reshape(B, L, n_q_heads * d) @ wo
     return y, M, z
+
+
+def _elu_plus_one_grad(x: np.ndarray) -> np.ndarray:
+    """d sigma / dx: 1 for x > 0, exp(x) otherwise."""
+    return np.where(x > 0.0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def infini_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: np.ndarray,
+                              M0: np.ndarray, z0: np.ndarray, seg_len: int, mode: str,
+                              d_out: np.ndarray, d_M: Optional[np.ndarray] = None,
+                              d_z: Optional[np.ndarray] = None, eps: float = 1e-6):
+    """Gradients of L = <d_out, out> + <d_M, M_S> + <d_z, z_S> with respect to
+    (q, k, v, beta, M0, z0), for the forward pass of ``infini_attention``.
+
+    Backpropagation through time over the segments (the training setting of
+    [LNCB-review] "実装上の流れ" and of [HF-repro]'s reproduction, where the
+    memory carries gradient from later segments to earlier ones): the segments
+    are visited in reverse, carrying the gradient of the state after each one.
+    Per segment, in reverse order of the forward's steps:
+      gate:       d gamma = sum d_out (A_mem - A_dot), d beta = d gamma g (1 - g);
+      attention:  softmax backward of A_dot = P V with d A_dot = (1 - g) d_out;
+      retrieval:  A_mem = n / den with n = sigma(Q) M_{s-1}, den = sigma(Q) z_{s-1}
+                  + eps: d n = d A_mem / den, d den = -sum(d A_mem n) / den^2;
+      update:     the linear or delta write of (K_s, V_s) into (M, z), whose
+                  gradient flows into K_s, V_s and the earlier state.
+    Returns (dq, dk, dv, dbeta, dM0, dz0).
+    """
+    B, Hq, L, dk_ = q.shape
+    Hkv = k.shape[1]
+    dv_ = v.shape[3]
+    grp = Hq // Hkv
+    gamma = gate_value(beta)
+    gsl = gamma * (1.0 - gamma)  # d gamma / d beta (0 at the infinities)
+    dq = np.zeros_like(q, dtype=np.float64)
+    dk = np.zeros_like(k, dtype=np.float64)
+    dv = np.zeros_like(v, dtype=np.float64)
+    dbeta = np.zeros(Hq, dtype=np.float64)
+    dM0 = np.zeros((B, Hkv, dk_, dv_)) if d_M is None else np.array(d_M, dtype=np.float64)
+    dz0 = np.zeros((B, Hkv, dk_)) if d_z is None else np.array(d_z, dtype=np.float64)
+    bounds = segment_bounds(L, seg_len)
+    scale = 1.0 / math.sqrt(dk_)
+    for b in range(B):
+        for j in range(Hkv):
+            _, _, states = memory_chain(k[b, j], v[b, j], M0[b, j], z0[b, j], seg_len, mode, eps,
+                                        keep_states=True)
+            gM, gz = dM0[b, j], dz0[b, j]  # gradient of the state after the segment
+            for s in reversed(range(len(bounds))):
+                a, e = bounds[s]
+                Mp, zp = states[s]
+                ks, vs = k[b, j, a:e], v[b, j, a:e]
+                n = e - a
+                gMp, gzp = gM.copy(), gz.copy()  # the state passes through the update
+                for h in range(j * grp, (j + 1) * grp):
+                    Q = q[b, h, a:e]
+                    dO = d_out[b, h, a:e]
+                    # forward values of this segment
+                    S = (Q @ ks.T) * scale
+                    S = np.where(np.triu(np.ones((n, n), dtype=bool), k=1), -np.inf, S)
+                    P = np.exp(S - S.max(axis=1, keepdims=True))
+                    P = P / P.sum(axis=1, keepdims=True)
+                    a_dot = P @ vs
+                    sq = elu_plus_one(Q)
+                    num = sq @ Mp
+                    den = sq @ zp + eps
+                    a_mem = num / den[:, None]
+                    # gate
+                    dbeta[h] += np.sum(dO * (a_mem - a_dot)) * gsl[h]
+                    # local attention
+                    dA = (1.0 - gamma[h]) * dO
+                    dv[b, j, a:e] += P.T @ dA
+                    dP = dA @ vs.T
+                    dS = P * (dP - np.sum(dP * P, axis=1, keepdims=True))
+                    dq[b, h, a:e] += (dS @ ks) * scale
+                    dk[b, j, a:e] += (dS.T @ Q) * scale
+                    # retrieval
+                    dAm = gamma[h] * dO
+                    dnum = dAm / den[:, None]
+                    dden = -np.sum(dAm * num, axis=1) / den ** 2
+                    dsq = dnum @ Mp.T + dden[:, None] * zp[None, :]
+                    gMp += sq.T @ dnum
+                    gzp += sq.T @ dden
+                    dq[b, h, a:e] += dsq * _elu_plus_one_grad(Q)
+                # memory update of this segment
+                sk = elu_plus_one(ks)
+                if mode == LINEAR:
+                    write = vs
+                    dsk = write @ gM.T + gz[None, :]
+                    dv[b, j, a:e] += sk @ gM
+                elif mode == DELTA:
+                    numk = sk @ Mp
+                    denk = sk @ zp + eps
+                    write = vs - numk / denk[:, None]
+                    dsk = write @ gM.T + gz[None, :]
+                    dW = sk @ gM
+                    dv[b, j, a:e] += dW
+                    dR = -dW
+                    dnumk = dR / denk[:, None]
+                    ddenk = -np.sum(dR * numk, axis=1) / denk ** 2
+                    dsk += dnumk @ Mp.T + ddenk[:, None] * zp[None, :]
+                    gMp += sk.T @ dnumk
+                    gzp += sk.T @ ddenk
+                else:
+                    raise ValueError(f"unknown update mode {mode!r}")
+                dk[b, j, a:e] += dsk * _elu_plus_one_grad(ks)
+                gM, gz = gMp, gzp
+            dM0[b, j], dz0[b, j] = gM, gz
+    return dq, dk, dv, dbeta, dM0, dz0

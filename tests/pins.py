@@ -349,10 +349,50 @@ def pin_p14_block(ora):
         close(z, bz, rtol=1e-12, atol=1e-12, what=f"{tag} z")
 
 
+def _loss(ora, c, N, mode, d_out, d_M, d_z):
+    out, M, z = ora.infini_attention(c["q"], c["k"], c["v"], c["beta"], c["M0"], c["z0"], N,
+                                     mode, c["eps"])
+    return float(np.sum(d_out * out) + np.sum(d_M * M) + np.sum(d_z * z))
+
+
+def pin_p15_backward_finite_differences(ora):
+    """The backward pass through time equals central finite differences of the
+    forward's scalar loss <d_out, out> + <d_M, M_S> + <d_z, z_S>, for every
+    element of q, k, v, beta, M0 and z0 (several segments, grouped heads,
+    both rules); at beta = +-inf the gate's gradient is exactly 0."""
+    h = 1e-5
+    for shp, N, mode in [(dict(B=1, Hq=2, Hkv=1, L=5, dk=3, dv=3), 2, "delta"),
+                         (dict(B=1, Hq=2, Hkv=1, L=5, dk=3, dv=3), 2, "linear"),
+                         (dict(B=2, Hq=2, Hkv=2, L=4, dk=2, dv=2), 3, "delta")]:
+        c = case64(151 + N + shp["B"], scale=1.2, nonzero_state=True, **shp)
+        rng = np.random.default_rng(152 + N)
+        d_out = rng.standard_normal((shp["B"], shp["Hq"], shp["L"], shp["dv"]))
+        d_M = rng.standard_normal(c["M0"].shape)
+        d_z = rng.standard_normal(c["z0"].shape)
+        grads = ora.infini_attention_backward(c["q"], c["k"], c["v"], c["beta"], c["M0"],
+                                              c["z0"], N, mode, d_out, d_M, d_z, c["eps"])
+        for name, g in zip(("q", "k", "v", "beta", "M0", "z0"), grads):
+            fd = np.zeros_like(c[name])
+            for idx in np.ndindex(*c[name].shape):
+                orig = c[name][idx]
+                c[name][idx] = orig + h
+                up = _loss(ora, c, N, mode, d_out, d_M, d_z)
+                c[name][idx] = orig - h
+                dn = _loss(ora, c, N, mode, d_out, d_M, d_z)
+                c[name][idx] = orig
+                fd[idx] = (up - dn) / (2 * h)
+            close(g, fd, rtol=1e-6, atol=1e-7, what=f"P-15 d{name} {mode} N={N}")
+        # gates at the infinities: no gradient into beta
+        inf_beta = np.array([INF, -INF])
+        g = ora.infini_attention_backward(c["q"], c["k"], c["v"], inf_beta, c["M0"], c["z0"], N,
+                                          mode, d_out, d_M, d_z, c["eps"])
+        assert np.all(g[3] == 0.0), "P-15: gradient into an infinite gate"
+
+
 ALL_PINS = [
     pin_sigma_library, pin_gate_library, pin_golden, pin_p1_sdpa, pin_p2_dense_linear,
     pin_p3_linear_closed_form, pin_p4_zero_start, pin_p5_delta_fixed_point, pin_p6_exact,
     pin_p7_brute_force, pin_p8_gqa, pin_p9_split_calls, pin_p10_structure,
     pin_p11_unit_segments, pin_p12_delta_affine, pin_p13_streaming,
-    pin_p14_block,
+    pin_p14_block, pin_p15_backward_finite_differences,
 ]

@@ -21,7 +21,8 @@ def test_oracle_pin(pin):
 _orig = {n: getattr(ref, n) for n in ("elu_plus_one", "gate_value", "kv_head_of",
                                        "local_causal_attention", "memory_retrieval",
                                        "memory_update", "infini_attention",
-                                       "streaming_decode", "infini_block")}
+                                       "streaming_decode", "infini_block",
+                                       "infini_attention_backward", "_elu_plus_one_grad")}
 
 
 def _retrieval_no_eps(qs, M, z, eps):
@@ -157,6 +158,17 @@ def _block_factory(variant):
     return block
 
 
+def _backward_with(old, new):
+    """The oracle's backward with one line of its source replaced."""
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(_orig["infini_attention_backward"]))
+    assert src.count(old) == 1, old
+    ns = dict(vars(ref))
+    exec(compile(src.replace(old, new), "<planted>", "exec"), ns)
+    return ns["infini_attention_backward"]
+
+
 MUTANTS = {
     "no_eps_retrieval": ("memory_retrieval", _retrieval_no_eps),
     "sigma_on_scaled_q": ("memory_retrieval", _retrieval_scaled_q),
@@ -176,6 +188,13 @@ MUTANTS = {
     "stream_updates_every_chunk": ("streaming_decode", _stream_factory("update_every_chunk")),
     "block_heads_interleaved": ("infini_block", _block_factory("column_major_heads")),
     "block_output_regrouped_wrong": ("infini_block", _block_factory("heads_regrouped_wrong")),
+    "backward_sigma_grad_one": ("_elu_plus_one_grad", lambda x: np.ones_like(x)),
+    "backward_sigma_grad_exp": ("_elu_plus_one_grad", lambda x: np.exp(x)),
+    "backward_delta_sign": ("infini_attention_backward", _backward_with("dR = -dW", "dR = dW")),
+    "backward_retrieval_no_den_term": ("infini_attention_backward", _backward_with(
+        "dden = -np.sum(dAm * num, axis=1) / den ** 2", "dden = 0.0 * den")),
+    "backward_drops_z_carry": ("infini_attention_backward", _backward_with(
+        "gMp, gzp = gM.copy(), gz.copy()", "gMp, gzp = gM.copy(), np.zeros_like(gz)")),
 }
 
 
