@@ -145,7 +145,9 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
  *           the current segment; read only
  *   out     [B, Hq, n_new, d_v] dtype (device), written
  * The library keeps a scratch buffer for the key-split partials in the
- * handle, grown on demand. The chunk must not cross a segment boundary: at
+ * handle, grown on demand: 4 (d_v + 2) B Hq n_new ceil((n_past + n_new) / 64)
+ * bytes, small for a few new rows; a long chunk is better served by
+ * infini_attn_forward. The chunk must not cross a segment boundary: at
  * the boundary, fold the finished segment into (M, z) with
  * infini_attn_update and start the cache again at row 0.
  * Errors: ERR_INVALID (null or misaligned pointer, n_new < 1, n_past < 0,
