@@ -29,9 +29,11 @@
 //     a static schedule of work items (query tile x head unit x segment) that
 //     alternates long and short query tiles, so every workgroup gets about
 //     the same number of key tiles. All data a workgroup needs moves from HBM
-//     to LDS by direct loads (global_load_lds: no register staging, no LDS
-//     store instructions) through a ring of three buffers, as one continuous
-//     stream of slots across items: per item its key tiles (padded to a
+//     to LDS by direct loads (buffer_load ... lds for the key tiles, whose
+//     per-lane offsets are the same for every tile, global_load_lds for the
+//     per-item slots: no register staging, no LDS store instructions)
+//     through a ring of three buffers, as one continuous stream of slots
+//     across items: per item its key tiles (padded to a
 //     multiple of three slots), M^T of the segment, then the next item's Q
 //     rows. The loads run two slots ahead of the work, so the next item's Q,
 //     tiles and snapshot are in flight while the current one finishes and no
@@ -110,6 +112,13 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 }
 
 #define IA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// One 16-byte-per-lane direct load from a buffer resource into LDS (lane l's
+// unit lands at lds + 16 l bytes); voffset per lane, soffset uniform.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint16_t *lds,
+                                                  int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, IA_LDS(lds), 16, voffset, soffset, 0, 0);
+}
 
 template <int D>
 struct Tile {
@@ -250,8 +259,10 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   // D of the slot (uniform per wave); the lane's row within the block and its
   // swizzled column are the same for every i (the rows a load covers advance
   // by a multiple of 32, the swizzle period divides 32), so two per-lane
-  // values serve all loads. A source row is min(row0 + lr, rowmax): rows past
-  // the segment end read its last row, whose results are masked or dropped.
+  // values serve all loads. The Q and M^T slots read source row min(row0 +
+  // lr, rowmax): rows past the segment end read its last row, whose results
+  // are dropped. The key tiles are buffer loads (below): rows past the
+  // segment end read as zero, and those keys are masked.
   const int lr = ((w * 64 + lane) / TL::CPR) % 32;
   const int lcol = 8 * ((lane % TL::CPR) ^ ((((w * 64 + lane) / TL::CPR) / TL::RP) % TL::CPR));
   auto blk = [&](int i) __attribute__((always_inline)) { return (8 * i + w) * 16 / D; };
@@ -273,18 +284,36 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   };
   // Key tile t of an item: K rows swizzled, then V^T copied verbatim.
   auto dma_tile = [&](const FusedItem &it, int t, uint16_t *buf) __attribute__((always_inline)) {
-    const uint16_t *kp = k + static_cast<size_t>(it.head) * L * D;
-    const uint16_t *vsrc =
-        vt + ((static_cast<size_t>(it.head) * S + it.s) * vt_tiles + t) * (D * 64);
+    // Buffer loads: the resource of K covers the segment's rows (rows past
+    // its end read as zero, and those keys are masked), that of V^T the
+    // segment's tiles; the per-lane byte offset is the same for every load
+    // of a kind, the rest is a scalar offset.
+    auto uniform_ptr = [](const uint16_t *p) __attribute__((always_inline)) {
+      const uint64_t a = reinterpret_cast<uint64_t>(p);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+      return reinterpret_cast<uint16_t *>((static_cast<uint64_t>(hi) << 32) | lo);
+    };
+    const uint16_t *kseg = k + (static_cast<size_t>(it.head) * L + it.a) * D;
+    const uint16_t *vseg = vt + (static_cast<size_t>(it.head) * S + it.s) * vt_tiles * (D * 64);
+    const auto krs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(kseg), 0, __builtin_amdgcn_readfirstlane((it.e - it.a) * D * 2), 0x00020000);
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(vseg), 0, __builtin_amdgcn_readfirstlane(vt_tiles * D * 64 * 2), 0x00020000);
+    int kvo = (lr * D + lcol) * 2, vvo = 16 * lane;
+    __asm__ volatile("" : "+v"(kvo), "+v"(vvo));
 #pragma unroll
     for (int i = 0; i < TL::IPW; ++i) {
       const int u0 = (8 * i + w) * 64;  // wave-uniform
       // For D >= 64 the first KU / 512 loads of every wave are K; for D = 32
       // the first load is K in waves 0..3 and V^T in waves 4..7.
       const bool is_k = (TL::KU % kThreads == 0) ? (i < TL::KU / kThreads) : (u0 < TL::KU);
-      ld(is_k ? rowsrc(kp, it.a + t * kBN + 32 * blk(i), it.e - 1)
-              : linsrc(vsrc + 8 * (u0 - TL::KU)),
-         buf, i);
+      if (is_k)
+        buffer_load_lds16(krs, buf + 8 * (8 * i + w) * 64, kvo,
+                          __builtin_amdgcn_readfirstlane((t * kBN + 32 * blk(i)) * D * 2));
+      else
+        buffer_load_lds16(vrs, buf + 8 * (8 * i + w) * 64, vvo,
+                          __builtin_amdgcn_readfirstlane((t * D * 64 + 8 * (u0 - TL::KU)) * 2));
     }
   };
   // M^T of an item's segment, swizzled like K, and the side area (one float
