@@ -250,12 +250,17 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
   // lie in consecutive lanes, so that each load of a wave reads whole rows.
   const int kg = tg / CCH, cc = tg % CCH;
   // The staging buffers hold [column][key], with key unit (4 keys, 8 bytes) u
-  // of column c at position u ^ kswz(c): the transposed writes of a wave then
-  // spread over all banks (the lanes of one write cover 16 columns 8 apart
-  // and four key units), while the operand reads, which take one unit of 32
-  // consecutive columns at a time, keep their pattern.
+  // of column c at position u ^ kswz(c). An 8-byte write is served per half
+  // wave (32 lanes, 64 banks of 4 bytes). Column c = 8 cc + j of a row
+  // (stride 34 words) starts at bank 16 cc + 34 j (mod 64), so the chunks cc
+  // and cc + 4 of one write would meet. The swizzle XORs the unit with a
+  // different multiple of 32 / CCH in each group of 32 columns (d = 128:
+  // 2 ((c >> 5) & 3); d = 64: 4 ((c >> 5) & 1); d = 32: none), which moves
+  // those chunks onto distinct banks: every write is conflict-free. The
+  // operand reads take one unit of 32 consecutive columns, whose swizzle is
+  // one value, so their pattern (conflict-free) is unchanged.
   auto kswz = [](int col) __attribute__((always_inline)) {
-    return ((col >> 5) & (CCH / 4 - 1)) * (64 / CCH);
+    return ((col >> 5) & (CCH / 4 - 1)) * (32 / CCH);
   };
   auto kpos = [&](int col, int unit) __attribute__((always_inline)) {
     return col * kStr + 4 * (unit ^ kswz(col));
