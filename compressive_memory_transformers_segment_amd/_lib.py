@@ -28,7 +28,7 @@ DELTA = 1
 EXPORTS = ("infini_attn_check", "infini_attn_workspace_size", "infini_attn_create",
            "infini_attn_forward", "infini_attn_destroy", "infini_attn_strerror",
            "infini_attn_set_timing", "infini_attn_get_timing", "infini_attn_decode",
-           "infini_attn_update", "infini_attn_block_forward")
+           "infini_attn_update", "infini_attn_block_forward", "infini_attn_backward")
 
 
 class InfiniAttnDesc(ctypes.Structure):
@@ -85,6 +85,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.infini_attn_block_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                                   i32, vp]
         lib.infini_attn_block_forward.restype = ctypes.c_int
+        lib.infini_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
+                                             vp, vp, vp, vp, vp, vp]
+        lib.infini_attn_backward.restype = ctypes.c_int
         lib.infini_attn_destroy.argtypes = [vp]
         lib.infini_attn_destroy.restype = ctypes.c_int
         lib.infini_attn_set_timing.argtypes = [vp, i32]
@@ -141,6 +144,17 @@ def infini_attn_forward(handle: int, q: int, k: int, v: int, beta: int, M: int, 
                                     out)
     if st != OK:
         raise InfiniAttnError(st, "infini_attn_forward")
+
+
+def infini_attn_backward(handle: int, q: int, k: int, v: int, beta: int, M0: int, z0: int,
+                         seg_len: int, update_mode: int, d_out: int, d_M: Optional[int],
+                         d_z: Optional[int], dq: int, dk: int, dv: int, dbeta: int, dM0: int,
+                         dz0: int) -> None:
+    st = load().infini_attn_backward(handle, q, k, v, beta, M0, z0, int(seg_len),
+                                     int(update_mode), d_out, d_M, d_z, dq, dk, dv, dbeta, dM0,
+                                     dz0)
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_backward")
 
 
 def infini_attn_decode(handle: int, q: int, n_new: int, k_cache: int, v_cache: int, n_past: int,
@@ -256,6 +270,47 @@ def forward(q, k, v, beta, M, z, seg_len: int, update_mode="linear", out=None,
     infini_attn_forward(h, q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
                         M.data_ptr(), z.data_ptr(), seg_len, _mode(update_mode), out.data_ptr())
     return out
+
+
+def backward(q, k, v, beta, M0, z0, seg_len: int, d_out, update_mode="linear", d_M=None,
+             d_z=None, eps: float = 1e-6):
+    """Gradients of <d_out, out> + <d_M, M_S> + <d_z, z_S> for the forward pass
+    that starts from (M0, z0) (neither is modified).
+
+    Shapes and dtypes as for ``forward``; d_out has the shape and dtype of out,
+    d_M, d_z those of M0, z0 (or None for zero). Returns fp32
+    (dq, dk, dv, dbeta, dM0, dz0).
+    """
+    import torch
+
+    _check_device_tensors(q=q, k=k, v=v, beta=beta, M=M0, z=z0, d_out=d_out)
+    if k.dtype != q.dtype or v.dtype != q.dtype or d_out.dtype != q.dtype:
+        raise TypeError("q, k, v and d_out must share one dtype")
+    B, Hq, L, D = q.shape
+    Hkv = k.shape[1]
+    if (tuple(k.shape) != (B, Hkv, L, D) or tuple(v.shape) != (B, Hkv, L, D)
+            or tuple(d_out.shape) != (B, Hq, L, D) or tuple(beta.shape) != (Hq,)
+            or tuple(M0.shape) != (B, Hkv, D, D) or tuple(z0.shape) != (B, Hkv, D)):
+        raise ValueError("inconsistent shapes")
+    for name, t, shape in (("d_M", d_M, (B, Hkv, D, D)), ("d_z", d_z, (B, Hkv, D))):
+        if t is not None:
+            _check_device_tensors(**{name: t})
+            if t.dtype != torch.float32 or tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be float32 of shape {shape}")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, Hq, L, D), **f32)
+    dk = torch.empty((B, Hkv, L, D), **f32)
+    dv = torch.empty((B, Hkv, L, D), **f32)
+    dbeta = torch.empty((Hq,), **f32)
+    dM0 = torch.empty((B, Hkv, D, D), **f32)
+    dz0 = torch.empty((B, Hkv, D), **f32)
+    h = handle_for(q, k, eps)
+    infini_attn_backward(h, q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                         M0.data_ptr(), z0.data_ptr(), seg_len, _mode(update_mode),
+                         d_out.data_ptr(), None if d_M is None else d_M.data_ptr(),
+                         None if d_z is None else d_z.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                         dv.data_ptr(), dbeta.data_ptr(), dM0.data_ptr(), dz0.data_ptr())
+    return dq, dk, dv, dbeta, dM0, dz0
 
 
 def _check_device_tensors(**ts):

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libinfini_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["infini_attn.hip", "segment_scan.hip", "segment_scan_mfma.hip", "fused_bf16.hip",
-           "fused_f32.hip", "decode.hip", "block.hip"]
+           "fused_f32.hip", "decode.hip", "block.hip", "backward.hip"]
 ARCH = "gfx950"
 
 # Extra flags per source. The fused attention kernel runs with the IEEE mode

@@ -5,6 +5,8 @@
 //   decode:   split partials of the local attention  ->  merge, retrieval, gate
 //   block:    Q/K/V projections (rocBLAS) and regrouping  ->  forward  ->  regroup
 //             ->  output projection
+//   backward: fp32 segment scan (snapshots)  ->  per-segment gradient kernels,
+//             the reverse state chains and the memory write's gradient
 // enqueued on the handle's stream with no host synchronisation.
 
 #include "infini_attn.h"
@@ -31,6 +33,8 @@ struct infini_attn_handle {
   void *blk_ws;  // the block's projections and regrouped attention output
   size_t blk_ws_bytes;
   void *blas;    // rocBLAS handle of the block's projections (created on first use)
+  void *bwd_ws;  // the backward pass's snapshots and per-segment gradients
+  size_t bwd_ws_bytes;
   bool timing;
   std::vector<TimedCall> recorded;  // calls timed since the last get
   std::vector<TimedCall> spare;     // event triples ready for reuse
@@ -218,6 +222,8 @@ int infini_attn_create(infini_attn_t **h, const infini_attn_desc *desc) {
   p->blk_ws = nullptr;
   p->blk_ws_bytes = 0;
   p->blas = nullptr;
+  p->bwd_ws = nullptr;
+  p->bwd_ws_bytes = 0;
   p->timing = false;
   *h = p;
   return INFINI_ATTN_OK;
@@ -446,6 +452,124 @@ int infini_attn_get_timing(infini_attn_t *h, int32_t *calls, float *scan_ms, flo
   return st;
 }
 
+int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const void *v,
+                         const float *beta, const float *M0, const float *z0, int32_t seg_len,
+                         int32_t update_mode, const void *d_out, const float *d_M,
+                         const float *d_z, float *dq, float *dk, float *dv, float *dbeta,
+                         float *dM0, float *dz0) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  const infini_attn_desc &d = h->desc;
+  int st = infini_attn_check(&d, seg_len, update_mode);
+  if (st != INFINI_ATTN_OK) return st;
+  if (!dbeta || !aligned(dbeta, 4)) return INFINI_ATTN_ERR_INVALID;
+  const size_t D = static_cast<size_t>(d.d_k);
+  const size_t kvheads = static_cast<size_t>(d.batch) * d.n_kv_heads;
+  if (kvheads > 0) {
+    if (!M0 || !z0 || !dM0 || !dz0) return INFINI_ATTN_ERR_INVALID;
+    if (!aligned(M0, 4) || !aligned(z0, 4) || !aligned(dM0, 4) || !aligned(dz0, 4))
+      return INFINI_ATTN_ERR_INVALID;
+    if ((d_M && !aligned(d_M, 4)) || (d_z && !aligned(d_z, 4))) return INFINI_ATTN_ERR_INVALID;
+  }
+  const bool rows = d.batch > 0 && d.seq_len > 0;
+  if (rows) {
+    if (!q || !k || !v || !beta || !d_out || !dq || !dk || !dv) return INFINI_ATTN_ERR_INVALID;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_out, 16) ||
+        !aligned(beta, 4) || !aligned(dq, 4) || !aligned(dk, 4) || !aligned(dv, 4))
+      return INFINI_ATTN_ERR_INVALID;
+  }
+  DeviceGuard guard(d.device);
+  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  hipStream_t stream = h->stream;
+  hipError_t e = hipMemsetAsync(dbeta, 0, sizeof(float) * d.n_q_heads, stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (kvheads == 0) return INFINI_ATTN_OK;
+  const size_t state_bytes = kvheads * D * D * sizeof(float);
+  const size_t z_bytes = kvheads * D * sizeof(float);
+  if (!rows) {  // no rows: the state passes through unchanged
+    e = d_M ? hipMemcpyAsync(dM0, d_M, state_bytes, hipMemcpyDeviceToDevice, stream)
+            : hipMemsetAsync(dM0, 0, state_bytes, stream);
+    if (e == hipSuccess)
+      e = d_z ? hipMemcpyAsync(dz0, d_z, z_bytes, hipMemcpyDeviceToDevice, stream)
+              : hipMemsetAsync(dz0, 0, z_bytes, stream);
+    return hip_status(e);
+  }
+
+  ia::Geometry g;
+  g.B = d.batch;
+  g.Hq = d.n_q_heads;
+  g.Hkv = d.n_kv_heads;
+  g.L = d.seq_len;
+  g.D = d.d_k;
+  g.N = seg_len;
+  g.S = n_segments(d.seq_len, seg_len);
+  g.eps = d.eps;
+  const int delta = update_mode == INFINI_ATTN_DELTA;
+
+  // Scratch layout (each part 256-byte aligned): z_pre, mt, M copy, lse, erow,
+  // dnum, dden, R, r, G (delta only), qz, gma, gza.
+  const size_t units = kvheads * g.S;
+  const size_t qrows = static_cast<size_t>(g.B) * g.Hq * g.L;
+  const size_t sz[13] = {
+      round_up(kvheads * (g.S + 1) * D * sizeof(float)), round_up(units * D * D * sizeof(float)),
+      round_up(state_bytes), round_up(qrows * sizeof(float)), round_up(qrows * sizeof(float)),
+      round_up(qrows * D * sizeof(float)), round_up(qrows * sizeof(float)),
+      round_up(units * D * D * sizeof(float)), round_up(units * D * sizeof(float)),
+      delta ? round_up(units * D * D * sizeof(float)) : 0, round_up(units * D * sizeof(float)),
+      round_up(units * D * D * sizeof(float)), round_up(units * D * sizeof(float))};
+  size_t total = 0;
+  for (size_t x : sz) total += x;
+  st = ensure_buffer(&h->bwd_ws, &h->bwd_ws_bytes, total);
+  if (st != INFINI_ATTN_OK) return st;
+  float *part[13];
+  char *base = static_cast<char *>(h->bwd_ws);
+  for (int i = 0; i < 13; ++i) {
+    part[i] = reinterpret_cast<float *>(base);
+    base += sz[i];
+  }
+  ia::BwdWorkspace w;
+  w.z_pre = part[0];
+  w.mt = part[1];
+  float *Mcopy = part[2];
+  w.lse = part[3];
+  w.erow = part[4];
+  w.dnum = part[5];
+  w.dden = part[6];
+  w.R = part[7];
+  w.r = part[8];
+  w.G = delta ? part[9] : nullptr;
+  w.qz = part[10];
+  w.gma = part[11];
+  w.gza = part[12];
+
+  // The zeroed accumulators (R, r, G, qz) are contiguous apart from the
+  // G gap, which is cleared with them.
+  e = hipMemsetAsync(w.R, 0, sz[7] + sz[8] + sz[9] + sz[10], stream);
+  if (e != hipSuccess) return hip_status(e);
+  // Forward state chain in fp32: the snapshots (M_{s-1}, z_{s-1}) of every segment.
+  e = hipMemcpyAsync(Mcopy, M0, state_bytes, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return hip_status(e);
+  ia::Workspace ws{};
+  ws.z_pre = w.z_pre;
+  ws.mt_pre_f32 = w.mt;
+  if (d.dtype == INFINI_ATTN_BF16) {
+    const uint16_t *qb = static_cast<const uint16_t *>(q), *kb = static_cast<const uint16_t *>(k),
+                   *vb = static_cast<const uint16_t *>(v),
+                   *ob = static_cast<const uint16_t *>(d_out);
+    e = ia::launch_segment_scan_f32(g, kb, vb, Mcopy, z0, delta, ws, stream);
+    if (e == hipSuccess)
+      e = ia::launch_backward<uint16_t>(g, qb, kb, vb, ob, beta, d_M, d_z, delta, w, dq, dk, dv,
+                                        dbeta, dM0, dz0, stream);
+  } else {
+    const float *qf = static_cast<const float *>(q), *kf = static_cast<const float *>(k),
+                *vf = static_cast<const float *>(v), *of = static_cast<const float *>(d_out);
+    e = ia::launch_segment_scan_f32(g, kf, vf, Mcopy, z0, delta, ws, stream);
+    if (e == hipSuccess)
+      e = ia::launch_backward<float>(g, qf, kf, vf, of, beta, d_M, d_z, delta, w, dq, dk, dv,
+                                     dbeta, dM0, dz0, stream);
+  }
+  return hip_status(e);
+}
+
 int infini_attn_destroy(infini_attn_t *h) {
   if (!h) return INFINI_ATTN_OK;
   int st = INFINI_ATTN_OK;
@@ -459,7 +583,7 @@ int infini_attn_destroy(infini_attn_t *h) {
     DeviceGuard guard(h->desc.device);
     ia::blas_destroy(h->blas);
   }
-  for (void *buf : {h->ws, h->dec_ws, h->blk_ws}) {
+  for (void *buf : {h->ws, h->dec_ws, h->blk_ws, h->bwd_ws}) {
     if (!buf) continue;
     DeviceGuard guard(h->desc.device);
     if (guard.err != hipSuccess || hipFree(buf) != hipSuccess) st = INFINI_ATTN_ERR_HIP;

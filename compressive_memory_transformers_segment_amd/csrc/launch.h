@@ -45,6 +45,12 @@ hipError_t launch_segment_scan_f32(const Geometry &g, const float *k, const floa
                                    const float *z, int delta, const Workspace &ws,
                                    hipStream_t stream);
 
+// The same fp32 scan over bf16 k, v: fp32 snapshots (ws.mt_pre_f32, z_pre)
+// for the backward pass, whatever the storage type.
+hipError_t launch_segment_scan_f32(const Geometry &g, const uint16_t *k, const uint16_t *v,
+                                   float *M, const float *z, int delta, const Workspace &ws,
+                                   hipStream_t stream);
+
 // Segment scan, bf16 storage: per-segment statistics on MFMA in parallel, then
 // the fp32 recurrence; writes z_pre (slot S = final z), mt_pre_bf16 and M.
 hipError_t launch_segment_scan_bf16(const Geometry &g, const uint16_t *k, const uint16_t *v,
@@ -61,6 +67,32 @@ hipError_t launch_fused_bf16(const Geometry &g, const uint16_t *q, const uint16_
 hipError_t launch_fused_f32(const Geometry &g, const float *q, const float *k, const float *v,
                             const float *beta, const Workspace &ws, float *out,
                             hipStream_t stream);
+
+// Scratch of the backward pass (fp32 throughout). Units are (b, kv head,
+// segment) in that order; rows are [B][Hq][L] for the per-query-row arrays.
+struct BwdWorkspace {
+  float *z_pre;  // [B*Hkv][S+1][D] z before every segment (scan output)
+  float *mt;     // [B*Hkv][S][D(v)][D(k)] M^T before every segment (scan output)
+  float *lse;    // [B*Hq*L] log-sum-exp of each query row's causal softmax
+  float *erow;   // [B*Hq*L] dO_i . A_dot_i
+  float *dnum;   // [B*Hq*L][D] gradient of the retrieval numerator
+  float *dden;   // [B*Hq*L] gradient of the retrieval denominator
+  float *R;      // [units][D][D] sum of sigma(q)^T dnum over the group (zeroed)
+  float *r;      // [units][D] sum of sigma(q)^T dden over the group (zeroed)
+  float *G;      // [units][D][D] delta rule's sigma(k)^T diag(1/denk) sigma(k) (zeroed)
+  float *qz;     // [units][D] delta rule's sigma(k)^T ddenk (zeroed)
+  float *gma;    // [units][D][D] gradient of M after each segment
+  float *gza;    // [units][D] gradient of z after each segment
+};
+
+// Backward pass: dq, dk, dv (fp32, the shapes of q, k, v), dbeta (zeroed by
+// the caller), dM0, dz0. The workspace's z_pre and mt must hold the forward's
+// fp32 snapshots; dM, dz may be null (zero).
+template <typename T>
+hipError_t launch_backward(const Geometry &g, const T *q, const T *k, const T *v, const T *dout,
+                           const float *beta, const float *dM, const float *dz, int delta,
+                           const BwdWorkspace &w, float *dq, float *dk, float *dv, float *dbeta,
+                           float *dM0, float *dz0, hipStream_t stream);
 
 // Geometry of one streaming-decode call: C new query rows per (batch, query
 // head) against rows [0, n_past + C) of a K/V cache of cap rows per kv head.

@@ -203,6 +203,42 @@ int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, 
                               float *M, float *z, int32_t seg_len, int32_t update_mode, void *y);
 
 /*
+ * Backward pass of infini_attn_forward: the gradients of
+ *   loss = <d_out, out> + <d_M, M_S> + <d_z, z_S>
+ * with respect to q, k, v, beta and the initial state (M_0, z_0), taken by
+ * backpropagation through time over the segments, the way the memory is
+ * trained end to end ([LNCB-review] "実装上の流れ": the segments are processed
+ * in order with the memory carried between them; [HF-repro] "Infini-Attention
+ * メカニズム", step State Transfer: the state is the only link between
+ * segments, so it is the only path by which later segments' gradients reach
+ * earlier ones). The forward quantities (softmax statistics, the state
+ * before each segment) are recomputed in fp32; nothing from a forward call
+ * is needed.
+ *   q, k, v, beta, seg_len, update_mode  as for infini_attn_forward (device)
+ *   M0  [B, Hkv, d_k, d_v] fp32, z0 [B, Hkv, d_k] fp32: the state the forward
+ *       started from (read only)
+ *   d_out [B, Hq, L, d_v] dtype (device): gradient of the loss w.r.t. out
+ *   d_M [B, Hkv, d_k, d_v], d_z [B, Hkv, d_k] fp32 (device), or NULL for zero:
+ *       gradient w.r.t. the final state
+ *   dq [B, Hq, L, d_k], dk [B, Hkv, L, d_k], dv [B, Hkv, L, d_v] fp32 (device),
+ *       written; dk and dv sum over the query heads of each kv group
+ *   dbeta [Hq] fp32 (device), written
+ *   dM0 [B, Hkv, d_k, d_v], dz0 [B, Hkv, d_k] fp32 (device), written
+ * Every arithmetic step is fp32. Output buffers must not alias inputs. The
+ * handle keeps fp32 scratch of about (B Hq L (d + 3) + 4 B Hkv S d^2) floats,
+ * grown on demand. dbeta sums atomically, so its last bits may vary from run
+ * to run. B = 0 writes dbeta = 0; L = 0 also passes (d_M, d_z) through to
+ * (dM0, dz0).
+ * Errors: as infini_attn_forward; ERR_INVALID also for a null d_out, dq, dk,
+ * dv, dbeta, M0, z0, dM0 or dz0 where the shapes are non-empty.
+ */
+int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const void *v,
+                         const float *beta, const float *M0, const float *z0, int32_t seg_len,
+                         int32_t update_mode, const void *d_out, const float *d_M,
+                         const float *d_z, float *dq, float *dk, float *dv, float *dbeta,
+                         float *dM0, float *dz0);
+
+/*
  * Per-kernel timing for profiling. With timing enabled, every forward call
  * records HIP events on the handle's stream around its segment-scan kernel
  * and its fused attention kernel. infini_attn_get_timing waits for the

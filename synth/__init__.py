@@ -42,6 +42,7 @@ __all__ = [
     "as_f64",
     "generate",
     "random_case",
+    "random_cotangents",
 ]
 
 
@@ -221,3 +222,17 @@ def random_case(seed: int, B: int, Hq: int, Hkv: int, L: int, dk: int, dv: int,
         z0 = np.zeros((B, Hkv, dk), dtype=np.float32)
     return dict(q=q, k=k, v=v, beta=b, M0=M0, z0=z0, eps=np.float32(1e-6))
 
+
+
+def random_cotangents(seed: int, B: int, Hq: int, Hkv: int, L: int, d: int, dtype: str = "f32",
+                      state: bool = True) -> Dict[str, Optional[np.ndarray]]:
+    """Seeded gradients of a loss with respect to the forward's outputs: d_out
+    [B, Hq, L, d] in the storage dtype, and (when ``state``) d_M [B, Hkv, d, d],
+    d_z [B, Hkv, d] in fp32; N(0, 1) draws in that order."""
+    rng = np.random.default_rng(seed)
+    d_out = _store(rng.standard_normal((B, Hq, L, d)), dtype)
+    if not state:
+        return dict(d_out=d_out, d_M=None, d_z=None)
+    d_M = round_fp32(rng.standard_normal((B, Hkv, d, d)))
+    d_z = round_fp32(rng.standard_normal((B, Hkv, d)))
+    return dict(d_out=d_out, d_M=d_M, d_z=d_z)

@@ -128,6 +128,8 @@ def test_destroy_null_and_forward_null_handle():
     lib = ia.load()
     assert lib.infini_attn_forward(None, None, None, None, None, None, None, 64, 0,
                                    None) == _lib.ERR_INVALID
+    assert lib.infini_attn_backward(None, None, None, None, None, None, None, 64, 0, None, None,
+                                    None, None, None, None, None, None, None) == _lib.ERR_INVALID
 
 
 def test_strerror():
