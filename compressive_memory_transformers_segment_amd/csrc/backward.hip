@@ -11,11 +11,11 @@
 //
 // The work splits into parts that are independent per segment and two short
 // chains that run backwards over the segments:
-//   query  per (b, q head, segment, 64 query rows): the local attention's dQ
+//   query  per (b, q head, segment, 128 query rows): the local attention's dQ
 //          (softmax backward with the row statistics recomputed), the
 //          retrieval backward (dnum = g dO / den, dden = -g sum(dO num) / den^2,
 //          dq += (dnum Mp^T + dden zp) sigma'(q)) and the gate's d beta;
-//   key    per (b, kv head, segment, 32 keys): the local attention's dK, dV
+//   key    per (b, kv head, segment, 128 keys): the local attention's dK, dV
 //          over every query row and query head of the group that sees the keys;
 //   outer  per (b, kv head, segment): R_s = sum sq^T dnum and r_s = sum sq^T dden
 //          over the group's query heads, and for the delta rule
@@ -39,7 +39,6 @@ namespace ia {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kQT = 64;  // query rows per tile
 constexpr int kKT = 32;  // keys (or state rows) per LDS chunk
 
 // acc[i][j] += sum_{kk < kn} A(r0 + 16 i, kk) * B(kk, c0 + 16 j), with
@@ -75,12 +74,6 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-__device__ __forceinline__ float max16(float x) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 16));
-  return x;
-}
-
 __device__ __forceinline__ float gate(float beta) { return 1.f / (1.f + expf(-beta)); }
 
 // sigma'(x) from sigma(x): 1 where x > 0 (sigma > 1), sigma itself elsewhere.
@@ -102,8 +95,38 @@ __device__ __forceinline__ void load_rows(float (*dst)[P], const T *src, int kn,
 }
 
 // ---------------------------------------------------------------------------
+// The two local-attention kernels run their products on the fp32 matrix
+// cores (v_mfma_f32_32x32x2_f32: one 32x32 block, two contraction steps per
+// instruction, full fp32). In a 32x32 result block, lane l owns column l % 32
+// and the rows kappa(r, g) = 8 (r / 4) + 4 g + r % 4 of its 16 registers r,
+// g = l / 32. A product whose contraction index is the row index of a result
+// block takes that block straight from registers as its B operand: step s
+// (of 16) of lane group g contracts over index kappa(s, g), and the A operand
+// reads the same index. The hardware sums over (step, lane group) pairs, so
+// any bijection between them and the contraction index gives the same sum as
+// long as both operands use it.
+
+__device__ __forceinline__ int kappa(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
 // query: dq, the softmax row statistics (lse, E) and dnum / dden for the
-// outer products, and the gate's contribution to d beta.
+// outer products, and the gate's contribution to d beta. 128 query rows per
+// workgroup, 32 per wave; key tiles of 32.
+//   S^T = K Q^T and (dO V^T)^T = V dO^T put one query per lane, so the row
+//   statistics of the softmax are per lane (plus the lane 32 away);
+//   dq^T = K^T dS^T takes dS^T from registers;
+//   retrieval: num^T = Mp^T sigma(Q)^T and dsq^T = Mp dnum^T, one 32-row
+//   chunk of Mp^T in LDS at a time.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_query_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -112,208 +135,203 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(
     float *__restrict__ dq, float *__restrict__ lse_out, float *__restrict__ e_out,
     float *__restrict__ dnum_out, float *__restrict__ dden_out, float *__restrict__ dbeta) {
   constexpr int P = D + 1;
-  constexpr int NJ = D / 16;
-  __shared__ float sQ[kQT][P];   // q rows; sigma(q) for the retrieval part
-  __shared__ float sO[kQT][P];   // d_out rows; dnum for the retrieval part
-  __shared__ float sK[kKT][P];   // key tile, then chunks of the state
-  __shared__ float sV[kKT][P];   // value tile
-  __shared__ float sP[kQT][kKT + 1];
+  constexpr int NB = D / 32;  // 32-wide blocks along d
+  constexpr int QT = 128;
+  __shared__ float sK[kKT][P];  // key tile, then 32-row chunks of Mp^T
+  __shared__ float sV[kKT][P];
   __shared__ float sZ[D];
-  __shared__ float sDen[kQT];
   __shared__ float sAcc;
 
-  const int t = threadIdx.x, r0 = t >> 4, c0 = t & 15;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
   const int s = blockIdx.y, bh = blockIdx.z;
   const int b = bh / Hq, h = bh % Hq;
   const int grp = Hq / Hkv;
   const size_t kvh = static_cast<size_t>(b) * Hkv + h / grp;
   const int a = s * N, e = min(a + N, L);
-  const int i0 = a + blockIdx.x * kQT;
+  const int i0 = a + blockIdx.x * QT;
   if (i0 >= e) return;
-  const int rows = min(kQT, e - i0);
-  const int kend = min(i0 + kQT, e);  // keys this tile's rows can see: [a, kend)
+  const int kend = min(i0 + QT, e);  // keys this tile's rows can see: [a, kend)
+  const int wq0 = i0 + 32 * w;       // this wave's first query row
+  const bool wave_live = wq0 < e;
+  const int qi = wq0 + l32;          // this lane's query row
+  const bool qvalid = qi < e;
   const float gam = gate(beta[h]);
   const float scale = 1.f / sqrtf(static_cast<float>(D));
-
-  const size_t qrow0 = static_cast<size_t>(bh) * L + i0;
-  load_rows<T, D, P>(sQ, q + qrow0 * D, kQT, rows, false);
-  load_rows<T, D, P>(sO, dout + qrow0 * D, kQT, rows, false);
-  if (t == 0) sAcc = 0.f;
+  const size_t qbase = static_cast<size_t>(bh) * L;
   const T *kb = k + kvh * L * D;
   const T *vb = v + kvh * L * D;
+  if (t == 0) sAcc = 0.f;
+  for (int c = t; c < D; c += kThreads) sZ[c] = zpre[(kvh * (S + 1) + s) * D + c];
 
-  auto qk = [&](float (&sc)[4][2]) {
-    zero(sc);
-    mm16<4, 2>(sc, D, [&](int r, int kk) { return sQ[r][kk]; },
-               [&](int kk, int c) { return sK[c][kk]; });
-  };
-  auto ov = [&](float (&o)[4][2]) {
-    zero(o);
-    mm16<4, 2>(o, D, [&](int r, int kk) { return sO[r][kk]; },
-               [&](int kk, int c) { return sV[c][kk]; });
-  };
-  auto visible = [&](int i, int jj, int j0) {
-    const int row = i0 + r0 + 16 * i, col = j0 + c0 + 16 * jj;
-    return col <= row && col < e;
-  };
-
-  // Pass 1: row max and sum of the causal softmax -> lse.
-  float m[4], l[4];
+  // This lane's query row and d_out row as B operands: element 2 u + g.
+  float qr[D / 2], orow[D / 2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
+  for (int u = 0; u < D / 2; ++u) {
+    const size_t o = (qbase + qi) * D + 2 * u + g;
+    qr[u] = qvalid ? load_as_f32(q, o) : 0.f;
+    orow[u] = qvalid ? load_as_f32(dout, o) : 0.f;
   }
-  for (int j0 = a; j0 < kend; j0 += kKT) {
+
+  auto load_kv = [&](int j0) {
     __syncthreads();
     load_rows<T, D, P>(sK, kb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
+    load_rows<T, D, P>(sV, vb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
     __syncthreads();
-    float sc[4][2];
-    qk(sc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x0 = visible(i, 0, j0) ? sc[i][0] * scale : -INFINITY;
-      float x1 = visible(i, 1, j0) ? sc[i][1] * scale : -INFINITY;
-      const float mn = fmaxf(m[i], max16(fmaxf(x0, x1)));
-      const float add = sum16(__expf(x0 - mn) + __expf(x1 - mn));
-      l[i] = l[i] * __expf(m[i] - mn) + add;
-      m[i] = mn;
+  };
+  auto scores = [&](f32x16 &st, f32x16 &ot) {
+    st = zero16();
+    ot = zero16();
+#pragma unroll 8
+    for (int u = 0; u < D / 2; ++u) {
+      st = mfma32(sK[l32][2 * u + g], qr[u], st);
+      ot = mfma32(sV[l32][2 * u + g], orow[u], ot);
     }
-  }
-  float lse[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lse[i] = m[i] + __logf(l[i]);
+  };
+  // Key tile j0 is visible to some row of this wave.
+  auto wave_sees = [&](int j0) { return wave_live && j0 <= wq0 + 31; };
 
-  // Pass 2: E_i = sum_j P_ij (dO_i . v_j), i.e. dO_i . A_dot_i.
-  float ep[4] = {0.f, 0.f, 0.f, 0.f};
+  // Pass 1: online max, sum and E = sum_j P_ij (dO_i . v_j) of each row.
+  float m = -INFINITY, l = 0.f, ea = 0.f;
   for (int j0 = a; j0 < kend; j0 += kKT) {
-    __syncthreads();
-    load_rows<T, D, P>(sK, kb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
-    load_rows<T, D, P>(sV, vb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
-    __syncthreads();
-    float sc[4][2], o[4][2];
-    qk(sc);
-    ov(o);
+    load_kv(j0);
+    if (!wave_sees(j0)) continue;
+    f32x16 st, ot;
+    scores(st, ot);
+    float x[16];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) {
+      const int key = j0 + kappa(r, g);
+      x[r] = (key <= qi && key < e) ? st[r] * scale : -INFINITY;
+      mx = fmaxf(mx, x[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    float ps = 0.f, pe = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        if (visible(i, jj, j0)) ep[i] += __expf(sc[i][jj] * scale - lse[i]) * o[i][jj];
+    for (int r = 0; r < 16; ++r) {
+      const float p = __expf(x[r] - mn);
+      ps += p;
+      pe += p * ot[r];
+    }
+    ps += __shfl_xor(ps, 32);
+    pe += __shfl_xor(pe, 32);
+    const float f = __expf(m - mn);
+    l = l * f + ps;
+    ea = ea * f + pe;
+    m = mn;
   }
-  float E[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) E[i] = sum16(ep[i]);
+  const float lse = m + __logf(l);
+  const float E = ea / l;
 
-  // Pass 3: dS = (1 - g) P (dO V^T - E), dq_attn = scale dS K.
-  float acc[4][NJ];
-  zero(acc);
+  // Pass 2: dS^T = (1 - g) P^T (dO V^T - E)^T, dq^T += K^T dS^T.
+  f32x16 dqa[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) dqa[cb] = zero16();
   for (int j0 = a; j0 < kend; j0 += kKT) {
-    __syncthreads();
-    load_rows<T, D, P>(sK, kb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
-    load_rows<T, D, P>(sV, vb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
-    __syncthreads();
-    float sc[4][2], o[4][2];
-    qk(sc);
-    ov(o);
+    load_kv(j0);
+    if (!wave_sees(j0)) continue;
+    f32x16 st, ot;
+    scores(st, ot);
+    float ds[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 16; ++r) {
+      const int key = j0 + kappa(r, g);
+      const float p = (key <= qi && key < e) ? __expf(st[r] * scale - lse) : 0.f;
+      ds[r] = (1.f - gam) * p * (ot[r] - E);
+    }
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const float p = visible(i, jj, j0) ? __expf(sc[i][jj] * scale - lse[i]) : 0.f;
-        sP[r0 + 16 * i][c0 + 16 * jj] = (1.f - gam) * p * (o[i][jj] - E[i]);
-      }
-    __syncthreads();
-    mm16<4, NJ>(acc, kKT, [&](int r, int kk) { return sP[r][kk]; },
-                [&](int kk, int c) { return sK[kk][c]; });
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqa[cb] = mfma32(sK[kappa(r, g)][32 * cb + l32], ds[r], dqa[cb]);
   }
 
   // Retrieval backward from the pre-segment snapshot (Mp^T in mt, zp in zpre).
-  const size_t unit = kvh * S + s;
-  const float *mtp = mt + unit * D * D;
-  __syncthreads();
-  for (int idx = t; idx < kQT * D; idx += kThreads) {
-    const int r = idx / D, c = idx % D;
-    sQ[r][c] = r < rows ? elu1(sQ[r][c]) : 0.f;
-  }
-  for (int c = t; c < D; c += kThreads) sZ[c] = zpre[(kvh * (S + 1) + s) * D + c];
-  float num[4][NJ];
-  zero(num);
-  for (int k0 = 0; k0 < D; k0 += kKT) {
+#pragma unroll
+  for (int u = 0; u < D / 2; ++u) qr[u] = elu1(qr[u]);  // sigma(q), element 2 u + g
+  float den = 0.f;
+#pragma unroll
+  for (int u = 0; u < D / 2; ++u) den += qr[u] * sZ[2 * u + g];
+  den += __shfl_xor(den, 32) + eps;
+  const float *mtp = mt + (kvh * S + s) * D * D;
+  f32x16 dsq[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) dsq[cb] = zero16();
+  float s1 = 0.f;  // dO_i . num_i, this lane's part
+  for (int jb = 0; jb < NB; ++jb) {
     __syncthreads();
     for (int idx = t; idx < kKT * D; idx += kThreads) {
-      const int kk = idx % kKT, j = idx / kKT;  // sK[kk][j] = Mp[k0 + kk][j] = mt[j][k0 + kk]
-      sK[kk][j] = mtp[static_cast<size_t>(j) * D + k0 + kk];
+      const int jj = idx / D, c = idx % D;  // sK[jj][c] = Mp^T[32 jb + jj][c]
+      sK[jj][c] = mtp[static_cast<size_t>(32 * jb + jj) * D + c];
     }
     __syncthreads();
-    mm16<4, NJ>(num, kKT, [&](int r, int kk) { return sQ[r][k0 + kk]; },
-                [&](int kk, int c) { return sK[kk][c]; });
-  }
-  if (t < kQT) {
-    float d = eps;
-    for (int c = 0; c < D; ++c) d += sQ[t][c] * sZ[c];
-    sDen[t] = d;
-  }
-  __syncthreads();
-  float dden[4];
-  float mem_dot = 0.f;  // sum over this thread's rows of dO . A_mem (lanes c0 == 0)
+    if (!wave_live) continue;
+    f32x16 num = zero16();  // num^T rows 32 jb + kappa, column = this lane's query
+#pragma unroll 8
+    for (int u = 0; u < D / 2; ++u) num = mfma32(sK[l32][2 * u + g], qr[u], num);
+    float dn[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + 16 * i;
-    const float den = sDen[r];
-    float part = 0.f;
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int j = 32 * jb + 8 * r4 + 4 * g;
+      float o4[4];
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) part += sO[r][c0 + 16 * jj] * num[i][jj];
-    const float s1 = sum16(part);  // dO_i . num_i
-    dden[i] = -gam * s1 / (den * den);
-    if (c0 == 0 && r < rows) mem_dot += s1 / den;
+      for (int i = 0; i < 4; ++i)
+        o4[i] = qvalid ? load_as_f32(dout, (qbase + qi) * D + j + i) : 0.f;
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int c = c0 + 16 * jj;
-      const float dn = gam * sO[r][c] / den;
-      sO[r][c] = dn;  // each element is read and written by its owner only
-      if (r < rows) dnum_out[(qrow0 + r) * D + c] = dn;
+      for (int i = 0; i < 4; ++i) {
+        s1 += o4[i] * num[4 * r4 + i];
+        dn[4 * r4 + i] = gam * o4[i] / den;
+      }
+      if (qvalid) {
+        float *dst = dnum_out + (qbase + qi) * D + j;
+        *reinterpret_cast<float4 *>(dst) = make_float4(dn[4 * r4], dn[4 * r4 + 1],
+                                                       dn[4 * r4 + 2], dn[4 * r4 + 3]);
+      }
     }
-    if (c0 == 0 && r < rows) {
-      dden_out[qrow0 + r] = dden[i];
-      lse_out[qrow0 + r] = lse[i];
-      e_out[qrow0 + r] = E[i];
-    }
-  }
-  float dsq[4][NJ];
-  zero(dsq);
-  for (int j0 = 0; j0 < D; j0 += kKT) {
-    __syncthreads();
-    for (int idx = t; idx < kKT * D; idx += kThreads) {
-      const int jj = idx / D, c = idx % D;  // sK[jj][c] = Mp[c][j0 + jj] = mt[j0 + jj][c]
-      sK[jj][c] = mtp[static_cast<size_t>(j0 + jj) * D + c];
-    }
-    __syncthreads();
-    mm16<4, NJ>(dsq, kKT, [&](int r, int kk) { return sO[r][j0 + kk]; },
-                [&](int kk, int c) { return sK[kk][c]; });
-  }
-  float att_dot = 0.f;  // sum over this thread's rows of dO . A_dot = E (lanes c0 == 0)
+    // dsq^T[c][i] += sum_j Mp[c][j] dnum[i][j], j = 32 jb + kappa(r, g).
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + 16 * i;
-    if (r >= rows) continue;
-    if (c0 == 0) att_dot += E[i];
+    for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int c = c0 + 16 * jj;
-      const float g = acc[i][jj] * scale + (dsq[i][jj] + dden[i] * sZ[c]) * elu1_grad_from(sQ[r][c]);
-      dq[(qrow0 + r) * D + c] = g;
-    }
+      for (int r = 0; r < 16; ++r) dsq[cb] = mfma32(sK[kappa(r, g)][32 * cb + l32], dn[r], dsq[cb]);
+  }
+  s1 += __shfl_xor(s1, 32);
+  const float dden = -gam * s1 / (den * den);
+  if (qvalid && g == 0) {
+    dden_out[qbase + qi] = dden;
+    lse_out[qbase + qi] = lse;
+    e_out[qbase + qi] = E;
+  }
+  if (qvalid) {
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int c = 32 * cb + 8 * r4 + 4 * g;
+        float res[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sg = elu1_grad_from(elu1(load_as_f32(q, (qbase + qi) * D + c + i)));
+          res[i] = dqa[cb][4 * r4 + i] * scale + (dsq[cb][4 * r4 + i] + dden * sZ[c + i]) * sg;
+        }
+        *reinterpret_cast<float4 *>(dq + (qbase + qi) * D + c) =
+            make_float4(res[0], res[1], res[2], res[3]);
+      }
   }
   // d beta: sum over rows of dO . (A_mem - A_dot), times g (1 - g).
-  const float contrib = mem_dot - att_dot;
+  const float contrib = (qvalid && g == 0) ? s1 / den - E : 0.f;
   if (contrib != 0.f) atomicAdd(&sAcc, contrib);
   __syncthreads();
   if (t == 0) atomicAdd(dbeta + h, sAcc * gam * (1.f - gam));
 }
 
 // ---------------------------------------------------------------------------
-// key: dK, dV of the local attention for 32 keys of one segment, over every
-// query head of the kv group and every query row at or after the keys.
+// key: dK, dV of the local attention for 128 keys of one segment (32 per
+// wave, K and V rows in registers), over every query head of the kv group and
+// every query row at or after the keys, in chunks of 32 rows staged in LDS
+// for all four waves.
+//   S = Q K^T and dO V^T put one key per lane;
+//   dv^T = dO^T P and dk^T = Q^T dS take P and dS from registers.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_key_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -321,81 +339,90 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(
     const float *__restrict__ E, int Hq, int Hkv, int L, int N, float *__restrict__ dk,
     float *__restrict__ dv) {
   constexpr int P = D + 1;
-  constexpr int NJ = D / 16;
-  __shared__ float sK[kKT][P];
-  __shared__ float sV[kKT][P];
-  __shared__ float sQ[kQT][P];
-  __shared__ float sO[kQT][P];
-  __shared__ float sPt[kKT][kQT + 1];  // (1 - g) P^T
-  __shared__ float sSt[kKT][kQT + 1];  // dS^T
-  __shared__ float sL[kQT], sE[kQT];
+  constexpr int NB = D / 32;
+  constexpr int KT = 128;
+  __shared__ float sQ[32][P];
+  __shared__ float sO[32][P];
+  __shared__ float sL[32], sE[32];
 
-  const int t = threadIdx.x, r0 = t >> 4, c0 = t & 15;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
   const int s = blockIdx.y, kvh = blockIdx.z;
   const int b = kvh / Hkv, j = kvh % Hkv;
   const int grp = Hq / Hkv;
   const int a = s * N, e = min(a + N, L);
-  const int j0 = a + blockIdx.x * kKT;
+  const int j0 = a + blockIdx.x * KT;
   if (j0 >= e) return;
-  const int keys = min(kKT, e - j0);
+  const int wk0 = j0 + 32 * w;  // this wave's first key
+  const bool wave_live = wk0 < e;
+  const int key = wk0 + l32;    // this lane's key
+  const bool kvalid = key < e;
   const float scale = 1.f / sqrtf(static_cast<float>(D));
-  const size_t krow0 = static_cast<size_t>(kvh) * L + j0;
-  load_rows<T, D, P>(sK, k + krow0 * D, kKT, keys, false);
-  load_rows<T, D, P>(sV, v + krow0 * D, kKT, keys, false);
+  const size_t krow = static_cast<size_t>(kvh) * L + key;
 
-  float gk[2][NJ], gv[2][NJ];
-  zero(gk);
-  zero(gv);
+  float kr[D / 2], vr[D / 2];
+#pragma unroll
+  for (int u = 0; u < D / 2; ++u) {
+    kr[u] = kvalid ? load_as_f32(k, krow * D + 2 * u + g) : 0.f;
+    vr[u] = kvalid ? load_as_f32(v, krow * D + 2 * u + g) : 0.f;
+  }
+  f32x16 gk[NB], gv[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    gk[cb] = zero16();
+    gv[cb] = zero16();
+  }
   for (int hl = 0; hl < grp; ++hl) {
     const int h = j * grp + hl;
     const float gam = gate(beta[h]);
     const size_t hrow = (static_cast<size_t>(b) * Hq + h) * L;
-    for (int i0 = j0; i0 < e; i0 += kQT) {
-      const int rows = min(kQT, e - i0);
+    for (int i0 = j0; i0 < e; i0 += 32) {
+      const int rows = min(32, e - i0);
       __syncthreads();
-      load_rows<T, D, P>(sQ, q + (hrow + i0) * D, kQT, rows, false);
-      load_rows<T, D, P>(sO, dout + (hrow + i0) * D, kQT, rows, false);
-      if (t < kQT) {
+      load_rows<T, D, P>(sQ, q + (hrow + i0) * D, 32, rows, false);
+      load_rows<T, D, P>(sO, dout + (hrow + i0) * D, 32, rows, false);
+      if (t < 32) {
         sL[t] = t < rows ? lse[hrow + i0 + t] : 0.f;
         sE[t] = t < rows ? E[hrow + i0 + t] : 0.f;
       }
       __syncthreads();
-      float st[2][4], ot[2][4];
-      zero(st);
-      zero(ot);
-      mm16<2, 4>(st, D, [&](int r, int kk) { return sK[r][kk]; },
-                 [&](int kk, int c) { return sQ[c][kk]; });
-      mm16<2, 4>(ot, D, [&](int r, int kk) { return sV[r][kk]; },
-                 [&](int kk, int c) { return sO[c][kk]; });
+      if (!wave_live || wk0 > i0 + 31) continue;  // every key after every row
+      f32x16 st = zero16(), ot = zero16();
+#pragma unroll 8
+      for (int u = 0; u < D / 2; ++u) {
+        st = mfma32(sQ[l32][2 * u + g], kr[u], st);
+        ot = mfma32(sO[l32][2 * u + g], vr[u], ot);
+      }
+      float pw[16], ds[16];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int r = 0; r < 16; ++r) {
+        const int qr = kappa(r, g), row = i0 + qr;
+        const bool vis = key <= row && row < e && kvalid;
+        const float p = vis ? __expf(st[r] * scale - sL[qr]) : 0.f;
+        pw[r] = (1.f - gam) * p;
+        ds[r] = pw[r] * (ot[r] - sE[qr]);
+      }
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = r0 + 16 * i, c = c0 + 16 * jj;
-          const int key = j0 + r, row = i0 + c;
-          const bool vis = key <= row && row < e && key < e;
-          const float p = vis ? __expf(st[i][jj] * scale - sL[c]) : 0.f;
-          sPt[r][c] = (1.f - gam) * p;
-          sSt[r][c] = (1.f - gam) * p * (ot[i][jj] - sE[c]);
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          gv[cb] = mfma32(sO[kappa(r, g)][32 * cb + l32], pw[r], gv[cb]);
+          gk[cb] = mfma32(sQ[kappa(r, g)][32 * cb + l32], ds[r], gk[cb]);
         }
-      __syncthreads();
-      mm16<2, NJ>(gv, kQT, [&](int r, int kk) { return sPt[r][kk]; },
-                  [&](int kk, int c) { return sO[kk][c]; });
-      mm16<2, NJ>(gk, kQT, [&](int r, int kk) { return sSt[r][kk]; },
-                  [&](int kk, int c) { return sQ[kk][c]; });
     }
   }
+  if (!kvalid) return;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = r0 + 16 * i;
-    if (r >= keys) continue;
+  for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const size_t o = (krow0 + r) * D + c0 + 16 * jj;
-      dk[o] = gk[i][jj] * scale;
-      dv[o] = gv[i][jj];
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int c = 32 * cb + 8 * r4 + 4 * g;
+      *reinterpret_cast<float4 *>(dk + krow * D + c) =
+          make_float4(gk[cb][4 * r4] * scale, gk[cb][4 * r4 + 1] * scale,
+                      gk[cb][4 * r4 + 2] * scale, gk[cb][4 * r4 + 3] * scale);
+      *reinterpret_cast<float4 *>(dv + krow * D + c) =
+          make_float4(gv[cb][4 * r4], gv[cb][4 * r4 + 1], gv[cb][4 * r4 + 2], gv[cb][4 * r4 + 3]);
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -715,12 +742,12 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
                         float *dM0, float *dz0, hipStream_t st) {
   const int grp = g.Hq / g.Hkv;
   const int kvheads = g.B * g.Hkv;
-  bwd_query_kernel<T, D><<<dim3((g.N + kQT - 1) / kQT, g.S, g.B * g.Hq), kThreads, 0, st>>>(
+  bwd_query_kernel<T, D><<<dim3((g.N + 127) / 128, g.S, g.B * g.Hq), kThreads, 0, st>>>(
       q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
       w.dnum, w.dden, dbeta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_key_kernel<T, D><<<dim3((g.N + kKT - 1) / kKT, g.S, kvheads), kThreads, 0, st>>>(
+  bwd_key_kernel<T, D><<<dim3((g.N + 127) / 128, g.S, kvheads), kThreads, 0, st>>>(
       q, k, v, dout, beta, w.lse, w.erow, g.Hq, g.Hkv, g.L, g.N, dk, dv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int rows_r = 1024;

@@ -474,7 +474,7 @@ int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const v
   if (rows) {
     if (!q || !k || !v || !beta || !d_out || !dq || !dk || !dv) return INFINI_ATTN_ERR_INVALID;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_out, 16) ||
-        !aligned(beta, 4) || !aligned(dq, 4) || !aligned(dk, 4) || !aligned(dv, 4))
+        !aligned(beta, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
       return INFINI_ATTN_ERR_INVALID;
   }
   DeviceGuard guard(d.device);

@@ -220,11 +220,13 @@ int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, 
  *   d_out [B, Hq, L, d_v] dtype (device): gradient of the loss w.r.t. out
  *   d_M [B, Hkv, d_k, d_v], d_z [B, Hkv, d_k] fp32 (device), or NULL for zero:
  *       gradient w.r.t. the final state
- *   dq [B, Hq, L, d_k], dk [B, Hkv, L, d_k], dv [B, Hkv, L, d_v] fp32 (device),
- *       written; dk and dv sum over the query heads of each kv group
+ *   dq [B, Hq, L, d_k], dk [B, Hkv, L, d_k], dv [B, Hkv, L, d_v] fp32, 16-byte
+ *       aligned (device), written; dk and dv sum over the query heads of each
+ *       kv group
  *   dbeta [Hq] fp32 (device), written
  *   dM0 [B, Hkv, d_k, d_v], dz0 [B, Hkv, d_k] fp32 (device), written
- * Every arithmetic step is fp32. Output buffers must not alias inputs. The
+ * Every arithmetic step is fp32 (the local attention's products on the fp32
+ * matrix cores). Output buffers must not alias inputs. The
  * handle keeps fp32 scratch of about (B Hq L (d + 3) + 4 B Hkv S d^2) floats,
  * grown on demand. dbeta sums atomically, so its last bits may vary from run
  * to run. B = 0 writes dbeta = 0; L = 0 also passes (d_M, d_z) through to
