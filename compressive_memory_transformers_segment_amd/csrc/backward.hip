@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(
   auto scores = [&](f32x16 &st, f32x16 &ot) {
     st = zero16();
     ot = zero16();
-#pragma unroll 8
+#pragma unroll
     for (int u = 0; u < D / 2; ++u) {
       st = mfma32(sK[l32][2 * u + g], qr[u], st);
       ot = mfma32(sV[l32][2 * u + g], orow[u], ot);
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(
     __syncthreads();
     if (!wave_live) continue;
     f32x16 num = zero16();  // num^T rows 32 jb + kappa, column = this lane's query
-#pragma unroll 8
+#pragma unroll
     for (int u = 0; u < D / 2; ++u) num = mfma32(sK[l32][2 * u + g], qr[u], num);
     float dn[16];
 #pragma unroll
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(
       __syncthreads();
       if (!wave_live || wk0 > i0 + 31) continue;  // every key after every row
       f32x16 st = zero16(), ot = zero16();
-#pragma unroll 8
+#pragma unroll
       for (int u = 0; u < D / 2; ++u) {
         st = mfma32(sQ[l32][2 * u + g], kr[u], st);
         ot = mfma32(sO[l32][2 * u + g], vr[u], ot);
