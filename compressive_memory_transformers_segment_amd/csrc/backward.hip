@@ -32,6 +32,8 @@
 //          dk += gz_s sigma'(k) row by row.
 // sigma'(x) = 1 for x > 0 and exp(x) = sigma(x) otherwise, i.e. min(sigma(x), 1).
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -112,6 +114,33 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// bf16 storage: a product of two stored bf16 tensors runs as
+// v_mfma_f32_32x32x16_bf16. Products of bf16 values are exact in fp32 and the
+// accumulation is fp32, so this is the same arithmetic as the fp32 path. Lane
+// group g supplies the 8 contraction indices 16 t + 8 g + e (e < 8) of step t
+// in both operands.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t *p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
+}
+
+// Rows [0, kn) of a [rows][D] bf16 tensor into an LDS tile with row stride
+// PB (zero past `valid`), 16 bytes at a time.
+template <int D, int PB>
+__device__ __forceinline__ void load_rows_bf16(uint16_t (*dst)[PB], const uint16_t *src, int kn,
+                                               int valid) {
+  constexpr int U = D / 8;
+  for (int idx = threadIdx.x; idx < kn * U; idx += kThreads) {
+    const int r = idx / U, c = 8 * (idx % U);
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (r < valid) x = *reinterpret_cast<const u32x4 *>(src + static_cast<size_t>(r) * D + c);
+    *reinterpret_cast<u32x4 *>(&dst[r][c]) = x;
+  }
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -137,8 +166,12 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(
   constexpr int P = D + 1;
   constexpr int NB = D / 32;  // 32-wide blocks along d
   constexpr int QT = 128;
-  __shared__ float sK[kKT][P];  // key tile, then 32-row chunks of Mp^T
-  __shared__ float sV[kKT][P];
+  constexpr bool BF = std::is_same<T, uint16_t>::value;
+  constexpr int PB = D + 8;   // bf16 row stride: 16-byte aligned rows
+  __shared__ float sK[kKT][P];  // fp32 storage: key tile; both: 32-row chunks of Mp^T
+  __shared__ float sV[BF ? 1 : kKT][P];
+  __shared__ __attribute__((aligned(16))) uint16_t sKb[BF ? kKT : 1][PB];  // bf16 key tile
+  __shared__ __attribute__((aligned(16))) uint16_t sVb[BF ? kKT : 1][PB];
   __shared__ float sZ[D];
   __shared__ float sAcc;
 
@@ -164,29 +197,61 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(
   if (t == 0) sAcc = 0.f;
   for (int c = t; c < D; c += kThreads) sZ[c] = zpre[(kvh * (S + 1) + s) * D + c];
 
-  // This lane's query row and d_out row as B operands: element 2 u + g.
-  float qr[D / 2], orow[D / 2];
+  // This lane's query row and d_out row as B operands: element 2 u + g (fp32
+  // storage), elements 16 t + 8 g + e (bf16 storage).
+  float qr[D / 2], orow[BF ? 1 : D / 2];
+  bf16x8 qb8[BF ? D / 16 : 1], ob8[BF ? D / 16 : 1];
+  if constexpr (BF) {
+    const bf16x8 z8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
-  for (int u = 0; u < D / 2; ++u) {
-    const size_t o = (qbase + qi) * D + 2 * u + g;
-    qr[u] = qvalid ? load_as_f32(q, o) : 0.f;
-    orow[u] = qvalid ? load_as_f32(dout, o) : 0.f;
+    for (int u = 0; u < D / 16; ++u) {
+      const size_t o = (qbase + qi) * D + 16 * u + 8 * g;
+      qb8[u] = qvalid ? ld_bf16x8(reinterpret_cast<const uint16_t *>(q) + o) : z8;
+      ob8[u] = qvalid ? ld_bf16x8(reinterpret_cast<const uint16_t *>(dout) + o) : z8;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < D / 2; ++u) {
+      const size_t o = (qbase + qi) * D + 2 * u + g;
+      qr[u] = qvalid ? load_as_f32(q, o) : 0.f;
+      orow[u] = qvalid ? load_as_f32(dout, o) : 0.f;
+    }
   }
 
   auto load_kv = [&](int j0) {
     __syncthreads();
-    load_rows<T, D, P>(sK, kb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
-    load_rows<T, D, P>(sV, vb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
+    if constexpr (BF) {
+      load_rows_bf16<D, PB>(sKb, reinterpret_cast<const uint16_t *>(kb) + static_cast<size_t>(j0) * D,
+                            kKT, kend - j0);
+      load_rows_bf16<D, PB>(sVb, reinterpret_cast<const uint16_t *>(vb) + static_cast<size_t>(j0) * D,
+                            kKT, kend - j0);
+    } else {
+      load_rows<T, D, P>(sK, kb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
+      load_rows<T, D, P>(sV, vb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
+    }
     __syncthreads();
   };
   auto scores = [&](f32x16 &st, f32x16 &ot) {
     st = zero16();
     ot = zero16();
+    if constexpr (BF) {
 #pragma unroll
-    for (int u = 0; u < D / 2; ++u) {
-      st = mfma32(sK[l32][2 * u + g], qr[u], st);
-      ot = mfma32(sV[l32][2 * u + g], orow[u], ot);
+      for (int u = 0; u < D / 16; ++u) {
+        st = mfma32(ld_bf16x8(&sKb[l32][16 * u + 8 * g]), qb8[u], st);
+        ot = mfma32(ld_bf16x8(&sVb[l32][16 * u + 8 * g]), ob8[u], ot);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < D / 2; ++u) {
+        st = mfma32(sK[l32][2 * u + g], qr[u], st);
+        ot = mfma32(sV[l32][2 * u + g], orow[u], ot);
+      }
     }
+  };
+  // Key row kk, column c of the current key tile as fp32.
+  auto key_at = [&](int kk, int c) -> float {
+    if constexpr (BF) return bf16_to_f32(sKb[kk][c]);
+    else return sK[kk][c];
   };
   // Key tile j0 is visible to some row of this wave.
   auto wave_sees = [&](int j0) { return wave_live && j0 <= wq0 + 31; };
@@ -244,10 +309,14 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dqa[cb] = mfma32(sK[kappa(r, g)][32 * cb + l32], ds[r], dqa[cb]);
+      for (int r = 0; r < 16; ++r) dqa[cb] = mfma32(key_at(kappa(r, g), 32 * cb + l32), ds[r], dqa[cb]);
   }
 
   // Retrieval backward from the pre-segment snapshot (Mp^T in mt, zp in zpre).
+  if constexpr (BF) {
+#pragma unroll
+    for (int u = 0; u < D / 2; ++u) qr[u] = qvalid ? load_as_f32(q, (qbase + qi) * D + 2 * u + g) : 0.f;
+  }
 #pragma unroll
   for (int u = 0; u < D / 2; ++u) qr[u] = elu1(qr[u]);  // sigma(q), element 2 u + g
   float den = 0.f;
@@ -341,8 +410,12 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(
   constexpr int P = D + 1;
   constexpr int NB = D / 32;
   constexpr int KT = 128;
-  __shared__ float sQ[32][P];
-  __shared__ float sO[32][P];
+  constexpr bool BF = std::is_same<T, uint16_t>::value;
+  constexpr int PB = D + 8;
+  __shared__ float sQ[BF ? 1 : 32][P];
+  __shared__ float sO[BF ? 1 : 32][P];
+  __shared__ __attribute__((aligned(16))) uint16_t sQb[BF ? 32 : 1][PB];
+  __shared__ __attribute__((aligned(16))) uint16_t sOb[BF ? 32 : 1][PB];
   __shared__ float sL[32], sE[32];
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -360,12 +433,31 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(
   const float scale = 1.f / sqrtf(static_cast<float>(D));
   const size_t krow = static_cast<size_t>(kvh) * L + key;
 
-  float kr[D / 2], vr[D / 2];
+  float kr[BF ? 1 : D / 2], vr[BF ? 1 : D / 2];
+  bf16x8 kb8[BF ? D / 16 : 1], vb8[BF ? D / 16 : 1];
+  if constexpr (BF) {
+    const bf16x8 z8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
-  for (int u = 0; u < D / 2; ++u) {
-    kr[u] = kvalid ? load_as_f32(k, krow * D + 2 * u + g) : 0.f;
-    vr[u] = kvalid ? load_as_f32(v, krow * D + 2 * u + g) : 0.f;
+    for (int u = 0; u < D / 16; ++u) {
+      const size_t o = krow * D + 16 * u + 8 * g;
+      kb8[u] = kvalid ? ld_bf16x8(reinterpret_cast<const uint16_t *>(k) + o) : z8;
+      vb8[u] = kvalid ? ld_bf16x8(reinterpret_cast<const uint16_t *>(v) + o) : z8;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < D / 2; ++u) {
+      kr[u] = kvalid ? load_as_f32(k, krow * D + 2 * u + g) : 0.f;
+      vr[u] = kvalid ? load_as_f32(v, krow * D + 2 * u + g) : 0.f;
+    }
   }
+  auto q_at = [&](int r, int c) -> float {
+    if constexpr (BF) return bf16_to_f32(sQb[r][c]);
+    else return sQ[r][c];
+  };
+  auto o_at = [&](int r, int c) -> float {
+    if constexpr (BF) return bf16_to_f32(sOb[r][c]);
+    else return sO[r][c];
+  };
   f32x16 gk[NB], gv[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
@@ -379,8 +471,14 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(
     for (int i0 = j0; i0 < e; i0 += 32) {
       const int rows = min(32, e - i0);
       __syncthreads();
-      load_rows<T, D, P>(sQ, q + (hrow + i0) * D, 32, rows, false);
-      load_rows<T, D, P>(sO, dout + (hrow + i0) * D, 32, rows, false);
+      if constexpr (BF) {
+        load_rows_bf16<D, PB>(sQb, reinterpret_cast<const uint16_t *>(q) + (hrow + i0) * D, 32, rows);
+        load_rows_bf16<D, PB>(sOb, reinterpret_cast<const uint16_t *>(dout) + (hrow + i0) * D, 32,
+                              rows);
+      } else {
+        load_rows<T, D, P>(sQ, q + (hrow + i0) * D, 32, rows, false);
+        load_rows<T, D, P>(sO, dout + (hrow + i0) * D, 32, rows, false);
+      }
       if (t < 32) {
         sL[t] = t < rows ? lse[hrow + i0 + t] : 0.f;
         sE[t] = t < rows ? E[hrow + i0 + t] : 0.f;
@@ -388,10 +486,18 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(
       __syncthreads();
       if (!wave_live || wk0 > i0 + 31) continue;  // every key after every row
       f32x16 st = zero16(), ot = zero16();
+      if constexpr (BF) {
 #pragma unroll
-      for (int u = 0; u < D / 2; ++u) {
-        st = mfma32(sQ[l32][2 * u + g], kr[u], st);
-        ot = mfma32(sO[l32][2 * u + g], vr[u], ot);
+        for (int u = 0; u < D / 16; ++u) {
+          st = mfma32(ld_bf16x8(&sQb[l32][16 * u + 8 * g]), kb8[u], st);
+          ot = mfma32(ld_bf16x8(&sOb[l32][16 * u + 8 * g]), vb8[u], ot);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < D / 2; ++u) {
+          st = mfma32(sQ[l32][2 * u + g], kr[u], st);
+          ot = mfma32(sO[l32][2 * u + g], vr[u], ot);
+        }
       }
       float pw[16], ds[16];
 #pragma unroll
@@ -406,8 +512,8 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(
       for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          gv[cb] = mfma32(sO[kappa(r, g)][32 * cb + l32], pw[r], gv[cb]);
-          gk[cb] = mfma32(sQ[kappa(r, g)][32 * cb + l32], ds[r], gk[cb]);
+          gv[cb] = mfma32(o_at(kappa(r, g), 32 * cb + l32), pw[r], gv[cb]);
+          gk[cb] = mfma32(q_at(kappa(r, g), 32 * cb + l32), ds[r], gk[cb]);
         }
     }
   }
