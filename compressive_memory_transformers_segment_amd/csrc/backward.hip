@@ -157,7 +157,7 @@ __device__ __forceinline__ f32x16 zero16() {
 //   retrieval: num^T = Mp^T sigma(Q)^T and dsq^T = Mp dnum^T, one 32-row
 //   chunk of Mp^T in LDS at a time.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_query_kernel(
+__global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1)) void bwd_query_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ beta, const float *__restrict__ mt,
     const float *__restrict__ zpre, int Hq, int Hkv, int L, int N, int S, float eps,
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(
 //   S = Q K^T and dO V^T put one key per lane;
 //   dv^T = dO^T P and dk^T = Q^T dS take P and dS from registers.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_key_kernel(
+__global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1)) void bwd_key_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ beta, const float *__restrict__ lse,
     const float *__restrict__ E, int Hq, int Hkv, int L, int N, float *__restrict__ dk,

@@ -12,8 +12,10 @@
 //
 // Column j of M evolves using only column j of M and z (the delta rule's
 // retrieval divides row-wise by a scalar that depends on z alone), so the
-// columns are split over workgroups with no communication. Each workgroup
-// owns CB columns of one (b, kv head), keeps them in registers, and walks the
+// columns are split over workgroups with no communication, and every column
+// goes through the same operations in the same order whatever the split. Each
+// workgroup owns CB columns of one (b, kv head), keeps them in registers, and
+// walks the
 // segments in order, R rows at a time. Before each segment it writes the
 // pre-segment snapshot (M_{s-1} transposed, z_{s-1}) that the fused attention
 // kernel reads for that segment's retrieval.
@@ -25,10 +27,15 @@ namespace ia {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCB = 16;  // columns of M per workgroup
 constexpr int kR = 64;   // rows of a segment processed per chunk
 
-template <typename T, int D>
+// Columns of M per workgroup: as few as keep every thread busy (threads
+// sharing one state row hold one column each), so that B * Hkv * D / CB
+// workgroups fill the chip.
+template <int D>
+constexpr int scan_cols() { return kThreads / D > 4 ? kThreads / D : 4; }
+
+template <typename T, int D, int kCB>
 __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
     const T *__restrict__ k, const T *__restrict__ v, float *__restrict__ M,
     const float *__restrict__ z, int L, int N, int S, float eps, int delta,
@@ -36,6 +43,7 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
   static_assert(D <= kThreads && kThreads % D == 0 && D % kCB == 0, "tile shape");
   constexpr int JSTEP = kThreads / D;  // threads sharing one row k of the state
   constexpr int JPT = kCB / JSTEP;     // state columns per thread
+  static_assert(JPT >= 1 && kCB % JSTEP == 0, "column split");
   constexpr int ISTEP = kThreads / kCB;
 
   __shared__ float sK[kR][D + 1];   // sigma(K) of the chunk (pad: conflict-free rows)
@@ -130,8 +138,9 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
 template <typename T, int D>
 hipError_t launch_scan_t(const Geometry &g, const T *k, const T *v, float *M, const float *z,
                          int delta, const Workspace &ws, hipStream_t stream) {
-  dim3 grid(D / kCB, g.B * g.Hkv);
-  segment_scan_kernel<T, D><<<grid, kThreads, 0, stream>>>(
+  constexpr int CB = scan_cols<D>();
+  dim3 grid(D / CB, g.B * g.Hkv);
+  segment_scan_kernel<T, D, CB><<<grid, kThreads, 0, stream>>>(
       k, v, M, z, g.L, g.N, g.S, g.eps, delta,
       ws.z_pre, ws.mt_pre_f32, ws.mt_pre_bf16);
   return hipGetLastError();
