@@ -24,8 +24,10 @@ segment):
   update backward           4 N d^2 linear (sigma(K) gM, V gM^T);
                             10 N d^2 + 2 d^3 delta (also sigma(K) M,
                             (Y / den) M^T, G_s, and (I - G_s) gM on the chain)
-Every step runs in fp32 on the vector ALUs, so the rate is priced against the
-fp32 vector peak (157.3 TFLOP/s).
+The arithmetic is fp32 throughout: products of two stored bf16 tensors run on
+the bf16 matrix cores (a bf16 product is exact in fp32, and they accumulate in
+fp32), the rest on the fp32 matrix cores and vector ALUs. The rate is priced
+against the fp32 peak (157.3 TFLOP/s).
 """
 
 from __future__ import annotations

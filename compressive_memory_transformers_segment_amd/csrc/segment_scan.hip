@@ -68,6 +68,26 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
   for (int r = 0; r < JPT; ++r) m_reg[r] = Mb[kk * D + c0 + j0 + JSTEP * r];
   float zval = z[static_cast<size_t>(bh) * D + kk];
 
+  // The next chunk's K and V values are fetched into registers while the
+  // current chunk is processed, so a chunk never waits on memory latency.
+  constexpr int KPT = kR * D / kThreads;                  // K values per thread
+  constexpr int VPT = (kR * kCB + kThreads - 1) / kThreads;  // V values per thread
+  float pk[KPT], pv[VPT];
+  auto fetch = [&](int i0, int rows) {
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int idx = t + r * kThreads, i = idx / D, c = idx % D;
+      pk[r] = i < rows ? load_as_f32(kb, static_cast<size_t>(i0 + i) * D + c) : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < VPT; ++r) {
+      const int idx = t + r * kThreads, i = idx / kCB, c = idx % kCB;
+      pv[r] = (idx < kR * kCB && i < rows)
+                  ? load_as_f32(vb, static_cast<size_t>(i0 + i) * D + c0 + c) : 0.f;
+    }
+  };
+  if (L > 0) fetch(0, min(kR, min(N, L)));
+
   for (int s = 0; s < S; ++s) {
     const int a = s * N;
     const int e = min(a + N, L);
@@ -93,13 +113,20 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
     for (int i0 = a; i0 < e; i0 += kR) {
       const int rows = min(kR, e - i0);
       __syncthreads();  // sK / sU free; sM / sZ visible
-      for (int idx = t; idx < kR * D; idx += kThreads) {
-        const int i = idx / D, c = idx % D;
-        sK[i][c] = (i < rows) ? elu1(load_as_f32(kb, static_cast<size_t>(i0 + i) * D + c)) : 0.f;
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) {
+        const int idx = t + r * kThreads, i = idx / D, c = idx % D;
+        sK[i][c] = (i < rows) ? elu1(pk[r]) : 0.f;
       }
-      for (int idx = t; idx < kR * kCB; idx += kThreads) {
-        const int i = idx / kCB, c = idx % kCB;
-        sU[i][c] = (i < rows) ? load_as_f32(vb, static_cast<size_t>(i0 + i) * D + c0 + c) : 0.f;
+#pragma unroll
+      for (int r = 0; r < VPT; ++r) {
+        const int idx = t + r * kThreads;
+        if (idx < kR * kCB) sU[idx / kCB][idx % kCB] = pv[r];
+      }
+      {  // the chunk after this one: the rest of this segment, else the next segment
+        const int nx = i0 + kR < e ? i0 + kR : e;
+        const int nend = nx == e ? min(e + N, L) : e;
+        if (nx < L) fetch(nx, min(kR, nend - nx));
       }
       __syncthreads();
       if (delta) {
@@ -117,7 +144,10 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
         }
         __syncthreads();
       }
-      for (int i = 0; i < rows; ++i) {
+      // All kR rows: rows past the chunk's end are zero in sK and sU and add
+      // exact zeros, and a fixed trip count lets the LDS reads pipeline.
+#pragma unroll 16
+      for (int i = 0; i < kR; ++i) {
         const float kv = sK[i][kk];
         dz += kv;
 #pragma unroll

@@ -225,8 +225,10 @@ int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, 
  *       kv group
  *   dbeta [Hq] fp32 (device), written
  *   dM0 [B, Hkv, d_k, d_v], dz0 [B, Hkv, d_k] fp32 (device), written
- * Every arithmetic step is fp32 (the local attention's products on the fp32
- * matrix cores). Output buffers must not alias inputs. The
+ * Every arithmetic step is fp32: for bf16 storage, products of two stored
+ * tensors run on the bf16 matrix cores, exact in fp32 with fp32 accumulation;
+ * the other products run on the fp32 matrix cores. Output buffers must not
+ * alias inputs. The
  * handle keeps fp32 scratch of about (B Hq L (d + 3) + 4 B Hkv S d^2) floats,
  * grown on demand. dbeta sums atomically, so its last bits may vary from run
  * to run. B = 0 writes dbeta = 0; L = 0 also passes (d_M, d_z) through to
