@@ -141,6 +141,29 @@ __device__ __forceinline__ void load_rows_bf16(uint16_t (*dst)[PB], const uint16
   }
 }
 
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): the pair carries x to
+// about 2^-17 relative, so a product of x with a stored bf16 operand runs as
+// two bf16 MFMAs at fp32-level accuracy. Element e of the pair holds x[e].
+__device__ __forceinline__ void split_bf16x8(const float *x, bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = static_cast<__bf16>(x[e]);
+    hi[e] = h;
+    lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
+  }
+}
+
+// The 8 values of column c at rows kappa(8 st + e, g), e < 8, of a bf16 LDS
+// tile: the A operand matching a result block's registers 8 st .. 8 st + 7
+// used as the B operand (the contraction runs over the block's rows).
+template <int PB>
+__device__ __forceinline__ bf16x8 gather_rows(const uint16_t (*tile)[PB], int st, int g, int c) {
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = __builtin_bit_cast(__bf16, tile[kappa(8 * st + e, g)][c]);
+  return a;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -306,10 +329,24 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
       const float p = (key <= qi && key < e) ? __expf(st[r] * scale - lse) : 0.f;
       ds[r] = (1.f - gam) * p * (ot[r] - E);
     }
+    if constexpr (BF) {
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb)
+      for (int st = 0; st < 2; ++st) {
+        bf16x8 hi, lo;
+        split_bf16x8(ds + 8 * st, hi, lo);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dqa[cb] = mfma32(key_at(kappa(r, g), 32 * cb + l32), ds[r], dqa[cb]);
+        for (int cb = 0; cb < NB; ++cb) {
+          const bf16x8 ak = gather_rows<PB>(sKb, st, g, 32 * cb + l32);
+          dqa[cb] = mfma32(ak, hi, dqa[cb]);
+          dqa[cb] = mfma32(ak, lo, dqa[cb]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqa[cb] = mfma32(key_at(kappa(r, g), 32 * cb + l32), ds[r], dqa[cb]);
+    }
   }
 
   // Retrieval backward from the pre-segment snapshot (Mp^T in mt, zp in zpre).
@@ -508,13 +545,31 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
         pw[r] = (1.f - gam) * p;
         ds[r] = pw[r] * (ot[r] - sE[qr]);
       }
+      if constexpr (BF) {
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb)
+        for (int st = 0; st < 2; ++st) {
+          bf16x8 phi, plo, dhi, dlo;
+          split_bf16x8(pw + 8 * st, phi, plo);
+          split_bf16x8(ds + 8 * st, dhi, dlo);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          gv[cb] = mfma32(o_at(kappa(r, g), 32 * cb + l32), pw[r], gv[cb]);
-          gk[cb] = mfma32(q_at(kappa(r, g), 32 * cb + l32), ds[r], gk[cb]);
+          for (int cb = 0; cb < NB; ++cb) {
+            const bf16x8 ao = gather_rows<PB>(sOb, st, g, 32 * cb + l32);
+            const bf16x8 aq = gather_rows<PB>(sQb, st, g, 32 * cb + l32);
+            gv[cb] = mfma32(ao, phi, gv[cb]);
+            gv[cb] = mfma32(ao, plo, gv[cb]);
+            gk[cb] = mfma32(aq, dhi, gk[cb]);
+            gk[cb] = mfma32(aq, dlo, gk[cb]);
+          }
         }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            gv[cb] = mfma32(o_at(kappa(r, g), 32 * cb + l32), pw[r], gv[cb]);
+            gk[cb] = mfma32(q_at(kappa(r, g), 32 * cb + l32), ds[r], gk[cb]);
+          }
+      }
     }
   }
   if (!kvalid) return;

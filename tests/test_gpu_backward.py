@@ -147,3 +147,15 @@ def test_backward_empty():
             assert np.array_equal(got[4], cot["d_M"].astype(np.float64))
             assert np.array_equal(got[5], cot["d_z"].astype(np.float64))
     torch.cuda.synchronize()
+
+
+def test_backward_300m_shape_two_segments():
+    """The 300M LLaMA-like layer (B=4, 16 heads, d = 64, segments of 2048, 5% of
+    the key rows scaled by 4) over its first two segments, delta rule."""
+    w = synth.WORKLOADS["llama300m_16k"]
+    inp = synth.generate(w, seq_len=4096)
+    inp["z0"] = inp["z0"] + np.float32(2048.0)  # as after one earlier 2048-row segment
+    cot = synth.random_cotangents(42, w.batch, w.n_q_heads, w.n_kv_heads, 4096, w.d, "bf16")
+    log("bwd llama300m_16k L=4096 delta")
+    check_grads("bwd 300m L=4096 delta", run_gpu_bwd(inp, cot, "bf16", w.seg_len, "delta"),
+                run_oracle_bwd(inp, cot, "bf16", w.seg_len, "delta"))
