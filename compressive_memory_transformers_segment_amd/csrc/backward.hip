@@ -9,8 +9,12 @@
 // the state the segment reads, (gM_s, gz_s) the gradient of the state after
 // it, sq = sigma(q), sk = sigma(k), den = sq . zp + eps, denk = sk . zp + eps.
 //
-// The work splits into parts that are independent per segment and two short
-// chains that run backwards over the segments:
+// The work splits into parts that are independent per segment and short
+// chains over the segments:
+//   states per (b, kv head, segment): the column sums of sigma(K) (then their
+//          prefix, z before each segment), H_s = sigma(K)^T V and, for the
+//          delta rule, G_s; then the d x d chain M_s = (I - G_s) M_{s-1} + H_s
+//          (G_s = 0 for the linear rule) gives the state every segment reads;
 //   query  per (b, q head, segment, 128 query rows): the local attention's dQ
 //          (softmax backward with the row statistics recomputed), the
 //          retrieval backward (dnum = g dO / den, dden = -g sum(dO num) / den^2,
@@ -591,12 +595,13 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
 //   kind 0 (R): rows = (query head of the group, row of the segment),
 //               A = sigma(q), B = dnum; r_s = sum A^T dden as well.
 //   kind 1 (G): rows = rows of the segment, A = sigma(k), B = sigma(k) / denk.
+//   kind 2 (H): rows = rows of the segment, A = sigma(k), B = v (x2).
 // out must be zeroed first; the row ranges of one unit add atomically.
 template <typename T, int D, int KIND>
 __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
-    const T *__restrict__ x, const float *__restrict__ dnum, const float *__restrict__ dden,
-    const float *__restrict__ zpre, int Hq, int Hkv, int L, int N, int S, float eps,
-    int rows_per_block, float *__restrict__ out, float *__restrict__ rvec) {
+    const T *__restrict__ x, const T *__restrict__ x2, const float *__restrict__ dnum,
+    const float *__restrict__ dden, const float *__restrict__ zpre, int Hq, int Hkv, int L, int N,
+    int S, float eps, int rows_per_block, float *__restrict__ out, float *__restrict__ rvec) {
   constexpr int P = D + 1;
   constexpr int MI = D / 16;
   __shared__ float sA[kKT][P];
@@ -637,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
       if (r < cnt) {
         const size_t row = src_row(c0u + r);
         av = elu1(load_as_f32(x, row * D + c));
-        bv = KIND == 0 ? dnum[row * D + c] : av;
+        bv = KIND == 0 ? dnum[row * D + c] : (KIND == 2 ? load_as_f32(x2, row * D + c) : av);
       }
       sA[r][c] = av;
       sB[r][c] = bv;
@@ -656,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
     } else {
       mm16<MI, MI>(acc, kKT, [&](int r, int kk) { return sA[kk][r]; },
                    [&](int kk, int c) { return sB[kk][c]; });
-      if (t < D)
+      if (KIND == 0 && t < D)
         for (int kk = 0; kk < kKT; ++kk) racc += sA[kk][t] * sX[kk];
     }
   }
@@ -670,10 +675,16 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// chain: gM backwards over the segments, 32 columns per workgroup (column c of
-// gM_{s-1} depends on column c of gM_s only). Writes gM_s (the gradient of the
-// state after segment s) for every s, and gM_0 into dM0.
-template <int D>
+// chain: X <- X - G_s X + R_s (the G term for the delta rule only), 32
+// columns per workgroup (column c of the result depends on column c of X
+// only).
+//   backward (FWD = false): X = gM, walked from s = S-1 down to 0; writes gM_s
+//     (the gradient of the state after segment s) for every s, and gM_0.
+//   forward (FWD = true): X = M, R = H, walked from s = 0 up; the delta
+//     update is affine in the state, M_s = (I - G_s) M_{s-1} + H_s, with
+//     H_s = sigma(K_s)^T V_s. Writes M_{s-1}^T for every s (the snapshot
+//     layout), nothing at the end.
+template <int D, bool FWD>
 __global__ __launch_bounds__(kThreads) void bwd_gm_chain_kernel(
     const float *__restrict__ R, const float *__restrict__ G, const float *__restrict__ dM,
     int S, int delta, float *__restrict__ gma, float *__restrict__ dM0) {
@@ -689,13 +700,16 @@ __global__ __launch_bounds__(kThreads) void bwd_gm_chain_kernel(
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
       g[i][jj] = dM ? dM[kvh * D * D + (r0 + 16 * i) * D + col0 + c0 + 16 * jj] : 0.f;
-  for (int s = S - 1; s >= 0; --s) {
+  for (int step = 0; step < S; ++step) {
+    const int s = FWD ? step : S - 1 - step;
     const size_t base = (kvh * S + s) * D * D;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        gma[base + (r0 + 16 * i) * D + col0 + c0 + 16 * jj] = g[i][jj];
+      for (int jj = 0; jj < 2; ++jj) {
+        const int r = r0 + 16 * i, c = col0 + c0 + 16 * jj;
+        gma[base + (FWD ? c * D + r : r * D + c)] = g[i][jj];
+      }
     if (delta) {
       __syncthreads();
 #pragma unroll
@@ -724,10 +738,50 @@ __global__ __launch_bounds__(kThreads) void bwd_gm_chain_kernel(
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) g[i][jj] += R[base + (r0 + 16 * i) * D + col0 + c0 + 16 * jj];
   }
+  if (!FWD) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) dM0[kvh * D * D + (r0 + 16 * i) * D + col0 + c0 + 16 * jj] = g[i][jj];
+      for (int jj = 0; jj < 2; ++jj)
+        dM0[kvh * D * D + (r0 + 16 * i) * D + col0 + c0 + 16 * jj] = g[i][jj];
+  }
+}
+
+// Per-segment column sums of sigma(k): dz[unit][c] = sum over the segment's
+// rows of sigma(k[i][c]).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_zsum_kernel(const T *__restrict__ k, int L, int N,
+                                                            int S, float *__restrict__ dz) {
+  constexpr int RG = kThreads / D;  // row groups
+  __shared__ float part[RG][D];
+  const int t = threadIdx.x, c = t % D, rg = t / D;
+  const int s = blockIdx.x;
+  const size_t kvh = blockIdx.y;
+  const int a = s * N, e = min(a + N, L);
+  const T *kb = k + kvh * L * D;
+  float acc = 0.f;
+  for (int i = a + rg; i < e; i += RG) acc += elu1(load_as_f32(kb, static_cast<size_t>(i) * D + c));
+  part[rg][c] = acc;
+  __syncthreads();
+  if (t < D) {
+    float z = 0.f;
+    for (int j = 0; j < RG; ++j) z += part[j][t];
+    dz[(kvh * S + s) * D + t] = z;
+  }
+}
+
+// z before every segment: z_pre[kvh][s] = z0 + sum_{t < s} dz[t] (slot S: the final z).
+__global__ void bwd_zprefix_kernel(const float *__restrict__ dz, const float *__restrict__ z0,
+                                   int S, int D, float *__restrict__ zpre) {
+  const size_t kvh = blockIdx.x;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float z = z0[kvh * D + c];
+    for (int s = 0; s < S; ++s) {
+      zpre[(kvh * (S + 1) + s) * D + c] = z;
+      z += dz[(kvh * S + s) * D + c];
+    }
+    zpre[(kvh * (S + 1) + S) * D + c] = z;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -898,31 +952,44 @@ __global__ void bwd_dk_gz_kernel(const T *__restrict__ k, const float *__restric
 
 template <typename T, int D>
 hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, const T *dout,
-                        const float *beta, const float *dM, const float *dz, int delta,
-                        const BwdWorkspace &w, float *dq, float *dk, float *dv, float *dbeta,
-                        float *dM0, float *dz0, hipStream_t st) {
+                        const float *beta, const float *M0, const float *z0, const float *dM,
+                        const float *dz, int delta, const BwdWorkspace &w, float *dq, float *dk,
+                        float *dv, float *dbeta, float *dM0, float *dz0, hipStream_t st) {
   const int grp = g.Hq / g.Hkv;
   const int kvheads = g.B * g.Hkv;
-  bwd_query_kernel<T, D><<<dim3((g.N + 127) / 128, g.S, g.B * g.Hq), kThreads, 0, st>>>(
-      q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
-      w.dnum, w.dden, dbeta);
+  const int rows_r = 1024;
+  // The forward's state before every segment: z prefix, then G_s (delta) and
+  // H_s in parallel, then the d x d chain.
+  bwd_zsum_kernel<T, D><<<dim3(g.S, kvheads), kThreads, 0, st>>>(k, g.L, g.N, g.S, w.dzs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_key_kernel<T, D><<<dim3((g.N + 127) / 128, g.S, kvheads), kThreads, 0, st>>>(
-      q, k, v, dout, beta, w.lse, w.erow, g.Hq, g.Hkv, g.L, g.N, dk, dv);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int rows_r = 1024;
-  bwd_outer_kernel<T, D, 0><<<dim3((grp * g.N + rows_r - 1) / rows_r, g.S, kvheads), kThreads, 0,
-                              st>>>(q, w.dnum, w.dden, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps,
-                                    rows_r, w.R, w.r);
+  bwd_zprefix_kernel<<<kvheads, D, 0, st>>>(w.dzs, z0, g.S, D, w.z_pre);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (delta) {
     bwd_outer_kernel<T, D, 1><<<dim3((g.N + rows_r - 1) / rows_r, g.S, kvheads), kThreads, 0,
-                                st>>>(k, nullptr, nullptr, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S,
-                                      g.eps, rows_r, w.G, nullptr);
+                                st>>>(k, nullptr, nullptr, nullptr, w.z_pre, g.Hq, g.Hkv, g.L, g.N,
+                                      g.S, g.eps, rows_r, w.G, nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  bwd_gm_chain_kernel<D><<<dim3(D / kKT, kvheads), kThreads, 0, st>>>(w.R, w.G, dM, g.S, delta,
+  bwd_outer_kernel<T, D, 2><<<dim3((g.N + rows_r - 1) / rows_r, g.S, kvheads), kThreads, 0,
+                              st>>>(k, v, nullptr, nullptr, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S,
+                                    g.eps, rows_r, w.H, nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_gm_chain_kernel<D, true><<<dim3(D / kKT, kvheads), kThreads, 0, st>>>(w.H, w.G, M0, g.S,
+                                                                           delta, w.mt, nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_query_kernel<T, D><<<dim3((g.N + 127) / 128, g.S, g.B * g.Hq), kThreads, 0, st>>>(
+      q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
+      w.dnum, w.dden, dbeta);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_key_kernel<T, D><<<dim3((g.N + 127) / 128, g.S, kvheads), kThreads, 0, st>>>(
+      q, k, v, dout, beta, w.lse, w.erow, g.Hq, g.Hkv, g.L, g.N, dk, dv);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_outer_kernel<T, D, 0><<<dim3((grp * g.N + rows_r - 1) / rows_r, g.S, kvheads), kThreads, 0,
+                              st>>>(q, nullptr, w.dnum, w.dden, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S,
+                                    g.eps, rows_r, w.R, w.r);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_gm_chain_kernel<D, false><<<dim3(D / kKT, kvheads), kThreads, 0, st>>>(w.R, w.G, dM, g.S, delta,
                                                                       w.gma, dM0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bwd_update_kernel<T, D><<<dim3((g.N + kKT - 1) / kKT, g.S, kvheads), kThreads, 0, st>>>(
@@ -941,31 +1008,33 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
 
 template <typename T>
 hipError_t launch_backward(const Geometry &g, const T *q, const T *k, const T *v, const T *dout,
-                           const float *beta, const float *dM, const float *dz, int delta,
-                           const BwdWorkspace &w, float *dq, float *dk, float *dv, float *dbeta,
-                           float *dM0, float *dz0, hipStream_t stream) {
+                           const float *beta, const float *M0, const float *z0, const float *dM,
+                           const float *dz, int delta, const BwdWorkspace &w, float *dq, float *dk,
+                           float *dv, float *dbeta, float *dM0, float *dz0, hipStream_t stream) {
   switch (g.D) {
     case 32:
-      return launch_bwd_t<T, 32>(g, q, k, v, dout, beta, dM, dz, delta, w, dq, dk, dv, dbeta, dM0,
-                                 dz0, stream);
+      return launch_bwd_t<T, 32>(g, q, k, v, dout, beta, M0, z0, dM, dz, delta, w, dq, dk, dv,
+                                 dbeta, dM0, dz0, stream);
     case 64:
-      return launch_bwd_t<T, 64>(g, q, k, v, dout, beta, dM, dz, delta, w, dq, dk, dv, dbeta, dM0,
-                                 dz0, stream);
+      return launch_bwd_t<T, 64>(g, q, k, v, dout, beta, M0, z0, dM, dz, delta, w, dq, dk, dv,
+                                 dbeta, dM0, dz0, stream);
     case 128:
-      return launch_bwd_t<T, 128>(g, q, k, v, dout, beta, dM, dz, delta, w, dq, dk, dv, dbeta,
-                                  dM0, dz0, stream);
+      return launch_bwd_t<T, 128>(g, q, k, v, dout, beta, M0, z0, dM, dz, delta, w, dq, dk, dv,
+                                  dbeta, dM0, dz0, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template hipError_t launch_backward<float>(const Geometry &, const float *, const float *,
                                            const float *, const float *, const float *,
-                                           const float *, const float *, int, const BwdWorkspace &,
+                                           const float *, const float *, const float *,
+                                           const float *, int, const BwdWorkspace &,
                                            float *, float *, float *, float *, float *, float *,
                                            hipStream_t);
 template hipError_t launch_backward<uint16_t>(const Geometry &, const uint16_t *, const uint16_t *,
                                               const uint16_t *, const uint16_t *, const float *,
-                                              const float *, const float *, int,
+                                              const float *, const float *, const float *,
+                                              const float *, int,
                                               const BwdWorkspace &, float *, float *, float *,
                                               float *, float *, float *, hipStream_t);
 

@@ -5,8 +5,9 @@
 //   decode:   split partials of the local attention  ->  merge, retrieval, gate
 //   block:    Q/K/V projections (rocBLAS) and regrouping  ->  forward  ->  regroup
 //             ->  output projection
-//   backward: fp32 segment scan (snapshots)  ->  per-segment gradient kernels,
-//             the reverse state chains and the memory write's gradient
+//   backward: the forward's per-segment states (parallel sums, a d x d chain)
+//             ->  per-segment gradient kernels, the reverse state chains and
+//             the memory write's gradient
 // enqueued on the handle's stream with no host synchronisation.
 
 #include "infini_attn.h"
@@ -505,31 +506,32 @@ int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const v
   g.eps = d.eps;
   const int delta = update_mode == INFINI_ATTN_DELTA;
 
-  // Scratch layout (each part 256-byte aligned): z_pre, mt, M copy, lse, erow,
-  // dnum, dden, R, r, G (delta only), qz, gma, gza.
+  // Scratch layout (each part 256-byte aligned): z_pre, mt, dzs, lse, erow,
+  // dnum, dden, R, r, G (delta only), qz, H, gma, gza.
   const size_t units = kvheads * g.S;
   const size_t qrows = static_cast<size_t>(g.B) * g.Hq * g.L;
-  const size_t sz[13] = {
+  const size_t sz[14] = {
       round_up(kvheads * (g.S + 1) * D * sizeof(float)), round_up(units * D * D * sizeof(float)),
-      round_up(state_bytes), round_up(qrows * sizeof(float)), round_up(qrows * sizeof(float)),
-      round_up(qrows * D * sizeof(float)), round_up(qrows * sizeof(float)),
-      round_up(units * D * D * sizeof(float)), round_up(units * D * sizeof(float)),
-      delta ? round_up(units * D * D * sizeof(float)) : 0, round_up(units * D * sizeof(float)),
+      round_up(units * D * sizeof(float)), round_up(qrows * sizeof(float)),
+      round_up(qrows * sizeof(float)), round_up(qrows * D * sizeof(float)),
+      round_up(qrows * sizeof(float)), round_up(units * D * D * sizeof(float)),
+      round_up(units * D * sizeof(float)), delta ? round_up(units * D * D * sizeof(float)) : 0,
+      round_up(units * D * sizeof(float)), round_up(units * D * D * sizeof(float)),
       round_up(units * D * D * sizeof(float)), round_up(units * D * sizeof(float))};
   size_t total = 0;
   for (size_t x : sz) total += x;
   st = ensure_buffer(&h->bwd_ws, &h->bwd_ws_bytes, total);
   if (st != INFINI_ATTN_OK) return st;
-  float *part[13];
+  float *part[14];
   char *base = static_cast<char *>(h->bwd_ws);
-  for (int i = 0; i < 13; ++i) {
+  for (int i = 0; i < 14; ++i) {
     part[i] = reinterpret_cast<float *>(base);
     base += sz[i];
   }
   ia::BwdWorkspace w;
   w.z_pre = part[0];
   w.mt = part[1];
-  float *Mcopy = part[2];
+  w.dzs = part[2];
   w.lse = part[3];
   w.erow = part[4];
   w.dnum = part[5];
@@ -538,34 +540,24 @@ int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const v
   w.r = part[8];
   w.G = delta ? part[9] : nullptr;
   w.qz = part[10];
-  w.gma = part[11];
-  w.gza = part[12];
+  w.H = part[11];
+  w.gma = part[12];
+  w.gza = part[13];
 
-  // The zeroed accumulators (R, r, G, qz) are contiguous apart from the
-  // G gap, which is cleared with them.
-  e = hipMemsetAsync(w.R, 0, sz[7] + sz[8] + sz[9] + sz[10], stream);
+  // The zeroed accumulators (R, r, G, qz, H) are contiguous.
+  e = hipMemsetAsync(w.R, 0, sz[7] + sz[8] + sz[9] + sz[10] + sz[11], stream);
   if (e != hipSuccess) return hip_status(e);
-  // Forward state chain in fp32: the snapshots (M_{s-1}, z_{s-1}) of every segment.
-  e = hipMemcpyAsync(Mcopy, M0, state_bytes, hipMemcpyDeviceToDevice, stream);
-  if (e != hipSuccess) return hip_status(e);
-  ia::Workspace ws{};
-  ws.z_pre = w.z_pre;
-  ws.mt_pre_f32 = w.mt;
   if (d.dtype == INFINI_ATTN_BF16) {
     const uint16_t *qb = static_cast<const uint16_t *>(q), *kb = static_cast<const uint16_t *>(k),
                    *vb = static_cast<const uint16_t *>(v),
                    *ob = static_cast<const uint16_t *>(d_out);
-    e = ia::launch_segment_scan_f32(g, kb, vb, Mcopy, z0, delta, ws, stream);
-    if (e == hipSuccess)
-      e = ia::launch_backward<uint16_t>(g, qb, kb, vb, ob, beta, d_M, d_z, delta, w, dq, dk, dv,
-                                        dbeta, dM0, dz0, stream);
+    e = ia::launch_backward<uint16_t>(g, qb, kb, vb, ob, beta, M0, z0, d_M, d_z, delta, w, dq, dk,
+                                      dv, dbeta, dM0, dz0, stream);
   } else {
     const float *qf = static_cast<const float *>(q), *kf = static_cast<const float *>(k),
                 *vf = static_cast<const float *>(v), *of = static_cast<const float *>(d_out);
-    e = ia::launch_segment_scan_f32(g, kf, vf, Mcopy, z0, delta, ws, stream);
-    if (e == hipSuccess)
-      e = ia::launch_backward<float>(g, qf, kf, vf, of, beta, d_M, d_z, delta, w, dq, dk, dv,
-                                     dbeta, dM0, dz0, stream);
+    e = ia::launch_backward<float>(g, qf, kf, vf, of, beta, M0, z0, d_M, d_z, delta, w, dq, dk,
+                                   dv, dbeta, dM0, dz0, stream);
   }
   return hip_status(e);
 }

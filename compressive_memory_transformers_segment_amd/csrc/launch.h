@@ -45,12 +45,6 @@ hipError_t launch_segment_scan_f32(const Geometry &g, const float *k, const floa
                                    const float *z, int delta, const Workspace &ws,
                                    hipStream_t stream);
 
-// The same fp32 scan over bf16 k, v: fp32 snapshots (ws.mt_pre_f32, z_pre)
-// for the backward pass, whatever the storage type.
-hipError_t launch_segment_scan_f32(const Geometry &g, const uint16_t *k, const uint16_t *v,
-                                   float *M, const float *z, int delta, const Workspace &ws,
-                                   hipStream_t stream);
-
 // Segment scan, bf16 storage: per-segment statistics on MFMA in parallel, then
 // the fp32 recurrence; writes z_pre (slot S = final z), mt_pre_bf16 and M.
 hipError_t launch_segment_scan_bf16(const Geometry &g, const uint16_t *k, const uint16_t *v,
@@ -83,16 +77,19 @@ struct BwdWorkspace {
   float *qz;     // [units][D] delta rule's sigma(k)^T ddenk (zeroed)
   float *gma;    // [units][D][D] gradient of M after each segment
   float *gza;    // [units][D] gradient of z after each segment
+  float *H;      // [units][D][D] sigma(k)^T v of each segment (zeroed)
+  float *dzs;    // [units][D] column sums of sigma(k) over each segment
 };
 
 // Backward pass: dq, dk, dv (fp32, the shapes of q, k, v), dbeta (zeroed by
-// the caller), dM0, dz0. The workspace's z_pre and mt must hold the forward's
-// fp32 snapshots; dM, dz may be null (zero).
+// the caller), dM0, dz0, for the forward that starts from (M0, z0), whose
+// per-segment states it recomputes into z_pre and mt; dM, dz may be null
+// (zero). R, r, G, qz and H must be zeroed.
 template <typename T>
 hipError_t launch_backward(const Geometry &g, const T *q, const T *k, const T *v, const T *dout,
-                           const float *beta, const float *dM, const float *dz, int delta,
-                           const BwdWorkspace &w, float *dq, float *dk, float *dv, float *dbeta,
-                           float *dM0, float *dz0, hipStream_t stream);
+                           const float *beta, const float *M0, const float *z0, const float *dM,
+                           const float *dz, int delta, const BwdWorkspace &w, float *dq, float *dk,
+                           float *dv, float *dbeta, float *dM0, float *dz0, hipStream_t stream);
 
 // Geometry of one streaming-decode call: C new query rows per (batch, query
 // head) against rows [0, n_past + C) of a K/V cache of cap rows per kv head.

@@ -189,15 +189,4 @@ hipError_t launch_segment_scan_f32(const Geometry &g, const float *k, const floa
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_segment_scan_f32(const Geometry &g, const uint16_t *k, const uint16_t *v,
-                                   float *M, const float *z, int delta, const Workspace &ws,
-                                   hipStream_t stream) {
-  switch (g.D) {
-    case 32: return launch_scan_t<uint16_t, 32>(g, k, v, M, z, delta, ws, stream);
-    case 64: return launch_scan_t<uint16_t, 64>(g, k, v, M, z, delta, ws, stream);
-    case 128: return launch_scan_t<uint16_t, 128>(g, k, v, M, z, delta, ws, stream);
-  }
-  return hipErrorInvalidValue;
-}
-
 }  // namespace ia
