@@ -229,7 +229,7 @@ int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, 
  * tensors run on the bf16 matrix cores, exact in fp32 with fp32 accumulation;
  * the other products run on the fp32 matrix cores. Output buffers must not
  * alias inputs. The
- * handle keeps fp32 scratch of about (B Hq L (d + 3) + 4 B Hkv S d^2) floats,
+ * handle keeps fp32 scratch of about (B Hq L (d + 3) + 5 B Hkv S d^2) floats,
  * grown on demand. dbeta sums atomically, so its last bits may vary from run
  * to run. B = 0 writes dbeta = 0; L = 0 also passes (d_M, d_z) through to
  * (dM0, dz0).
