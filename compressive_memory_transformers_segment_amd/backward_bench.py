@@ -8,7 +8,8 @@ v, beta and (M_0, z_0), taken through every segment in reverse. Shapes: the
 Llama-3-8B attention shape (B = 1, 32 query heads over 8 kv heads, d = 128,
 16 segments of 2048 rows, L = 32768) under both update rules, and the 300M
 LLaMA-like layer (B = 4, 16 heads, d = 64, 8 segments of 2048, L = 16384),
-delta rule; bf16 storage. Inputs are seeded N(0, 1)/sqrt(d) values generated
+delta rule, and the streaming long-context shape (B = 1, 8 heads, d = 128,
+512 segments of 2048, L = 1048576), delta rule; bf16 storage. Inputs are seeded N(0, 1)/sqrt(d) values generated
 on the device, d_out ~ N(0, 1), d_M = d_z = 0, M_0 = 0 and z_0 = 2048 (the
 scale one earlier 2048-row segment leaves).
 
@@ -42,6 +43,7 @@ PEAK_FP32_TFLOPS = 157.3
 SHAPES = {
     "llama3_8b_gqa": dict(B=1, Hq=32, Hkv=8, D=128, N=2048, L=32768, modes=("delta", "linear")),
     "llama300m_16k": dict(B=4, Hq=16, Hkv=16, D=64, N=2048, L=16384, modes=("delta",)),
+    "stream_1m": dict(B=1, Hq=8, Hkv=8, D=128, N=2048, L=1048576, modes=("delta",)),
 }
 
 
