@@ -389,10 +389,62 @@ def pin_p15_backward_finite_differences(ora):
         assert np.all(g[3] == 0.0), "P-15: gradient into an infinite gate"
 
 
+def pin_p16_memory_chain(ora):
+    """The (M, z) recurrence on its own (``memory_chain``, which the full-size
+    state comparisons use as their only reference) equals the token-by-token
+    brute force's final state, and each state it keeps equals the brute
+    force's final state over the rows before that segment; under the linear
+    rule it also equals the closed form sum sig(k)^T v, sum sig(k). Checked on
+    fp64 inputs and on bf16-stored inputs streamed through ``upcast``, with a
+    ragged last segment, under both rules."""
+    from synth import round_bf16_bits, round_fp32
+    shp = dict(B=2, Hq=4, Hkv=2, L=11, dk=3, dv=4)
+    N = 4  # segments of 4, 4, 3
+    for mode in ("linear", "delta"):
+        c = case64(161, scale=1.3, nonzero_state=True, **shp)
+        kb = round_bf16_bits(round_fp32(c["k"]))
+        vb = round_bf16_bits(round_fp32(c["v"]))
+        variants = [("fp64", c["k"], c["v"], None),
+                    ("bf16", kb, vb, lambda a: as_f64(a, "bf16"))]
+        for tag, k, v, up in variants:
+            kf = c["k"] if up is None else as_f64(kb, "bf16")
+            vf = c["v"] if up is None else as_f64(vb, "bf16")
+            _, bM, bz = ind.brute_force(c["q"], kf, vf, c["beta"], c["M0"], c["z0"], N, mode,
+                                        c["eps"])
+            for b in range(shp["B"]):
+                for j in range(shp["Hkv"]):
+                    M, z, states = ora.memory_chain(k[b, j], v[b, j], c["M0"][b, j],
+                                                    c["z0"][b, j], N, mode, c["eps"],
+                                                    keep_states=True, upcast=up)
+                    what = f"P-16 {mode} {tag} b{b} j{j}"
+                    close(M, bM[b, j], rtol=1e-11, atol=1e-12, what=f"{what} M_S")
+                    close(z, bz[b, j], rtol=1e-13, atol=1e-13, what=f"{what} z_S")
+                    if mode == "linear":
+                        sk = np.where(kf[b, j] > 0, kf[b, j] + 1.0,
+                                      np.exp(np.minimum(kf[b, j], 0.0)))
+                        close(M, c["M0"][b, j] + sk.T @ vf[b, j], rtol=1e-12, atol=1e-12,
+                              what=f"{what} closed-form M")
+                        close(z, c["z0"][b, j] + sk.sum(axis=0), rtol=1e-13, atol=1e-13,
+                              what=f"{what} closed-form z")
+                    starts = list(range(0, shp["L"], N))
+                    assert len(states) == len(starts), f"{what}: {len(states)} states"
+                    for s, a in enumerate(starts):
+                        if a == 0:
+                            pM, pz = c["M0"][b, j], c["z0"][b, j]
+                        else:
+                            sub = dict(q=c["q"][:, :, :a], k=kf[:, :, :a], v=vf[:, :, :a])
+                            _, pMs, pzs = ind.brute_force(sub["q"], sub["k"], sub["v"],
+                                                          c["beta"], c["M0"], c["z0"], N, mode,
+                                                          c["eps"])
+                            pM, pz = pMs[b, j], pzs[b, j]
+                        close(states[s][0], pM, rtol=1e-11, atol=1e-12, what=f"{what} M_{s-1}")
+                        close(states[s][1], pz, rtol=1e-13, atol=1e-13, what=f"{what} z_{s-1}")
+
+
 ALL_PINS = [
     pin_sigma_library, pin_gate_library, pin_golden, pin_p1_sdpa, pin_p2_dense_linear,
     pin_p3_linear_closed_form, pin_p4_zero_start, pin_p5_delta_fixed_point, pin_p6_exact,
     pin_p7_brute_force, pin_p8_gqa, pin_p9_split_calls, pin_p10_structure,
     pin_p11_unit_segments, pin_p12_delta_affine, pin_p13_streaming,
-    pin_p14_block, pin_p15_backward_finite_differences,
+    pin_p14_block, pin_p15_backward_finite_differences, pin_p16_memory_chain,
 ]

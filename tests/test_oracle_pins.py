@@ -22,7 +22,8 @@ _orig = {n: getattr(ref, n) for n in ("elu_plus_one", "gate_value", "kv_head_of"
                                        "local_causal_attention", "memory_retrieval",
                                        "memory_update", "infini_attention",
                                        "streaming_decode", "infini_block",
-                                       "infini_attention_backward", "_elu_plus_one_grad")}
+                                       "infini_attention_backward", "_elu_plus_one_grad",
+                                       "memory_chain")}
 
 
 def _retrieval_no_eps(qs, M, z, eps):
@@ -169,6 +170,23 @@ def _backward_with(old, new):
     return ns["infini_attention_backward"]
 
 
+def _chain_with(old, new):
+    """The oracle's memory_chain with one line of its source replaced."""
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(_orig["memory_chain"]))
+    assert src.count(old) == 1, old
+    ns = dict(vars(ref))
+    exec(compile(src.replace(old, new), "<planted>", "exec"), ns)
+    return ns["memory_chain"]
+
+
+def _chain_pre_last_state(k, v, M0, z0, seg_len, mode, eps=1e-6, keep_states=False, upcast=None):
+    """Returns the state before the last segment instead of after it."""
+    M, z, states = _orig["memory_chain"](k, v, M0, z0, seg_len, mode, eps, True, upcast)
+    return states[-1][0], states[-1][1], (states if keep_states else None)
+
+
 MUTANTS = {
     "no_eps_retrieval": ("memory_retrieval", _retrieval_no_eps),
     "sigma_on_scaled_q": ("memory_retrieval", _retrieval_scaled_q),
@@ -195,6 +213,13 @@ MUTANTS = {
         "dden = -np.sum(dAm * num, axis=1) / den ** 2", "dden = 0.0 * den")),
     "backward_drops_z_carry": ("infini_attention_backward", _backward_with(
         "gMp, gzp = gM.copy(), gz.copy()", "gMp, gzp = gM.copy(), np.zeros_like(gz)")),
+    "chain_returns_pre_last_state": ("memory_chain", _chain_pre_last_state),
+    "chain_keeps_states_after_update": ("memory_chain", _chain_with(
+        "M, z = memory_update(ks, vs, M, z, mode, eps)",
+        "M, z = memory_update(ks, vs, M, z, mode, eps)\n        if keep_states:\n"
+        "            states[-1] = (M.copy(), z.copy())")),
+    "chain_skips_last_segment": ("memory_chain", _chain_with(
+        "for (a, e) in segment_bounds(L, seg_len):", "for (a, e) in segment_bounds(L, seg_len)[:-1]:")),
 }
 
 
