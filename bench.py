@@ -13,7 +13,6 @@ heads, d=128, segments of 2048 rows, L=32768, bf16 storage).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -25,11 +24,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "Infini-attn fwd tokens/sec on 1 MI355X; % MFMA bf16 peak; HBM GB/s"
-PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 bf16 FLOP/clk x 2.4 GHz (dense)
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 bf16 FLOP/clk x 2.4 GHz (dense MFMA)
+PEAK_F32_VALU_TFLOPS = 157.3  # published fp32 vector peak (packed FMA, 256 CU at 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_bf16_llama3_8b_gqa_traffic.txt")
-FUSED_SRC = os.path.join(ROOT, "compressive_memory_transformers_segment_amd", "csrc",
-                         "fused_bf16.hip")
 
 
 def log(msg: str) -> None:
@@ -66,23 +63,37 @@ def work_counts(w, mode: str) -> dict:
                 bytes=qo + kv + state, fused_bytes=qo + kv)
 
 
-def stored_traffic(fused_launch_bytes: float):
-    """HBM traffic of the fused kernel from committed rocprofv3 counter runs,
-    or None when the counters were taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    kv = {}
-    for line in open(TRAFFIC_FILE):
-        if "=" in line and not line.lstrip().startswith("#"):
-            a, b = line.split("=", 1)
-            kv[a.strip()] = b.strip()
-    src_hash = hashlib.sha256(open(FUSED_SRC, "rb").read()).hexdigest()[:16]
-    if kv.get("kernel_source_sha256_16") != src_hash:
-        return None
+def fused_kernel_name(w) -> str:
+    if w.dtype != "bf16":
+        return f"fused_f32_kernel<{w.d}>"
+    g = w.n_q_heads // w.n_kv_heads
+    return f"fused_bf16_kernel<{w.d}, {4 if g % 4 == 0 else 2 if g % 2 == 0 else 1}>"
+
+
+def host_info() -> dict:
+    """CPU model, BLAS library and its thread count on this host."""
+    import numpy as np
+    model = "unknown"
     try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    a = np.ones((64, 64))
+    _ = a @ a  # loads the BLAS library so that threadpoolctl sees it
+    blas, threads = "unknown", 1
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            blas = f"{infos[0].get('internal_api')} {infos[0].get('version')}"
+            threads = max(i.get("num_threads", 1) for i in infos)
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cpu_model": model, "blas": blas, "blas_threads": threads,
+            "cpus_visible": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline(w, inp, mode: str, budget_s: float) -> dict:
@@ -93,12 +104,7 @@ def cpu_baseline(w, inp, mode: str, budget_s: float) -> dict:
     import oracle
     import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                            if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        blas_threads = 1
+    info = host_info()
     N = w.seg_len
 
     def run(n_seg: int) -> float:
@@ -114,15 +120,23 @@ def cpu_baseline(w, inp, mode: str, budget_s: float) -> dict:
 
     t1 = run(1)
     n = max(1, min(w.n_segments, int(budget_s / max(t1, 1e-3))))
+    reps = 1
     if n > 1:
         t = run(n)
     else:
         n, t = 1, t1
+    if n == w.n_segments and t < 0.5 * budget_s:
+        # The whole workload is a short sample: repeat it to fill the budget.
+        reps = max(1, int(budget_s / max(t, 1e-4)))
+        t = sum(run(n) for _ in range(reps))
     tokens = w.batch * min(n * N, w.seq_len)
-    return {"value": tokens / t, "unit": "tokens/s", "cores": blas_threads, "kind": "oracle",
+    return {"value": reps * tokens / t, "unit": "tokens/s", "cores": info["blas_threads"],
+            "kind": "oracle",
             "sample": f"first {n} of {w.n_segments} segments ({tokens} tokens, all "
-                      f"{w.batch * w.n_q_heads} query heads), {mode} rule, fp64 numpy; "
-                      f"{t:.2f} s; host cpus visible: {len(os.sched_getaffinity(0))}"}
+                      f"{w.batch * w.n_q_heads} query heads) x {reps}, {mode} rule, "
+                      f"fp64 numpy; {t:.2f} s",
+            "cpu_model": info["cpu_model"], "blas": info["blas"],
+            "cpus_visible": info["cpus_visible"]}
 
 
 def main(argv=None) -> int:
@@ -153,9 +167,9 @@ def main(argv=None) -> int:
     import compressive_memory_transformers_segment_amd as ia
     import synth
 
+    from compressive_memory_transformers_segment_amd import traffic as traffic_mod
+
     w = synth.WORKLOADS[args.workload]
-    if w.dtype != "bf16":
-        log("note: fp32 workload; roofline is still quoted against the bf16 MFMA peak")
     ia.load()
     log(f"generating {w.describe()}")
     t0 = time.perf_counter()
@@ -171,23 +185,33 @@ def main(argv=None) -> int:
 
     q, k, v = up(inp["q"]), up(inp["k"]), up(inp["v"])
     beta = torch.from_numpy(inp["beta"]).to(dev)
-    M = torch.from_numpy(inp["M0"]).to(dev)
-    z = torch.from_numpy(inp["z0"]).to(dev)
+    M0 = torch.from_numpy(inp["M0"]).to(dev)
+    z0 = torch.from_numpy(inp["z0"]).to(dev)
+    M, z = M0.clone(), z0.clone()
     out = torch.empty((w.batch, w.n_q_heads, w.seq_len, w.d), dtype=q.dtype, device=dev)
     h = ia.handle_for(q, k, w.eps)
+    n_ev = args.warmup + args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_ev)]
 
-    def step():
+    def step(i):
+        # Every step starts from the workload's initial state (reset outside the
+        # events); the events bracket the forward call on the stream it runs on.
+        M.copy_(M0)
+        z.copy_(z0)
+        ev[i][0].record()
         ia.forward(q, k, v, beta, M, z, w.seg_len, args.mode, out=out, eps=w.eps)
+        ev[i][1].record()
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     ia.infini_attn_set_timing(h, True)
     ia.infini_attn_get_timing(h)  # clear
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.warmup, n_ev):
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     calls, scan_ms, fused_ms = ia.infini_attn_get_timing(h)
@@ -196,22 +220,37 @@ def main(argv=None) -> int:
     if not bool(torch.isfinite(out.float()).all()):
         log("ERROR: non-finite output")
         return 1
+    step_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, n_ev))
+    med_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
 
     wc = work_counts(w, args.mode)
-    ms_step = elapsed * 1e3 / args.steps
     tokens = w.batch * w.seq_len
     fused_avg_s = fused_ms / calls / 1e3
     scan_avg_s = scan_ms / calls / 1e3
     achieved = wc["fused_flops"] / fused_avg_s / 1e12
-    traffic = stored_traffic(wc["fused_bytes"])
+    kname = fused_kernel_name(w)
+    counted = traffic_mod.load(w.name, args.mode)
+    kernel_traffic = None
+    hbm_counters = None
+    traffic_ratio = None
+    if counted is not None:
+        if kname in counted:
+            kernel_traffic = counted[kname]["fetch"] + counted[kname]["write"]
+        pass_bytes = sum(c["fetch"] + c["write"] for c in counted.values())
+        hbm_counters = pass_bytes / (med_ms / 1e3) / 1e9
+        traffic_ratio = pass_bytes / wc["bytes"]
+    bf16 = w.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_VALU_TFLOPS
+    tflops = wc["total_flops"] / (med_ms / 1e3) / 1e12
     result = {
         "metric": METRIC,
-        "value": tokens * args.steps / elapsed,
+        "value": tokens / (med_ms / 1e3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": med_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -220,20 +259,23 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "d": w.d, "seg_len": w.seg_len,
                    "seq_len": w.seq_len, "segments": w.n_segments, "update": args.mode},
-        "tflops_algorithmic": wc["total_flops"] * args.steps / elapsed / 1e12,
-        "mfma_bf16_peak_frac": wc["total_flops"] * args.steps / elapsed / 1e12 / PEAK_BF16_TFLOPS,
-        "hbm_gbs_algorithmic": wc["bytes"] * args.steps / elapsed / 1e9,
+        "timing": {"ms_per_step_median": med_ms, "ms_per_step_min": step_ms[0],
+                   "ms_per_step_max": step_ms[-1],
+                   "wall_ms_per_step_with_state_reset": elapsed * 1e3 / args.steps},
+        "tflops_algorithmic": tflops,
+        "mfma_bf16_peak_frac": tflops / PEAK_BF16_TFLOPS,
+        "hbm_gbs_algorithmic": wc["bytes"] / (med_ms / 1e3) / 1e9,
+        "hbm_gbs_counters": hbm_counters,
+        "hbm_traffic_over_algorithmic": traffic_ratio,
         "kernels_ms": {"segment_scan": scan_avg_s * 1e3, "fused_attention": fused_avg_s * 1e3},
         "roofline": {
-            "kernel": (f"fused_bf16_kernel<{w.d}, "
-                       f"{4 if (w.n_q_heads // w.n_kv_heads) % 4 == 0 else 2 if (w.n_q_heads // w.n_kv_heads) % 2 == 0 else 1}>"
-                       if w.dtype == "bf16" else f"fused_f32_kernel<{w.d}>"),
-            "bound": "mfma",
+            "kernel": kname,
+            "bound": "mfma" if bf16 else "alu",
             "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": traffic,
+            "frac": achieved / peak,
+            "traffic": kernel_traffic,
             "flops_per_launch": wc["fused_flops"],
         },
     }

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
     const T *__restrict__ dout, const float *__restrict__ beta, const float *__restrict__ mt,
     const float *__restrict__ zpre, int Hq, int Hkv, int L, int N, int S, float eps,
     float *__restrict__ dq, float *__restrict__ lse_out, float *__restrict__ e_out,
-    float *__restrict__ dnum_out, float *__restrict__ dden_out, float *__restrict__ dbeta) {
+    float *__restrict__ dnum_out, float *__restrict__ dden_out, float *__restrict__ dbeta_part) {
   constexpr int P = D + 1;
   constexpr int NB = D / 32;  // 32-wide blocks along d
   constexpr int QT = 128;
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   __shared__ __attribute__((aligned(16))) uint16_t sKb[BF ? kKT : 1][PB];  // bf16 key tile
   __shared__ __attribute__((aligned(16))) uint16_t sVb[BF ? kKT : 1][PB];
   __shared__ float sZ[D];
-  __shared__ float sAcc;
+  __shared__ float sAcc[kThreads / 64];
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -210,7 +210,15 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   const size_t kvh = static_cast<size_t>(b) * Hkv + h / grp;
   const int a = s * N, e = min(a + N, L);
   const int i0 = a + blockIdx.x * QT;
-  if (i0 >= e) return;
+  // This block's slot of the gate gradient's partial sums (summed in a fixed
+  // order afterwards): head h, then (b, s, row block).
+  float *dbeta_slot =
+      dbeta_part + static_cast<size_t>(h) * (static_cast<size_t>(gridDim.z / Hq) * S * gridDim.x) +
+      (static_cast<size_t>(b) * S + s) * gridDim.x + blockIdx.x;
+  if (i0 >= e) {
+    if (t == 0) *dbeta_slot = 0.f;
+    return;
+  }
   const int kend = min(i0 + QT, e);  // keys this tile's rows can see: [a, kend)
   const int wq0 = i0 + 32 * w;       // this wave's first query row
   const bool wave_live = wq0 < e;
@@ -221,7 +229,6 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   const size_t qbase = static_cast<size_t>(bh) * L;
   const T *kb = k + kvh * L * D;
   const T *vb = v + kvh * L * D;
-  if (t == 0) sAcc = 0.f;
   for (int c = t; c < D; c += kThreads) sZ[c] = zpre[(kvh * (S + 1) + s) * D + c];
 
   // This lane's query row and d_out row as B operands: element 2 u + g (fp32
@@ -429,10 +436,19 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
       }
   }
   // d beta: sum over rows of dO . (A_mem - A_dot), times g (1 - g).
-  const float contrib = (qvalid && g == 0) ? s1 / den - E : 0.f;
-  if (contrib != 0.f) atomicAdd(&sAcc, contrib);
+  // Summed in a fixed order: a butterfly within the wave, then the waves in
+  // index order, so the result does not depend on timing.
+  float contrib = (qvalid && g == 0) ? s1 / den - E : 0.f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) contrib += __shfl_xor(contrib, o);
+  if (lane == 0) sAcc[w] = contrib;
   __syncthreads();
-  if (t == 0) atomicAdd(dbeta + h, sAcc * gam * (1.f - gam));
+  if (t == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) tot += sAcc[i];
+    *dbeta_slot = tot * gam * (1.f - gam);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -596,12 +612,14 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
 //               A = sigma(q), B = dnum; r_s = sum A^T dden as well.
 //   kind 1 (G): rows = rows of the segment, A = sigma(k), B = sigma(k) / denk.
 //   kind 2 (H): rows = rows of the segment, A = sigma(k), B = v (x2).
-// out must be zeroed first; the row ranges of one unit add atomically.
+// Each block writes the partial sum of its row range, D x D floats and then
+// (kind 0) D floats of r, to part[unit][block]; bwd_sum_parts_kernel adds the
+// blocks of a unit in index order, so the result does not depend on timing.
 template <typename T, int D, int KIND>
 __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
     const T *__restrict__ x, const T *__restrict__ x2, const float *__restrict__ dnum,
     const float *__restrict__ dden, const float *__restrict__ zpre, int Hq, int Hkv, int L, int N,
-    int S, float eps, int rows_per_block, float *__restrict__ out, float *__restrict__ rvec) {
+    int S, float eps, int rows_per_block, float *__restrict__ part) {
   constexpr int P = D + 1;
   constexpr int MI = D / 16;
   __shared__ float sA[kKT][P];
@@ -617,7 +635,13 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
   const int total = KIND == 0 ? grp * n : n;
   const int u0 = blockIdx.x * rows_per_block;
   const int u1 = min(u0 + rows_per_block, total);
-  if (u0 >= u1) return;
+  constexpr int kPart = D * D + (KIND == 0 ? D : 0);  // floats of one block's partial
+  const size_t unit = static_cast<size_t>(kvh) * S + s;
+  float *o = part + (unit * gridDim.x + blockIdx.x) * kPart;
+  if (u0 >= u1) {  // no rows (short last segment): a zero partial
+    for (int i = t; i < kPart; i += kThreads) o[i] = 0.f;
+    return;
+  }
   if (KIND == 1)
     for (int c = t; c < D; c += kThreads) sZ[c] = zpre[(static_cast<size_t>(kvh) * (S + 1) + s) * D + c];
 
@@ -665,13 +689,30 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
         for (int kk = 0; kk < kKT; ++kk) racc += sA[kk][t] * sX[kk];
     }
   }
-  const size_t unit = static_cast<size_t>(kvh) * S + s;
-  float *o = out + unit * D * D;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < MI; ++jj) atomicAdd(o + (r0 + 16 * i) * D + c0 + 16 * jj, acc[i][jj]);
-  if (KIND == 0 && t < D) atomicAdd(rvec + unit * D + t, racc);
+    for (int jj = 0; jj < MI; ++jj) o[(r0 + 16 * i) * D + c0 + 16 * jj] = acc[i][jj];
+  if (KIND == 0 && t < D) o[D * D + t] = racc;
+}
+
+// out_mat[u][i] (i < mat) and out_vec[u][i - mat] (mat <= i < mat + vec) =
+// sum over b = 0 .. nblk - 1, in that order, of part[u][b][i].
+// Grid: (units, ceil((mat + vec) / kThreads)).
+__global__ __launch_bounds__(kThreads) void bwd_sum_parts_kernel(
+    const float *__restrict__ part, int nblk, int mat, int vec, float *__restrict__ out_mat,
+    float *__restrict__ out_vec) {
+  const int i = blockIdx.y * kThreads + threadIdx.x;
+  const int per = mat + vec;
+  if (i >= per) return;
+  const size_t u = blockIdx.x;
+  const float *p = part + u * nblk * static_cast<size_t>(per) + i;
+  float acc = 0.f;
+  for (int b = 0; b < nblk; ++b) acc += p[static_cast<size_t>(b) * per];
+  if (i < mat)
+    out_mat[u * mat + i] = acc;
+  else
+    out_vec[u * vec + (i - mat)] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -791,7 +832,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_update_kernel(
     const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ mt,
     const float *__restrict__ zpre, const float *__restrict__ gma, int L, int N, int S, float eps,
-    int delta, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ qz) {
+    int delta, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ qz_part) {
   constexpr int P = D + 1;
   constexpr int NJ = D / 16;
   __shared__ float sK[kKT][P];  // sigma(k)
@@ -805,10 +846,16 @@ __global__ __launch_bounds__(kThreads) void bwd_update_kernel(
   const int s = blockIdx.y, kvh = blockIdx.z;
   const int a = s * N, e = min(a + N, L);
   const int i0 = a + blockIdx.x * kKT;
-  if (i0 >= e) return;
+  const size_t unit = static_cast<size_t>(kvh) * S + s;
+  // This chunk's partial of qz_s (delta rule), summed in chunk order later.
+  float *qzp = qz_part + (unit * gridDim.x + blockIdx.x) * D;
+  if (i0 >= e) {
+    if (delta)
+      for (int c = t; c < D; c += kThreads) qzp[c] = 0.f;
+    return;
+  }
   const int rows = min(kKT, e - i0);
   const size_t row0 = static_cast<size_t>(kvh) * L + i0;
-  const size_t unit = static_cast<size_t>(kvh) * S + s;
   const float *gm = gma + unit * D * D;
   const float *mtp = mt + unit * D * D;
   load_rows<T, D, P>(sK, k + row0 * D, kKT, rows, true);
@@ -875,7 +922,7 @@ __global__ __launch_bounds__(kThreads) void bwd_update_kernel(
     if (t < D) {
       float acc = 0.f;
       for (int r = 0; r < kKT; ++r) acc += sK[r][t] * sDd[r];
-      atomicAdd(qz + unit * D + t, acc);
+      qzp[t] = acc;
     }
   }
 
@@ -950,6 +997,17 @@ __global__ void bwd_dk_gz_kernel(const T *__restrict__ k, const float *__restric
   dk[idx] += gza[(kvh * S + s) * D + c] * sg;
 }
 
+// Sum the per-block partials of `units` units in block order (see
+// bwd_sum_parts_kernel).
+hipError_t sum_parts(const float *part, size_t units, int nblk, int mat, int vec, float *out_mat,
+                     float *out_vec, hipStream_t st) {
+  if (units == 0) return hipSuccess;
+  if (units > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(units), (mat + vec + kThreads - 1) / kThreads);
+  bwd_sum_parts_kernel<<<grid, kThreads, 0, st>>>(part, nblk, mat, vec, out_mat, out_vec);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, const T *dout,
                         const float *beta, const float *M0, const float *z0, const float *dM,
@@ -957,7 +1015,10 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
                         float *dv, float *dbeta, float *dM0, float *dz0, hipStream_t st) {
   const int grp = g.Hq / g.Hkv;
   const int kvheads = g.B * g.Hkv;
-  const int rows_r = 1024;
+  const size_t units = static_cast<size_t>(kvheads) * g.S;
+  const BwdBlocks nb = backward_blocks(g);
+  if ((static_cast<long long>(grp) * g.N + nb.rows_per - 1) / nb.rows_per > 0x7fffffffLL)
+    return hipErrorInvalidConfiguration;
   // The forward's state before every segment: z prefix, then G_s (delta) and
   // H_s in parallel, then the d x d chain.
   bwd_zsum_kernel<T, D><<<dim3(g.S, kvheads), kThreads, 0, st>>>(k, g.L, g.N, g.S, w.dzs);
@@ -966,35 +1027,43 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
   bwd_zprefix_kernel<<<kvheads, D, 0, st>>>(w.dzs, z0, g.S, D, w.z_pre);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (delta) {
-    bwd_outer_kernel<T, D, 1><<<dim3((g.N + rows_r - 1) / rows_r, g.S, kvheads), kThreads, 0,
-                                st>>>(k, nullptr, nullptr, nullptr, w.z_pre, g.Hq, g.Hkv, g.L, g.N,
-                                      g.S, g.eps, rows_r, w.G, nullptr);
+    bwd_outer_kernel<T, D, 1><<<dim3(nb.rows, g.S, kvheads), kThreads, 0, st>>>(
+        k, nullptr, nullptr, nullptr, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, nb.rows_per,
+        w.part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = sum_parts(w.part, units, nb.rows, D * D, 0, w.G, nullptr, st)) != hipSuccess)
+      return e;
   }
-  bwd_outer_kernel<T, D, 2><<<dim3((g.N + rows_r - 1) / rows_r, g.S, kvheads), kThreads, 0,
-                              st>>>(k, v, nullptr, nullptr, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S,
-                                    g.eps, rows_r, w.H, nullptr);
+  bwd_outer_kernel<T, D, 2><<<dim3(nb.rows, g.S, kvheads), kThreads, 0, st>>>(
+      k, v, nullptr, nullptr, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, nb.rows_per, w.part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = sum_parts(w.part, units, nb.rows, D * D, 0, w.H, nullptr, st)) != hipSuccess) return e;
   bwd_gm_chain_kernel<D, true><<<dim3(D / kKT, kvheads), kThreads, 0, st>>>(w.H, w.G, M0, g.S,
                                                                            delta, w.mt, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_query_kernel<T, D><<<dim3((g.N + 127) / 128, g.S, g.B * g.Hq), kThreads, 0, st>>>(
+  bwd_query_kernel<T, D><<<dim3(nb.qblocks, g.S, g.B * g.Hq), kThreads, 0, st>>>(
       q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
-      w.dnum, w.dden, dbeta);
+      w.dnum, w.dden, w.dbeta_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_key_kernel<T, D><<<dim3((g.N + 127) / 128, g.S, kvheads), kThreads, 0, st>>>(
+  if ((e = sum_parts(w.dbeta_part, g.Hq, g.B * g.S * nb.qblocks, 1, 0, dbeta, nullptr, st)) !=
+      hipSuccess)
+    return e;
+  bwd_key_kernel<T, D><<<dim3(nb.qblocks, g.S, kvheads), kThreads, 0, st>>>(
       q, k, v, dout, beta, w.lse, w.erow, g.Hq, g.Hkv, g.L, g.N, dk, dv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_outer_kernel<T, D, 0><<<dim3((grp * g.N + rows_r - 1) / rows_r, g.S, kvheads), kThreads, 0,
-                              st>>>(q, nullptr, w.dnum, w.dden, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S,
-                                    g.eps, rows_r, w.R, w.r);
+  bwd_outer_kernel<T, D, 0><<<dim3(nb.group_rows, g.S, kvheads), kThreads, 0, st>>>(
+      q, nullptr, w.dnum, w.dden, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, nb.rows_per, w.part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = sum_parts(w.part, units, nb.group_rows, D * D, D, w.R, w.r, st)) != hipSuccess)
+    return e;
   bwd_gm_chain_kernel<D, false><<<dim3(D / kKT, kvheads), kThreads, 0, st>>>(w.R, w.G, dM, g.S, delta,
                                                                       w.gma, dM0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_update_kernel<T, D><<<dim3((g.N + kKT - 1) / kKT, g.S, kvheads), kThreads, 0, st>>>(
-      k, v, w.mt, w.z_pre, w.gma, g.L, g.N, g.S, g.eps, delta, dk, dv, w.qz);
+  bwd_update_kernel<T, D><<<dim3(nb.chunks, g.S, kvheads), kThreads, 0, st>>>(
+      k, v, w.mt, w.z_pre, w.gma, g.L, g.N, g.S, g.eps, delta, dk, dv, w.qz_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (delta && (e = sum_parts(w.qz_part, units, nb.chunks, D, 0, w.qz, nullptr, st)) != hipSuccess)
+    return e;
   bwd_gz_chain_kernel<<<kvheads, D, 0, st>>>(w.r, w.qz, dz, g.S, D, w.gza, dz0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t total = static_cast<size_t>(kvheads) * g.L * D;
@@ -1005,6 +1074,17 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
 }
 
 }  // namespace
+
+BwdBlocks backward_blocks(const Geometry &g) {
+  BwdBlocks nb;
+  nb.rows_per = 1024;
+  nb.rows = (g.N + nb.rows_per - 1) / nb.rows_per;
+  nb.group_rows = static_cast<int>(
+      (static_cast<long long>(g.Hq / g.Hkv) * g.N + nb.rows_per - 1) / nb.rows_per);
+  nb.qblocks = (g.N + 127) / 128;
+  nb.chunks = (g.N + kKT - 1) / kKT;
+  return nb;
+}
 
 template <typename T>
 hipError_t launch_backward(const Geometry &g, const T *q, const T *k, const T *v, const T *dout,

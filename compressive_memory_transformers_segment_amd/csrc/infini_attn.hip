@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -61,12 +62,19 @@ int check_desc(const infini_attn_desc *d) {
   if (d->d_k != d->d_v) return INFINI_ATTN_ERR_UNSUPPORTED;
   if (d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return INFINI_ATTN_ERR_UNSUPPORTED;
   // Every tensor is addressed with 64-bit offsets, but grid dimensions are
-  // limited: B * Hq blocks along one axis.
+  // limited: B * Hq blocks along one axis. Rows per call stay below 2^30, so
+  // that row counts rounded up to a tile in 32-bit arithmetic cannot overflow.
   if (static_cast<int64_t>(d->batch) * d->n_q_heads > 65535) return INFINI_ATTN_ERR_UNSUPPORTED;
+  if (d->seq_len > (1 << 30)) return INFINI_ATTN_ERR_UNSUPPORTED;
   return INFINI_ATTN_OK;
 }
 
 int n_segments(int L, int N) { return L == 0 ? 0 : (L + N - 1) / N; }
+
+// Segment length the kernels see: a segment never holds more rows than the
+// call has, so seg_len >= L is one segment of L rows (the same result), and
+// workspace and grids are sized by rows that exist.
+int effective_seg(int L, int seg_len) { return (L > 0 && seg_len > L) ? L : seg_len; }
 
 // Workspace layout (each part 256-byte aligned), in this order:
 //   z_pre  [B*Hkv][S+1][D] fp32   (slot S receives the final z)
@@ -198,7 +206,8 @@ int infini_attn_workspace_size(const infini_attn_desc *desc, int32_t seg_len, si
   if (!bytes) return INFINI_ATTN_ERR_INVALID;
   const int st = infini_attn_check(desc, seg_len, INFINI_ATTN_LINEAR);
   if (st != INFINI_ATTN_OK) return st;
-  *bytes = ws_layout(desc, n_segments(desc->seq_len, seg_len), seg_len).total;
+  const int N = effective_seg(desc->seq_len, seg_len);
+  *bytes = ws_layout(desc, n_segments(desc->seq_len, N), N).total;
   return INFINI_ATTN_OK;
 }
 
@@ -252,8 +261,8 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
   g.Hkv = d.n_kv_heads;
   g.L = d.seq_len;
   g.D = d.d_k;
-  g.N = seg_len;
-  g.S = n_segments(d.seq_len, seg_len);
+  g.N = effective_seg(d.seq_len, seg_len);
+  g.S = n_segments(d.seq_len, g.N);
   g.eps = d.eps;
 
   ia::Workspace ws;
@@ -501,30 +510,38 @@ int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const v
   g.Hkv = d.n_kv_heads;
   g.L = d.seq_len;
   g.D = d.d_k;
-  g.N = seg_len;
-  g.S = n_segments(d.seq_len, seg_len);
+  g.N = effective_seg(d.seq_len, seg_len);
+  g.S = n_segments(d.seq_len, g.N);
   g.eps = d.eps;
   const int delta = update_mode == INFINI_ATTN_DELTA;
 
   // Scratch layout (each part 256-byte aligned): z_pre, mt, dzs, lse, erow,
-  // dnum, dden, R, r, G (delta only), qz, H, gma, gza.
+  // dnum, dden, R, r, G (delta only), qz, H, gma, gza, and the per-block
+  // partial sums (products, qz, dbeta).
   const size_t units = kvheads * g.S;
   const size_t qrows = static_cast<size_t>(g.B) * g.Hq * g.L;
-  const size_t sz[14] = {
+  const ia::BwdBlocks nb = ia::backward_blocks(g);
+  const size_t part_floats =
+      units * std::max(static_cast<size_t>(nb.rows) * D * D,
+                       static_cast<size_t>(nb.group_rows) * (D * D + D));
+  const size_t sz[17] = {
       round_up(kvheads * (g.S + 1) * D * sizeof(float)), round_up(units * D * D * sizeof(float)),
       round_up(units * D * sizeof(float)), round_up(qrows * sizeof(float)),
       round_up(qrows * sizeof(float)), round_up(qrows * D * sizeof(float)),
       round_up(qrows * sizeof(float)), round_up(units * D * D * sizeof(float)),
       round_up(units * D * sizeof(float)), delta ? round_up(units * D * D * sizeof(float)) : 0,
       round_up(units * D * sizeof(float)), round_up(units * D * D * sizeof(float)),
-      round_up(units * D * D * sizeof(float)), round_up(units * D * sizeof(float))};
+      round_up(units * D * D * sizeof(float)), round_up(units * D * sizeof(float)),
+      round_up(part_floats * sizeof(float)),
+      round_up(units * nb.chunks * D * sizeof(float)),
+      round_up(static_cast<size_t>(g.Hq) * g.B * g.S * nb.qblocks * sizeof(float))};
   size_t total = 0;
   for (size_t x : sz) total += x;
   st = ensure_buffer(&h->bwd_ws, &h->bwd_ws_bytes, total);
   if (st != INFINI_ATTN_OK) return st;
-  float *part[14];
+  float *part[17];
   char *base = static_cast<char *>(h->bwd_ws);
-  for (int i = 0; i < 14; ++i) {
+  for (int i = 0; i < 17; ++i) {
     part[i] = reinterpret_cast<float *>(base);
     base += sz[i];
   }
@@ -543,10 +560,16 @@ int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const v
   w.H = part[11];
   w.gma = part[12];
   w.gza = part[13];
+  w.part = part[14];
+  w.qz_part = part[15];
+  w.dbeta_part = part[16];
 
-  // The zeroed accumulators (R, r, G, qz, H) are contiguous.
-  e = hipMemsetAsync(w.R, 0, sz[7] + sz[8] + sz[9] + sz[10] + sz[11], stream);
-  if (e != hipSuccess) return hip_status(e);
+  // R, r, G, H, qz (delta) and dbeta are written whole by the ordered sums of
+  // their partials; the linear rule has no qz term.
+  if (!delta) {
+    e = hipMemsetAsync(w.qz, 0, sz[10], stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
   if (d.dtype == INFINI_ATTN_BF16) {
     const uint16_t *qb = static_cast<const uint16_t *>(q), *kb = static_cast<const uint16_t *>(k),
                    *vb = static_cast<const uint16_t *>(v),

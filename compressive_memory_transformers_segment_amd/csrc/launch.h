@@ -79,7 +79,21 @@ struct BwdWorkspace {
   float *gza;    // [units][D] gradient of z after each segment
   float *H;      // [units][D][D] sigma(k)^T v of each segment (zeroed)
   float *dzs;    // [units][D] column sums of sigma(k) over each segment
+  // Per-block partial sums, added in a fixed order so that every gradient is
+  // the same from run to run:
+  float *part;        // [units][blocks][D*D (+ D)] of the G, H and R, r products
+  float *qz_part;     // [units][chunks][D] of qz (delta rule)
+  float *dbeta_part;  // [Hq][B][S][qblocks] of dbeta
 };
+
+// Blocks per unit of the backward's kernels (see backward.hip), which size the
+// partial-sum scratch: rows_per rows per block of the G and H products (rows
+// of them), of the R product (group_rows of them, over every query head of the
+// group), 128-row query blocks, and 32-row chunks of the update's gradient.
+struct BwdBlocks {
+  int rows_per, rows, group_rows, qblocks, chunks;
+};
+BwdBlocks backward_blocks(const Geometry &g);
 
 // Backward pass: dq, dk, dv (fp32, the shapes of q, k, v), dbeta (zeroed by
 // the caller), dM0, dz0, for the forward that starts from (M0, z0), whose

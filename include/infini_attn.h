@@ -65,7 +65,7 @@ typedef struct infini_attn_desc {
   int32_t batch;      /* B >= 1 */
   int32_t n_q_heads;  /* Hq >= 1, a multiple of n_kv_heads */
   int32_t n_kv_heads; /* Hkv >= 1; query head h reads kv head h / (Hq / Hkv) */
-  int32_t seq_len;    /* L >= 1 rows per call */
+  int32_t seq_len;    /* L rows per call, 0 .. 2^30 (larger: ERR_UNSUPPORTED) */
   int32_t d_k;        /* key / query width; supported: 32, 64, 128 */
   int32_t d_v;        /* value width; this build requires d_v == d_k */
   int32_t dtype;      /* INFINI_ATTN_F32 or INFINI_ATTN_BF16 */
@@ -111,7 +111,9 @@ int infini_attn_create(infini_attn_t **h, const infini_attn_desc *desc);
  *   beta [Hq]              fp32, one gate parameter per query head (device)
  *   M    [B, Hkv, d_k, d_v] fp32 in/out (device): M_0 on entry, M_S on exit
  *   z    [B, Hkv, d_k]      fp32 in/out (device): z_0 on entry, z_S on exit
- *   seg_len     >= 1 rows per segment; S = ceil(L / seg_len) segments
+ *   seg_len     >= 1 rows per segment; S = ceil(L / seg_len) segments (any
+ *               seg_len >= L is one segment of L rows; workspace and launches
+ *               are sized by min(seg_len, L))
  *   update_mode INFINI_ATTN_LINEAR or INFINI_ATTN_DELTA
  *   out  [B, Hq, L, d_v]   dtype (device), written; must not overlap any input
  * Passing (M_S, z_S) back with the next L rows continues the same stream of
@@ -229,9 +231,12 @@ int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, 
  * tensors run on the bf16 matrix cores, exact in fp32 with fp32 accumulation;
  * the other products run on the fp32 matrix cores. Output buffers must not
  * alias inputs. The
- * handle keeps fp32 scratch of about (B Hq L (d + 3) + 5 B Hkv S d^2) floats,
- * grown on demand. dbeta sums atomically, so its last bits may vary from run
- * to run. B = 0 writes dbeta = 0; L = 0 also passes (d_M, d_z) through to
+ * handle keeps fp32 scratch of about (B Hq L (d + 3) + 5 B Hkv S d^2 +
+ * B Hkv S (d^2 + d) ceil(max(seg_len, (Hq / Hkv) seg_len) / 1024)) floats,
+ * grown on demand. Every sum over blocks of rows is taken in a fixed order
+ * (per-block partials, then an ordered sum; no floating-point atomics), so
+ * repeated calls on the same inputs and device return bitwise identical
+ * gradients. B = 0 writes dbeta = 0; L = 0 also passes (d_M, d_z) through to
  * (dM0, dz0).
  * Errors: as infini_attn_forward; ERR_INVALID also for a null d_out, dq, dk,
  * dv, dbeta, M0, z0, dM0 or dz0 where the shapes are non-empty.

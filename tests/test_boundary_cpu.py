@@ -76,6 +76,8 @@ def test_library_is_built_for_gfx950_only():
     (dict(d_k=256, d_v=256), 64, ia.LINEAR, _lib.ERR_UNSUPPORTED),
     (dict(batch=2, n_q_heads=40000, n_kv_heads=1), 64, ia.LINEAR, _lib.ERR_UNSUPPORTED),
     (dict(seq_len=70000), 1, ia.LINEAR, _lib.ERR_UNSUPPORTED),
+    (dict(seq_len=(1 << 30) + 1), 1 << 30, ia.LINEAR, _lib.ERR_UNSUPPORTED),
+    (dict(), 2**31 - 1, ia.DELTA, 0),
 ])
 def test_check_codes(fields, seg, mode, expect):
     assert ia.infini_attn_check(desc(**fields), seg, mode) == expect
@@ -104,6 +106,18 @@ def test_workspace_size():
         + up(8 * 16 * 2 * 128 * 128 * 4) + up(8 * 16 * 32 * 128 * 64 * 2))
     with pytest.raises(ia.InfiniAttnError):
         ia.infini_attn_workspace_size(desc(), 0)
+
+
+def test_workspace_of_a_segment_longer_than_the_call():
+    """seg_len >= L is one segment of L rows: the workspace is that of
+    seg_len = L, also for seg_len near the int32 limit (no 32-bit overflow in
+    the tile counts, no request sized by rows that do not exist)."""
+    d = desc(batch=1, n_q_heads=32, n_kv_heads=8, seq_len=4096, d_k=128, d_v=128)
+    ref = ia.infini_attn_workspace_size(d, 4096)
+    for seg in (4097, 1 << 24, 2**31 - 1):
+        assert ia.infini_attn_workspace_size(d, seg) == ref
+    d200 = desc(seq_len=200)
+    assert ia.infini_attn_workspace_size(d200, 2**31 - 1) == ia.infini_attn_workspace_size(d200, 200)
 
 
 def test_create_without_device_reports_hip_error():

@@ -59,13 +59,14 @@ def run_oracle_bwd(inp, cot, dtype, seg_len, mode):
         None if cot["d_z"] is None else cot["d_z"].astype(np.float64), float(inp["eps"]))
 
 
-def check_grads(tag, gpu, ref):
+def check_grads(tag, gpu, ref, tol=None):
     for name, g, o in zip(NAMES, gpu, ref):
         assert g.shape == o.shape, f"{tag} {name}: shape {g.shape} vs {o.shape}"
         e = errors(g, o)
         log(f"{tag} {name}: {e}")
+        bound = (tol or {}).get(name, TOL)
         assert e["finite"], f"{tag} {name}: non-finite values"
-        assert e["max_rel"] <= TOL, f"{tag} {name}: max relative error {e['max_rel']:.3e}"
+        assert e["max_rel"] <= bound, f"{tag} {name}: max relative error {e['max_rel']:.3e}"
 
 
 def case(seed, dtype, seg_len, mode, state=True, **kw):
@@ -159,3 +160,45 @@ def test_backward_300m_shape_two_segments():
     log("bwd llama300m_16k L=4096 delta")
     check_grads("bwd 300m L=4096 delta", run_gpu_bwd(inp, cot, "bf16", w.seg_len, "delta"),
                 run_oracle_bwd(inp, cot, "bf16", w.seg_len, "delta"))
+
+
+def test_backward_is_bitwise_deterministic():
+    """Every gradient is summed in a fixed order (per-block partials added in
+    block order, no float atomics), so two calls on the same inputs agree bit
+    for bit. Grouped heads, the delta rule and segments longer than one
+    product block (1024 rows) give every partial-sum path more than one block
+    per unit; the result also matches the oracle."""
+    inp = synth.random_case(660, dtype="bf16", B=1, Hq=4, Hkv=1, L=2500, dk=64, dv=64,
+                            nonzero_state=True, scale=2.0 / 8.0)
+    cot = synth.random_cotangents(667, 1, 4, 1, 2500, 64, "bf16")
+    log("bwd determinism bf16 N=1200 delta GQA 4:1")
+    first = run_gpu_bwd(inp, cot, "bf16", 1200, "delta")
+    second = run_gpu_bwd(inp, cot, "bf16", 1200, "delta")
+    for name, a, b in zip(NAMES, first, second):
+        assert np.array_equal(a, b), f"{name} differs between two identical calls"
+    check_grads("bwd determinism", first, run_oracle_bwd(inp, cot, "bf16", 1200, "delta"))
+
+
+def test_backward_8b_shape_from_zero_state():
+    """The Llama-3-8B head layout over its first two segments from the
+    workload's own start, M0 = 0 and z0 = 0, checked per tensor (normwise).
+
+    With z0 = 0 every denominator of the first delta write is eps, so
+    G_1 = sigma(K_1)^T sigma(K_1) / eps has entries near 1e9, and dM0, about
+    -G_1^T gM_1, is ~1e8. Each entry of G_1 is a sum of N = 2048 positive fp32
+    terms, whose relative error is bounded by N u = 2048 * 2^-24 = 1.2e-4
+    (u the fp32 unit roundoff); dM0 inherits that bound, doubled for the
+    product's own rounding. The other gradients keep the 1e-4 bound."""
+    w = synth.WORKLOADS["llama3_8b_gqa"]
+    inp = synth.generate(w, seq_len=4096)
+    cot = synth.random_cotangents(43, w.batch, w.n_q_heads, w.n_kv_heads, 4096, w.d, "bf16")
+    log("bwd llama3_8b_gqa L=4096 delta zero state")
+    check_grads("bwd 8b L=4096 delta z0=0", run_gpu_bwd(inp, cot, "bf16", w.seg_len, "delta"),
+                run_oracle_bwd(inp, cot, "bf16", w.seg_len, "delta"),
+                tol={"dM0": 2 * w.seg_len * 2.0 ** -24})
+
+
+def test_backward_long_bf16_delta_chain():
+    """128 segments of 64 rows, bf16 storage, delta rule: the reverse chain
+    through 128 products (I - G_s) against the oracle's BPTT."""
+    case(670, "bf16", 64, "delta", B=1, Hq=2, Hkv=1, L=8192, dk=32, dv=32, nonzero_state=True)

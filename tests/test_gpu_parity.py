@@ -136,9 +136,10 @@ def test_segment_counts_around_the_scan_ring(S, d, mode):
               run_oracle(inp, "bf16", 64, mode), "bf16")
 
 
-@pytest.mark.parametrize("seg_len", [1, 5, 2000])
+@pytest.mark.parametrize("seg_len", [1, 5, 2000, 1 << 24, 2**31 - 1])
 def test_segment_length_extremes(seg_len):
-    """N = 1 (every row its own segment), an odd N, and N > L (one short segment)."""
+    """N = 1 (every row its own segment), an odd N, and N > L (one short
+    segment), also N near the int32 limit."""
     inp = synth.random_case(11, B=1, Hq=2, Hkv=1, L=200, dk=32, dv=32, dtype="bf16",
                             nonzero_state=True, scale=0.5)
     check_all(f"N={seg_len}", run_gpu(inp, "bf16", seg_len, "delta"),
