@@ -20,6 +20,8 @@ ERR_INVALID = -1
 ERR_UNSUPPORTED = -2
 ERR_HIP = -3
 ERR_OOM = -4
+ERR_SCRATCH = -5
+DECODE_SCRATCH_BYTES = 16 << 20  # INFINI_ATTN_DECODE_SCRATCH_BYTES
 F32 = 0
 BF16 = 1
 LINEAR = 0
@@ -28,7 +30,8 @@ DELTA = 1
 EXPORTS = ("infini_attn_check", "infini_attn_workspace_size", "infini_attn_create",
            "infini_attn_forward", "infini_attn_destroy", "infini_attn_strerror",
            "infini_attn_set_timing", "infini_attn_get_timing", "infini_attn_decode",
-           "infini_attn_update", "infini_attn_block_forward", "infini_attn_backward")
+           "infini_attn_update", "infini_attn_block_forward", "infini_attn_backward",
+           "infini_attn_decode_noalloc")
 
 
 class InfiniAttnDesc(ctypes.Structure):
@@ -80,6 +83,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.infini_attn_forward.restype = ctypes.c_int
         lib.infini_attn_decode.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp, vp]
         lib.infini_attn_decode.restype = ctypes.c_int
+        lib.infini_attn_decode_noalloc.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp, vp]
+        lib.infini_attn_decode_noalloc.restype = ctypes.c_int
         lib.infini_attn_update.argtypes = [vp, vp, vp, vp, vp, i32]
         lib.infini_attn_update.restype = ctypes.c_int
         lib.infini_attn_block_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
@@ -163,6 +168,14 @@ def infini_attn_decode(handle: int, q: int, n_new: int, k_cache: int, v_cache: i
                                    z, out)
     if st != OK:
         raise InfiniAttnError(st, "infini_attn_decode")
+
+
+def infini_attn_decode_noalloc(handle: int, q: int, n_new: int, k_cache: int, v_cache: int,
+                               n_past: int, beta: int, M: int, z: int, out: int) -> None:
+    st = load().infini_attn_decode_noalloc(handle, q, int(n_new), k_cache, v_cache, int(n_past),
+                                           beta, M, z, out)
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_decode_noalloc")
 
 
 def infini_attn_update(handle: int, k: int, v: int, M: int, z: int, update_mode: int) -> None:
@@ -326,12 +339,14 @@ def _check_device_tensors(**ts):
             raise TypeError(f"{name} must be float32")
 
 
-def decode(q, k_cache, v_cache, n_past: int, beta, M, z, out=None, eps: float = 1e-6):
+def decode(q, k_cache, v_cache, n_past: int, beta, M, z, out=None, eps: float = 1e-6,
+           noalloc: bool = False):
     """Streaming decode of q [B, Hq, C, d] (positions n_past .. n_past + C - 1
     of the current segment) against k_cache / v_cache [B, Hkv, cap, d], whose
     rows 0 .. n_past + C - 1 hold the segment (the new rows included). (M, z)
     is the state before the segment and is not modified. Returns out
-    [B, Hq, C, d]."""
+    [B, Hq, C, d]. With ``noalloc`` the library call allocates nothing (its
+    partials use the fixed per-device scratch array)."""
     import torch
 
     _check_device_tensors(q=q, k_cache=k_cache, v_cache=v_cache, beta=beta, M=M, z=z)
@@ -348,8 +363,9 @@ def decode(q, k_cache, v_cache, n_past: int, beta, M, z, out=None, eps: float = 
     elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
     h = handle_for(q, k_cache, eps, seq_len=cap)
-    infini_attn_decode(h, q.data_ptr(), C, k_cache.data_ptr(), v_cache.data_ptr(), n_past,
-                       beta.data_ptr(), M.data_ptr(), z.data_ptr(), out.data_ptr())
+    fn = infini_attn_decode_noalloc if noalloc else infini_attn_decode
+    fn(h, q.data_ptr(), C, k_cache.data_ptr(), v_cache.data_ptr(), n_past, beta.data_ptr(),
+       M.data_ptr(), z.data_ptr(), out.data_ptr())
     return out
 
 

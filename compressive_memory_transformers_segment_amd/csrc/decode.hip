@@ -29,10 +29,19 @@
 //     (denominator sigma(q).z by a wave reduction), applies the gate and
 //     stores the row.
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
 namespace ia {
+
+// Fixed scratch of the allocation-free decode entry point: the key-split
+// partials live here instead of in a buffer the handle grows. In host code
+// this name is only a stand-in for the symbol; the device address of each
+// device's copy comes from decode_scratch().
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
 namespace {
 
 constexpr int kDecKeys = 64;         // keys per workgroup (one split)
@@ -366,6 +375,23 @@ hipError_t launch_decode_d(const DecodeGeometry &g, const T *q, const T *kc, con
 }  // namespace
 
 int decode_splits(int n_keys) { return (n_keys + kDecKeys - 1) / kDecKeys; }
+
+hipError_t decode_scratch(int dev, float **ptr) {
+  static std::mutex mu;
+  static float *addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // Each device holds its own copy of the array at its own address; the
+    // caller has made `dev` current.
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float *>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t decode_partial_floats(const DecodeGeometry &g) {
   return static_cast<size_t>(g.B) * g.Hkv * decode_splits(g.n_past + g.C) *

@@ -187,6 +187,61 @@ hipError_t copy_final_z(const infini_attn_handle *h, const ia::Geometry &g, floa
                           static_cast<size_t>(g.B) * g.Hkv, hipMemcpyDeviceToDevice, h->stream);
 }
 
+// Streaming decode. The split partials go to the handle's buffer (grown on
+// demand) or, for the allocation-free variant, to the fixed per-device
+// scratch array, which bounds the request size and is shared by every call
+// on the device.
+int decode_call(infini_attn_handle *h, const void *q, int32_t n_new, const void *k_cache,
+                const void *v_cache, int32_t n_past, const float *beta, const float *M,
+                const float *z, void *out, bool noalloc) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  const infini_attn_desc &d = h->desc;
+  int st = check_desc(&d);
+  if (st != INFINI_ATTN_OK) return st;
+  if (n_new < 1 || n_past < 0 || static_cast<int64_t>(n_past) + n_new > d.seq_len)
+    return INFINI_ATTN_ERR_INVALID;
+  const int64_t nq = static_cast<int64_t>(d.n_q_heads / d.n_kv_heads) * n_new;
+  if ((nq + 15) / 16 > 65535) return INFINI_ATTN_ERR_UNSUPPORTED;  // grid z of the split kernel
+  if (d.batch == 0) return INFINI_ATTN_OK;
+  if (!q || !k_cache || !v_cache || !beta || !M || !z || !out) return INFINI_ATTN_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return INFINI_ATTN_ERR_INVALID;
+  if (!aligned(beta, 4) || !aligned(M, 4) || !aligned(z, 4)) return INFINI_ATTN_ERR_INVALID;
+  ia::DecodeGeometry g;
+  g.B = d.batch;
+  g.Hq = d.n_q_heads;
+  g.Hkv = d.n_kv_heads;
+  g.D = d.d_k;
+  g.C = n_new;
+  g.cap = d.seq_len;
+  g.n_past = n_past;
+  g.eps = d.eps;
+  const size_t part_bytes = ia::decode_partial_floats(g) * sizeof(float);
+  if (noalloc && part_bytes > ia::kDecodeScratchBytes) return INFINI_ATTN_ERR_SCRATCH;
+  DeviceGuard guard(d.device);
+  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  float *part = nullptr;
+  if (noalloc) {
+    // Looked up by infini_attn_create with the device current; cached.
+    if (ia::decode_scratch(d.device, &part) != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  } else {
+    st = ensure_buffer(&h->dec_ws, &h->dec_ws_bytes, part_bytes);
+    if (st != INFINI_ATTN_OK) return st;
+    part = static_cast<float *>(h->dec_ws);
+  }
+  const hipError_t e =
+      d.dtype == INFINI_ATTN_BF16
+          ? ia::launch_decode_bf16(g, static_cast<const uint16_t *>(q),
+                                   static_cast<const uint16_t *>(k_cache),
+                                   static_cast<const uint16_t *>(v_cache), beta, M, z, part,
+                                   static_cast<uint16_t *>(out), h->stream)
+          : ia::launch_decode_f32(g, static_cast<const float *>(q),
+                                  static_cast<const float *>(k_cache),
+                                  static_cast<const float *>(v_cache), beta, M, z, part,
+                                  static_cast<float *>(out), h->stream);
+  return hip_status(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,6 +276,11 @@ int infini_attn_create(infini_attn_t **h, const infini_attn_desc *desc) {
   if (desc->device >= count) return INFINI_ATTN_ERR_INVALID;
   DeviceGuard guard(desc->device);
   if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  // The allocation-free decode's scratch address on this device, looked up
+  // once per device with the device current (no allocation: the array is
+  // part of the library's code object).
+  float *scratch_addr = nullptr;
+  if (ia::decode_scratch(desc->device, &scratch_addr) != hipSuccess) return INFINI_ATTN_ERR_HIP;
   infini_attn_handle *p = new (std::nothrow) infini_attn_handle;
   if (!p) return INFINI_ATTN_ERR_OOM;
   p->desc = *desc;
@@ -337,44 +397,13 @@ int infini_attn_update(infini_attn_t *h, const void *k, const void *v, float *M,
 int infini_attn_decode(infini_attn_t *h, const void *q, int32_t n_new, const void *k_cache,
                        const void *v_cache, int32_t n_past, const float *beta, const float *M,
                        const float *z, void *out) {
-  if (!h) return INFINI_ATTN_ERR_INVALID;
-  const infini_attn_desc &d = h->desc;
-  int st = check_desc(&d);
-  if (st != INFINI_ATTN_OK) return st;
-  if (n_new < 1 || n_past < 0 || static_cast<int64_t>(n_past) + n_new > d.seq_len)
-    return INFINI_ATTN_ERR_INVALID;
-  const int64_t nq = static_cast<int64_t>(d.n_q_heads / d.n_kv_heads) * n_new;
-  if ((nq + 15) / 16 > 65535) return INFINI_ATTN_ERR_UNSUPPORTED;  // grid z of the split kernel
-  if (d.batch == 0) return INFINI_ATTN_OK;
-  if (!q || !k_cache || !v_cache || !beta || !M || !z || !out) return INFINI_ATTN_ERR_INVALID;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
-    return INFINI_ATTN_ERR_INVALID;
-  if (!aligned(beta, 4) || !aligned(M, 4) || !aligned(z, 4)) return INFINI_ATTN_ERR_INVALID;
-  DeviceGuard guard(d.device);
-  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
-  ia::DecodeGeometry g;
-  g.B = d.batch;
-  g.Hq = d.n_q_heads;
-  g.Hkv = d.n_kv_heads;
-  g.D = d.d_k;
-  g.C = n_new;
-  g.cap = d.seq_len;
-  g.n_past = n_past;
-  g.eps = d.eps;
-  st = ensure_buffer(&h->dec_ws, &h->dec_ws_bytes, ia::decode_partial_floats(g) * sizeof(float));
-  if (st != INFINI_ATTN_OK) return st;
-  float *part = static_cast<float *>(h->dec_ws);
-  const hipError_t e =
-      d.dtype == INFINI_ATTN_BF16
-          ? ia::launch_decode_bf16(g, static_cast<const uint16_t *>(q),
-                                   static_cast<const uint16_t *>(k_cache),
-                                   static_cast<const uint16_t *>(v_cache), beta, M, z, part,
-                                   static_cast<uint16_t *>(out), h->stream)
-          : ia::launch_decode_f32(g, static_cast<const float *>(q),
-                                  static_cast<const float *>(k_cache),
-                                  static_cast<const float *>(v_cache), beta, M, z, part,
-                                  static_cast<float *>(out), h->stream);
-  return hip_status(e);
+  return decode_call(h, q, n_new, k_cache, v_cache, n_past, beta, M, z, out, false);
+}
+
+int infini_attn_decode_noalloc(infini_attn_t *h, const void *q, int32_t n_new,
+                               const void *k_cache, const void *v_cache, int32_t n_past,
+                               const float *beta, const float *M, const float *z, void *out) {
+  return decode_call(h, q, n_new, k_cache, v_cache, n_past, beta, M, z, out, true);
 }
 
 int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, const void *wq,
@@ -614,6 +643,8 @@ const char *infini_attn_strerror(int status) {
     case INFINI_ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case INFINI_ATTN_ERR_HIP: return "HIP runtime or launch failure";
     case INFINI_ATTN_ERR_OOM: return "out of device memory";
+    case INFINI_ATTN_ERR_SCRATCH:
+      return "request larger than the fixed scratch of the allocation-free entry point";
   }
   return "unknown status";
 }

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "infini_attn.h"
+
 namespace ia {
 
 // Problem geometry of one forward call, already validated on the host.
@@ -119,6 +121,15 @@ struct DecodeGeometry {
 // fp32 scratch the split partials need.
 int decode_splits(int n_keys);
 size_t decode_partial_floats(const DecodeGeometry &g);
+
+// The allocation-free decode keeps its split partials in a fixed device array
+// of this many bytes (one per device, held until the process ends).
+constexpr size_t kDecodeScratchBytes = INFINI_ATTN_DECODE_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+// Device address of the fixed decode scratch on device `dev`, which must be
+// the current device; looked up once per device and cached.
+hipError_t decode_scratch(int dev, float **ptr);
 
 // Streaming decode: split partials of the local attention into `part`, then
 // merge, retrieval from (M, z), gate and store into out [B][Hq][C][D].

@@ -52,6 +52,10 @@ extern "C" {
 #define INFINI_ATTN_ERR_UNSUPPORTED (-2) /* valid request this build has no kernel for */
 #define INFINI_ATTN_ERR_HIP (-3)         /* HIP runtime or launch failure, no device */
 #define INFINI_ATTN_ERR_OOM (-4)         /* workspace allocation failed */
+#define INFINI_ATTN_ERR_SCRATCH (-5)     /* request larger than a fixed scratch array */
+
+/* Bytes of the fixed per-device scratch array of infini_attn_decode_noalloc. */
+#define INFINI_ATTN_DECODE_SCRATCH_BYTES (16u << 20)
 
 /* Storage type of q, k, v and out. beta, M and z are always fp32. */
 #define INFINI_ATTN_F32 0
@@ -159,6 +163,29 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
 int infini_attn_decode(infini_attn_t *h, const void *q, int32_t n_new, const void *k_cache,
                        const void *v_cache, int32_t n_past, const float *beta, const float *M,
                        const float *z, void *out);
+
+/*
+ * Allocation-free variant of infini_attn_decode, for callers that cannot
+ * allocate device memory during the call: code under HIP graph capture, tight
+ * serving loops, and harnesses that forbid hipMalloc. Same arguments, same
+ * kernels and the same result as infini_attn_decode, but the key-split
+ * partials go to a fixed array of INFINI_ATTN_DECODE_SCRATCH_BYTES that the
+ * library's code object holds on every device it runs on (until the process
+ * ends), instead of a buffer the handle grows: the call allocates nothing and
+ * calls no allocating library routine. Its address on a device is looked up
+ * by infini_attn_create, with that device current.
+ * The partials need 4 (d_v + 2) B Hq n_new ceil((n_past + n_new) / 64) bytes;
+ * a larger request returns ERR_SCRATCH before anything is enqueued (one new
+ * row against a full 2048-row segment of the Llama-3-8B attention shape takes
+ * 532 KB). Every call on one device shares that device's array and overwrites
+ * what the previous call left there (nothing in it needs to start at zero):
+ * calls that may overlap on one device, from any handle or stream, race and
+ * must be serialised by the caller.
+ * Errors: as infini_attn_decode, with ERR_SCRATCH in place of ERR_OOM.
+ */
+int infini_attn_decode_noalloc(infini_attn_t *h, const void *q, int32_t n_new,
+                               const void *k_cache, const void *v_cache, int32_t n_past,
+                               const float *beta, const float *M, const float *z, void *out);
 
 /*
  * Memory update of one finished segment: the desc.seq_len rows of k, v are
