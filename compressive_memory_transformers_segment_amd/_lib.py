@@ -31,7 +31,7 @@ EXPORTS = ("infini_attn_check", "infini_attn_workspace_size", "infini_attn_creat
            "infini_attn_forward", "infini_attn_destroy", "infini_attn_strerror",
            "infini_attn_set_timing", "infini_attn_get_timing", "infini_attn_decode",
            "infini_attn_update", "infini_attn_block_forward", "infini_attn_backward",
-           "infini_attn_decode_noalloc")
+           "infini_attn_decode_noalloc", "infini_attn_block_forward_qkv")
 
 
 class InfiniAttnDesc(ctypes.Structure):
@@ -90,6 +90,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         lib.infini_attn_block_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                                   i32, vp]
         lib.infini_attn_block_forward.restype = ctypes.c_int
+        lib.infini_attn_block_forward_qkv.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32,
+                                                      vp]
+        lib.infini_attn_block_forward_qkv.restype = ctypes.c_int
         lib.infini_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
                                              vp, vp, vp, vp, vp, vp]
         lib.infini_attn_backward.restype = ctypes.c_int
@@ -191,6 +194,15 @@ def infini_attn_block_forward(handle: int, d_model: int, x: int, wq: int, wk: in
                                           int(seg_len), int(update_mode), y)
     if st != OK:
         raise InfiniAttnError(st, "infini_attn_block_forward")
+
+
+def infini_attn_block_forward_qkv(handle: int, d_model: int, x: int, wqkv: int, wo: int,
+                                  beta: int, M: int, z: int, seg_len: int, update_mode: int,
+                                  y: int) -> None:
+    st = load().infini_attn_block_forward_qkv(handle, int(d_model), x, wqkv, wo, beta, M, z,
+                                              int(seg_len), int(update_mode), y)
+    if st != OK:
+        raise InfiniAttnError(st, "infini_attn_block_forward_qkv")
 
 
 def infini_attn_destroy(handle: Optional[int]) -> None:
@@ -389,24 +401,31 @@ def update(k, v, M, z, update_mode="linear", eps: float = 1e-6, n_q_heads: Optio
 
 
 def block_forward(x, wq, wk, wv, wo, beta, M, z, seg_len: int, update_mode="linear",
-                  n_q_heads: int = 1, n_kv_heads: int = 1, out=None, eps: float = 1e-6):
+                  n_q_heads: int = 1, n_kv_heads: int = 1, out=None, eps: float = 1e-6,
+                  wqkv=None):
     """The Infini-attention block on x [B, L, d_model]: Q/K/V projections
-    (wq [d_model, Hq d], wk / wv [d_model, Hkv d]), the forward pass, and the
-    output projection wo [Hq d, d_model]. (M, z) are updated in place.
-    Returns y [B, L, d_model]."""
+    (wq [d_model, Hq d], wk / wv [d_model, Hkv d], or instead wqkv [d_model,
+    (Hq + 2 Hkv) d] with wq = wk = wv = None: the three side by side), the
+    forward pass, and the output projection wo [Hq d, d_model]. (M, z) are
+    updated in place. Returns y [B, L, d_model]."""
     import torch
 
-    _check_device_tensors(x=x, wq=wq, wk=wk, wv=wv, wo=wo, beta=beta, M=M, z=z)
-    for name, t in (("wq", wq), ("wk", wk), ("wv", wv), ("wo", wo)):
+    fused = wqkv is not None
+    ws = dict(wqkv=wqkv) if fused else dict(wq=wq, wk=wk, wv=wv)
+    _check_device_tensors(x=x, wo=wo, beta=beta, M=M, z=z, **ws)
+    for name, t in list(ws.items()) + [("wo", wo)]:
         if t.dtype != x.dtype:
             raise TypeError(f"{name} must have the dtype of x")
     B, L, dm = x.shape
     Hq, Hkv = int(n_q_heads), int(n_kv_heads)
-    if Hq < 1 or Hkv < 1 or Hq % Hkv or wq.shape[1] % Hq:
+    width = wo.shape[0]
+    if Hq < 1 or Hkv < 1 or Hq % Hkv or width % Hq:
         raise ValueError("inconsistent head counts")
-    D = wq.shape[1] // Hq
-    if (tuple(wq.shape) != (dm, Hq * D) or tuple(wk.shape) != (dm, Hkv * D)
-            or tuple(wv.shape) != (dm, Hkv * D) or tuple(wo.shape) != (Hq * D, dm)
+    D = width // Hq
+    wshapes = ((tuple(wqkv.shape) == (dm, (Hq + 2 * Hkv) * D)) if fused else
+               (tuple(wq.shape) == (dm, Hq * D) and tuple(wk.shape) == (dm, Hkv * D)
+                and tuple(wv.shape) == (dm, Hkv * D)))
+    if (not wshapes or tuple(wo.shape) != (Hq * D, dm)
             or tuple(beta.shape) != (Hq,) or tuple(M.shape) != (B, Hkv, D, D)
             or tuple(z.shape) != (B, Hkv, D)):
         raise ValueError("inconsistent shapes")
@@ -417,9 +436,14 @@ def block_forward(x, wq, wk, wv, wo, beta, M, z, seg_len: int, update_mode="line
     qlike = x.new_empty((B, Hq, 0, D))
     klike = x.new_empty((B, Hkv, 0, D))
     h = handle_for(qlike, klike, eps, seq_len=L)
-    infini_attn_block_forward(h, dm, x.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(),
-                              wo.data_ptr(), beta.data_ptr(), M.data_ptr(), z.data_ptr(), seg_len,
-                              _mode(update_mode), out.data_ptr())
+    if fused:
+        infini_attn_block_forward_qkv(h, dm, x.data_ptr(), wqkv.data_ptr(), wo.data_ptr(),
+                                      beta.data_ptr(), M.data_ptr(), z.data_ptr(), seg_len,
+                                      _mode(update_mode), out.data_ptr())
+    else:
+        infini_attn_block_forward(h, dm, x.data_ptr(), wq.data_ptr(), wk.data_ptr(),
+                                  wv.data_ptr(), wo.data_ptr(), beta.data_ptr(), M.data_ptr(),
+                                  z.data_ptr(), seg_len, _mode(update_mode), out.data_ptr())
     return out
 
 

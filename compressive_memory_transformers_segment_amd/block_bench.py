@@ -1,10 +1,14 @@
 """Throughput of the whole Infini-attention block on one GPU.
 
-    python -m compressive_memory_transformers_segment_amd.block_bench [--steps K] [--mode delta|linear]
+    python -m compressive_memory_transformers_segment_amd.block_bench [--steps K]
+        [--mode delta|linear] [--weights fused|separate]
 
-One step is one infini_attn_block_forward call at the Llama-3-8B layer shape:
-x [1, 32768, 4096] bf16, 32 query heads and 8 kv heads of d = 128 (wq
-[4096, 4096], wk / wv [4096, 1024], wo [4096, 4096]), segments of 2048 rows.
+One step is one block call at the Llama-3-8B layer shape: x [1, 32768, 4096]
+bf16, 32 query heads and 8 kv heads of d = 128 (wq [4096, 4096], wk / wv
+[4096, 1024], wo [4096, 4096]), segments of 2048 rows; with fused weights
+(the default) infini_attn_block_forward_qkv takes [Wq|Wk|Wv] [4096, 6144] and
+projects with one GEMM, with separate ones infini_attn_block_forward runs one
+GEMM per weight.
 Inputs are seeded on the device: x ~ N(0, 1), weights ~ N(0, 1/fan_in),
 beta ~ N(0, 1), zero initial state. Prints one JSON line: ms per block,
 tokens/s, and the algorithmic TFLOP/s of the block (projections, attention,
@@ -28,6 +32,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--mode", default="delta", choices=["linear", "delta"])
+    ap.add_argument("--weights", default="fused", choices=["fused", "separate"])
     args = ap.parse_args(argv)
     import torch
 
@@ -46,14 +51,19 @@ def main(argv=None) -> int:
     x = rnd(B, L, dm)
     wq, wk, wv = (rnd(dm, n * D, scale=1 / math.sqrt(dm)) for n in (Hq, Hkv, Hkv))
     wo = rnd(Hq * D, dm, scale=1 / math.sqrt(Hq * D))
+    wqkv = torch.cat([wq, wk, wv], dim=1).contiguous() if args.weights == "fused" else None
     beta = torch.randn((Hq,), generator=g, device=dev)
     M = torch.zeros((B, Hkv, D, D), device=dev)
     z = torch.zeros((B, Hkv, D), device=dev)
     y = torch.empty_like(x)
 
     def step():
-        _lib.block_forward(x, wq, wk, wv, wo, beta, M, z, N, args.mode, n_q_heads=Hq,
-                           n_kv_heads=Hkv, out=y)
+        if wqkv is not None:
+            _lib.block_forward(x, None, None, None, wo, beta, M, z, N, args.mode, n_q_heads=Hq,
+                               n_kv_heads=Hkv, out=y, wqkv=wqkv)
+        else:
+            _lib.block_forward(x, wq, wk, wv, wo, beta, M, z, N, args.mode, n_q_heads=Hq,
+                               n_kv_heads=Hkv, out=y)
 
     for _ in range(args.warmup):
         step()
@@ -76,6 +86,7 @@ def main(argv=None) -> int:
     res = {
         "workload": "llama3_8b_layer", "batch": B, "seq_len": L, "d_model": dm,
         "n_q_heads": Hq, "n_kv_heads": Hkv, "d": D, "seg_len": N, "update": args.mode,
+        "weights": args.weights,
         "steps": args.steps, "ms_per_block": ms, "tokens_per_s": B * L / (ms * 1e-3),
         "flops": {"projections": proj, "attention_retrieval": attn, "memory_update": scan},
         "tflops_algorithmic": flops / (ms * 1e-3) / 1e12,

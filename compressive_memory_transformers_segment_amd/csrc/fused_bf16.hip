@@ -206,8 +206,8 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ vt, int vt_tiles, const float *__restrict__ beta,
     const float *__restrict__ z_pre, const uint16_t *__restrict__ mt_pre,
-    uint16_t *__restrict__ out, int Hq, int Hkv, int L, int N, int S, int n_qt, int n_items,
-    float eps, float scale_log2) {
+    uint16_t *__restrict__ out, Layout lq, Layout lkv, Layout lo, int Hq, int Hkv, int L, int N,
+    int S, int n_qt, int n_items, float eps, float scale_log2) {
   using TL = Tile<D>;
   constexpr int NT = D / 16;          // k-steps over d
   constexpr int ND = D / 32;          // 32-row d tiles of O^T
@@ -272,10 +272,11 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   // (The lane values pass through an empty asm statement at each use, so the
   // compiler does not hoist per-lane addresses out of the loops and keep them
   // in registers the MFMA work needs.)
-  auto rowsrc = [&](const uint16_t *base, int row0, int rowmax) __attribute__((always_inline)) {
+  auto rowsrc = [&](const uint16_t *base, int row0, int rowmax, long long stride)
+                    __attribute__((always_inline)) {
     int r = lr, c = lcol;
     __asm__ volatile("" : "+v"(r), "+v"(c));
-    return base + static_cast<size_t>(min(row0 + r, rowmax)) * D + c;
+    return base + min(row0 + r, rowmax) * stride + c;
   };
   auto linsrc = [&](const uint16_t *base) __attribute__((always_inline)) {
     int ln = lane;
@@ -294,13 +295,17 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
       const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
       return reinterpret_cast<uint16_t *>((static_cast<uint64_t>(hi) << 32) | lo);
     };
-    const uint16_t *kseg = k + (static_cast<size_t>(it.head) * L + it.a) * D;
+    const uint16_t *kseg = k + head_offset(lkv, it.head, Hkv) + it.a * lkv.sr;
     const uint16_t *vseg = vt + (static_cast<size_t>(it.head) * S + it.s) * vt_tiles * (D * 64);
+    // (The resource ends with the segment's last row; its rows lie
+    // lkv.sr elements apart.)
     const auto krs = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(kseg), 0, __builtin_amdgcn_readfirstlane((it.e - it.a) * D * 2), 0x00020000);
+        uniform_ptr(kseg), 0,
+        __builtin_amdgcn_readfirstlane(static_cast<int>(((it.e - it.a - 1) * lkv.sr + D) * 2)),
+        0x00020000);
     const auto vrs = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(vseg), 0, __builtin_amdgcn_readfirstlane(vt_tiles * D * 64 * 2), 0x00020000);
-    int kvo = (lr * D + lcol) * 2, vvo = 16 * lane;
+    int kvo = static_cast<int>((lr * lkv.sr + lcol) * 2), vvo = 16 * lane;
     __asm__ volatile("" : "+v"(kvo), "+v"(vvo));
 #pragma unroll
     for (int i = 0; i < TL::IPW; ++i) {
@@ -309,8 +314,9 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
       // the first load is K in waves 0..3 and V^T in waves 4..7.
       const bool is_k = (TL::KU % kThreads == 0) ? (i < TL::KU / kThreads) : (u0 < TL::KU);
       if (is_k)
-        buffer_load_lds16(krs, buf + 8 * (8 * i + w) * 64, kvo,
-                          __builtin_amdgcn_readfirstlane((t * kBN + 32 * blk(i)) * D * 2));
+        buffer_load_lds16(
+            krs, buf + 8 * (8 * i + w) * 64, kvo,
+            __builtin_amdgcn_readfirstlane(static_cast<int>((t * kBN + 32 * blk(i)) * lkv.sr * 2)));
       else
         buffer_load_lds16(vrs, buf + 8 * (8 * i + w) * 64, vvo,
                           __builtin_amdgcn_readfirstlane((t * D * 64 + 8 * (u0 - TL::KU)) * 2));
@@ -322,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   auto dma_mem = [&](const FusedItem &it, uint16_t *buf) __attribute__((always_inline)) {
     const uint16_t *mt = mt_pre + (static_cast<size_t>(it.head) * S + it.s) * D * D;
 #pragma unroll
-    for (int i = 0; i < TL::IPW; ++i) ld(rowsrc(mt, 32 * blk(i), D - 1), buf, i);  // rows past D (D < 128): unread copies
+    for (int i = 0; i < TL::IPW; ++i) ld(rowsrc(mt, 32 * blk(i), D - 1, D), buf, i);  // rows past D (D < 128): unread copies
     const float *zs = z_pre + (static_cast<size_t>(it.head) * (S + 1) + it.s) * D;
     const float *side = (w == kWaves - 1) ? beta + it.bq % Hq + (lane < HPW ? lane : 0)
                                           : zs + (64 * w + lane) % D;
@@ -333,7 +339,8 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < TL::IPW; ++i) {
       const int wv = 4 * half + blk(i);  // the wave that reads this block
-      ld(rowsrc(q + static_cast<size_t>(it.bq + wv / RW) * L * D, it.q0 + (wv % RW) * 32, it.e - 1),
+      ld(rowsrc(q + head_offset(lq, it.bq + wv / RW, Hq), it.q0 + (wv % RW) * 32, it.e - 1,
+                lq.sr),
          buf, i);
     }
   };
@@ -477,12 +484,15 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     // The buffer's base and size are wave-uniform (readfirstlane states it;
     // a buffer resource must be in scalar registers).
     const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(32, cur.e - qw)));
-    const size_t obase = (static_cast<size_t>(cur.bq + w / RW) * L + qw) * D;
+    const size_t obase = head_offset(lo, cur.bq + w / RW, Hq) + qw * lo.sr;
     const uint32_t ob_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(obase));
     const uint32_t ob_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(obase >> 32));
     uint16_t *ob = out + ((static_cast<size_t>(ob_hi) << 32) | ob_lo);
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(ob, 0, nrows * D * 2, 0x00020000);
-    const int lane_off = (l32 < nrows ? l32 : nrows) * D * 2;
+    // The resource ends with this wave's last row in the segment (rows lo.sr
+    // elements apart); lanes past it address the next row and are dropped.
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        ob, 0, nrows > 0 ? static_cast<int>(((nrows - 1) * lo.sr + D) * 2) : 0, 0x00020000);
+    const int lane_off = static_cast<int>((l32 < nrows ? l32 : nrows) * lo.sr * 2);
     // One 32-row block of A_mem^T at a time (the fences keep the four
     // accumulation chains from being interleaved, which would hold four
     // accumulators at once). Row 32 dt + l32 of M^T has the swizzle of row
@@ -677,8 +687,8 @@ hipError_t launch_t(const Geometry &g, const uint16_t *q, const uint16_t *k, con
   const long long grid = n_items < slots ? n_items : slots;
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   fused_bf16_kernel<D, HPW><<<dim3(static_cast<unsigned>(grid)), kThreads, 0, stream>>>(
-      q, k, ws.vt, ws.vt_tiles, beta, ws.z_pre, ws.mt_pre_bf16, out, g.Hq, g.Hkv, g.L, g.N, g.S,
-      n_qt, static_cast<int>(n_items), g.eps, scale_log2);
+      q, k, ws.vt, ws.vt_tiles, beta, ws.z_pre, ws.mt_pre_bf16, out, g.lq, g.lkv, g.lo, g.Hq,
+      g.Hkv, g.L, g.N, g.S, n_qt, static_cast<int>(n_items), g.eps, scale_log2);
   return hipGetLastError();
 }
 

@@ -27,8 +27,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void fused_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ beta, const float *__restrict__ z_pre,
-    const float *__restrict__ mt_pre, float *__restrict__ out, int Hq, int Hkv, int L, int N,
-    int S, float eps) {
+    const float *__restrict__ mt_pre, float *__restrict__ out, Layout lq, Layout lkv, Layout lo,
+    int Hq, int Hkv, int L, int N, int S, float eps) {
   constexpr int DQ = D / 4;
   constexpr int SA = kBN * D > kBM * (kKC + 1) ? kBN * D : kBM * (kKC + 1);
   __shared__ float sA[SA];       // K tile; later sigma(Q) chunk (row stride kKC + 1)
@@ -48,15 +48,16 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(
   const int qi = q0 + row;
   const bool valid = qi < e;
 
-  const float *qp = q + static_cast<size_t>(bhq) * L * D;
-  const size_t kvoff = (static_cast<size_t>(b) * Hkv + hk) * L * D;
+  // Row i of this head's q, k, v at qp + i * lq.sr, kp / vp + i * lkv.sr.
+  const float *qp = q + head_offset(lq, bhq, Hq);
+  const long long kvoff = head_offset(lkv, b * Hkv + hk, Hkv);
   const float *kp = k + kvoff;
   const float *vp = v + kvoff;
 
   float qv[DQ], o[DQ];
 #pragma unroll
   for (int c = 0; c < DQ; ++c) {
-    qv[c] = valid ? qp[static_cast<size_t>(qi) * D + 4 * c + qd] : 0.f;
+    qv[c] = valid ? qp[qi * lq.sr + 4 * c + qd] : 0.f;
     o[c] = 0.f;
   }
   const float scale = rsqrtf(static_cast<float>(D));
@@ -66,10 +67,10 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(
   for (int kv0 = a; kv0 < kv_end; kv0 += kBN) {
     __syncthreads();
     for (int idx = t; idx < kBN * D; idx += kThreads) {
-      const int r = idx / D;
+      const int r = idx / D, c = idx % D;
       const bool in = kv0 + r < e;
-      sA[idx] = in ? kp[static_cast<size_t>(kv0) * D + idx] : 0.f;
-      sB[idx] = in ? vp[static_cast<size_t>(kv0) * D + idx] : 0.f;
+      sA[idx] = in ? kp[(kv0 + r) * lkv.sr + c] : 0.f;
+      sB[idx] = in ? vp[(kv0 + r) * lkv.sr + c] : 0.f;
     }
     __syncthreads();
     float sc[kBN];
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(
     for (int idx = t; idx < kBM * kKC; idx += kThreads) {
       const int r = idx / kKC, c = idx % kKC;
       const int qr = q0 + r;
-      sA[r * (kKC + 1) + c] = (qr < e) ? elu1(qp[static_cast<size_t>(qr) * D + k0 + c]) : 0.f;
+      sA[r * (kKC + 1) + c] = (qr < e) ? elu1(qp[qr * lq.sr + k0 + c]) : 0.f;
     }
     for (int idx = t; idx < D * kKC; idx += kThreads) {
       const int jv = idx / kKC, c = idx % kKC;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(
   const float gam = 1.f / (1.f + __expf(-beta[h]));
   const float inv_l = 1.f / l;
   if (valid) {
-    float *op = out + (static_cast<size_t>(bhq) * L + qi) * D;
+    float *op = out + head_offset(lo, bhq, Hq) + qi * lo.sr;
 #pragma unroll
     for (int c = 0; c < DQ; ++c) op[4 * c + qd] = gam * (am[c] / den) + (1.f - gam) * (o[c] * inv_l);
   }
@@ -156,7 +157,8 @@ hipError_t launch_t(const Geometry &g, const float *q, const float *k, const flo
                     const float *beta, const Workspace &ws, float *out, hipStream_t stream) {
   dim3 grid((g.N + kBM - 1) / kBM, g.S, g.B * g.Hq);
   fused_f32_kernel<D><<<grid, kThreads, 0, stream>>>(q, k, v, beta, ws.z_pre, ws.mt_pre_f32, out,
-                                                     g.Hq, g.Hkv, g.L, g.N, g.S, g.eps);
+                                                     g.lq, g.lkv, g.lo, g.Hq, g.Hkv, g.L, g.N,
+                                                     g.S, g.eps);
   return hipGetLastError();
 }
 

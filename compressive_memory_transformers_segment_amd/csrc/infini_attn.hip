@@ -69,7 +69,10 @@ int check_desc(const infini_attn_desc *d) {
   return INFINI_ATTN_OK;
 }
 
-int n_segments(int L, int N) { return L == 0 ? 0 : (L + N - 1) / N; }
+// ceil(L / N), in 64-bit so that any seg_len up to INT32_MAX is safe.
+int n_segments(int L, int N) {
+  return L == 0 ? 0 : static_cast<int>((static_cast<int64_t>(L) + N - 1) / N);
+}
 
 // Segment length the kernels see: a segment never holds more rows than the
 // call has, so seg_len >= L is one segment of L rows (the same result), and
@@ -187,6 +190,82 @@ hipError_t copy_final_z(const infini_attn_handle *h, const ia::Geometry &g, floa
                           static_cast<size_t>(g.B) * g.Hkv, hipMemcpyDeviceToDevice, h->stream);
 }
 
+// The forward pass on tensors of the given layouts (the C ABI's head-major
+// ones, or the block's row-major projections).
+int forward_impl(infini_attn_handle *h, const void *q, const void *k, const void *v,
+                 const float *beta, float *M, float *z, int32_t seg_len, int32_t update_mode,
+                 void *out, const ia::Layout &lq, const ia::Layout &lkv, const ia::Layout &lo) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  const infini_attn_desc &d = h->desc;
+  int st = infini_attn_check(&d, seg_len, update_mode);
+  if (st != INFINI_ATTN_OK) return st;
+  if (d.batch == 0 || d.seq_len == 0) return INFINI_ATTN_OK;  // nothing to do; state unchanged
+  if (!q || !k || !v || !beta || !M || !z || !out) return INFINI_ATTN_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return INFINI_ATTN_ERR_INVALID;
+  if (!aligned(beta, 4) || !aligned(M, 4) || !aligned(z, 4)) return INFINI_ATTN_ERR_INVALID;
+
+  DeviceGuard guard(d.device);
+  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+
+  ia::Geometry g;
+  g.B = d.batch;
+  g.Hq = d.n_q_heads;
+  g.Hkv = d.n_kv_heads;
+  g.L = d.seq_len;
+  g.D = d.d_k;
+  g.N = effective_seg(d.seq_len, seg_len);
+  g.S = n_segments(d.seq_len, g.N);
+  g.eps = d.eps;
+  g.lq = lq;
+  g.lkv = lkv;
+  g.lo = lo;
+  // The bf16 kernels address a segment's rows (and a tile's) through 32-bit
+  // buffer offsets.
+  const int64_t elt = d.dtype == INFINI_ATTN_BF16 ? 2 : 4;
+  if ((static_cast<int64_t>(g.N) * std::max(lq.sr, std::max(lkv.sr, lo.sr)) + d.d_k) * elt >
+      INT32_MAX)
+    return INFINI_ATTN_ERR_UNSUPPORTED;
+
+  ia::Workspace ws;
+  st = bind_workspace(h, g, &ws);
+  if (st != INFINI_ATTN_OK) return st;
+  const bool bf16 = d.dtype == INFINI_ATTN_BF16;
+
+  TimedCall tc{};
+  if (h->timing) {
+    if (!h->spare.empty()) {
+      tc = h->spare.back();
+      h->spare.pop_back();
+    } else {
+      for (int i = 0; i < 3; ++i) {
+        if (hipEventCreate(&tc.ev[i]) != hipSuccess) {
+          for (int j = 0; j < i; ++j) (void)hipEventDestroy(tc.ev[j]);
+          return INFINI_ATTN_ERR_HIP;
+        }
+      }
+    }
+    h->recorded.push_back(tc);
+    if (hipEventRecord(tc.ev[0], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  }
+  const int delta = update_mode == INFINI_ATTN_DELTA;
+  hipError_t e = launch_scan(h, g, k, v, M, z, delta, ws);
+  if (e != hipSuccess) return hip_status(e);
+  if (h->timing && hipEventRecord(tc.ev[1], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  if (bf16) {
+    e = ia::launch_fused_bf16(g, static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                              static_cast<const uint16_t *>(v), beta, ws,
+                              static_cast<uint16_t *>(out), h->stream);
+  } else {
+    e = ia::launch_fused_f32(g, static_cast<const float *>(q), static_cast<const float *>(k),
+                             static_cast<const float *>(v), beta, ws, static_cast<float *>(out),
+                             h->stream);
+  }
+  if (e != hipSuccess) return hip_status(e);
+  if (h->timing && hipEventRecord(tc.ev[2], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  return hip_status(copy_final_z(h, g, z, ws));
+}
+
 // Streaming decode. The split partials go to the handle's buffer (grown on
 // demand) or, for the allocation-free variant, to the fixed per-device
 // scratch array, which bounds the request size and is shared by every call
@@ -240,6 +319,67 @@ int decode_call(infini_attn_handle *h, const void *q, int32_t n_new, const void 
                                   static_cast<const float *>(v_cache), beta, M, z, part,
                                   static_cast<float *>(out), h->stream);
   return hip_status(e);
+}
+
+// The Infini-attention block. The projections land row-major in one buffer,
+// QKV [B, L, W] with W = (Hq + 2 Hkv) d (the query heads' columns, then the
+// key heads', then the value heads'): one GEMM against a fused [Wq|Wk|Wv]
+// weight, or one GEMM per weight writing its column block. The attention
+// kernels read their heads' rows of it in place (row stride W) and write O
+// row-major [B, L, Hq d], the output projection's input; nothing is
+// regrouped.
+int block_call(infini_attn_handle *h, int32_t d_model, const void *x, const void *wq,
+               const void *wk, const void *wv, const void *wqkv, const void *wo,
+               const float *beta, float *M, float *z, int32_t seg_len, int32_t update_mode,
+               void *y) {
+  if (!h) return INFINI_ATTN_ERR_INVALID;
+  const infini_attn_desc &d = h->desc;
+  int st = infini_attn_check(&d, seg_len, update_mode);
+  if (st != INFINI_ATTN_OK) return st;
+  if (d_model < 1) return INFINI_ATTN_ERR_INVALID;
+  if (d.batch == 0 || d.seq_len == 0) return INFINI_ATTN_OK;
+  if (!x || !wo || !beta || !M || !z || !y) return INFINI_ATTN_ERR_INVALID;
+  const int64_t rows = static_cast<int64_t>(d.batch) * d.seq_len;
+  const int64_t D = d.d_k, Hq = d.n_q_heads, Hkv = d.n_kv_heads;
+  const int64_t W = (Hq + 2 * Hkv) * D;
+  if (rows > INT32_MAX || W > INT32_MAX) return INFINI_ATTN_ERR_UNSUPPORTED;
+  DeviceGuard guard(d.device);
+  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
+  if (!h->blas) {
+    st = ia::blas_create(&h->blas, h->stream);
+    if (st != INFINI_ATTN_OK) return st;
+  }
+  const size_t elt = d.dtype == INFINI_ATTN_BF16 ? 2 : 4;
+  // QKV [rows][W], then O [rows][Hq D] (each part 256-byte aligned).
+  const size_t o_off = round_up(static_cast<size_t>(rows) * W * elt);
+  st = ensure_buffer(&h->blk_ws, &h->blk_ws_bytes, o_off + round_up(rows * Hq * D * elt));
+  if (st != INFINI_ATTN_OK) return st;
+  char *qkv = static_cast<char *>(h->blk_ws);
+  char *o = qkv + o_off;
+  const int n = static_cast<int>(rows);
+  if (wqkv) {
+    st = ia::blas_gemm_rowmajor(h->blas, d.dtype, n, static_cast<int>(W), d_model, x, d_model,
+                                wqkv, static_cast<int>(W), qkv, static_cast<int>(W));
+    if (st != INFINI_ATTN_OK) return st;
+  } else {
+    const struct {
+      const void *w;
+      int64_t col, width;
+    } proj[3] = {{wq, 0, Hq * D}, {wk, Hq * D, Hkv * D}, {wv, (Hq + Hkv) * D, Hkv * D}};
+    for (const auto &pj : proj) {
+      st = ia::blas_gemm_rowmajor(h->blas, d.dtype, n, static_cast<int>(pj.width), d_model, x,
+                                  d_model, pj.w, static_cast<int>(pj.width),
+                                  qkv + pj.col * elt, static_cast<int>(W));
+      if (st != INFINI_ATTN_OK) return st;
+    }
+  }
+  const ia::Layout lrow{d.seq_len * W, D, W};
+  const ia::Layout lout{d.seq_len * Hq * D, D, Hq * D};
+  st = forward_impl(h, qkv, qkv + Hq * D * elt, qkv + (Hq + Hkv) * D * elt, beta, M, z, seg_len,
+                    update_mode, o, lrow, lrow, lout);
+  if (st != INFINI_ATTN_OK) return st;
+  return ia::blas_gemm_rowmajor(h->blas, d.dtype, n, d_model, static_cast<int>(Hq * D), o,
+                                static_cast<int>(Hq * D), wo, d_model, y, d_model);
 }
 
 }  // namespace
@@ -304,64 +444,9 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
                         int32_t update_mode, void *out) {
   if (!h) return INFINI_ATTN_ERR_INVALID;
   const infini_attn_desc &d = h->desc;
-  int st = infini_attn_check(&d, seg_len, update_mode);
-  if (st != INFINI_ATTN_OK) return st;
-  if (d.batch == 0 || d.seq_len == 0) return INFINI_ATTN_OK;  // nothing to do; state unchanged
-  if (!q || !k || !v || !beta || !M || !z || !out) return INFINI_ATTN_ERR_INVALID;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
-    return INFINI_ATTN_ERR_INVALID;
-  if (!aligned(beta, 4) || !aligned(M, 4) || !aligned(z, 4)) return INFINI_ATTN_ERR_INVALID;
-
-  DeviceGuard guard(d.device);
-  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
-
-  ia::Geometry g;
-  g.B = d.batch;
-  g.Hq = d.n_q_heads;
-  g.Hkv = d.n_kv_heads;
-  g.L = d.seq_len;
-  g.D = d.d_k;
-  g.N = effective_seg(d.seq_len, seg_len);
-  g.S = n_segments(d.seq_len, g.N);
-  g.eps = d.eps;
-
-  ia::Workspace ws;
-  st = bind_workspace(h, g, &ws);
-  if (st != INFINI_ATTN_OK) return st;
-  const bool bf16 = d.dtype == INFINI_ATTN_BF16;
-
-  TimedCall tc{};
-  if (h->timing) {
-    if (!h->spare.empty()) {
-      tc = h->spare.back();
-      h->spare.pop_back();
-    } else {
-      for (int i = 0; i < 3; ++i) {
-        if (hipEventCreate(&tc.ev[i]) != hipSuccess) {
-          for (int j = 0; j < i; ++j) (void)hipEventDestroy(tc.ev[j]);
-          return INFINI_ATTN_ERR_HIP;
-        }
-      }
-    }
-    h->recorded.push_back(tc);
-    if (hipEventRecord(tc.ev[0], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
-  }
-  const int delta = update_mode == INFINI_ATTN_DELTA;
-  hipError_t e = launch_scan(h, g, k, v, M, z, delta, ws);
-  if (e != hipSuccess) return hip_status(e);
-  if (h->timing && hipEventRecord(tc.ev[1], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
-  if (bf16) {
-    e = ia::launch_fused_bf16(g, static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                              static_cast<const uint16_t *>(v), beta, ws,
-                              static_cast<uint16_t *>(out), h->stream);
-  } else {
-    e = ia::launch_fused_f32(g, static_cast<const float *>(q), static_cast<const float *>(k),
-                             static_cast<const float *>(v), beta, ws, static_cast<float *>(out),
-                             h->stream);
-  }
-  if (e != hipSuccess) return hip_status(e);
-  if (h->timing && hipEventRecord(tc.ev[2], h->stream) != hipSuccess) return INFINI_ATTN_ERR_HIP;
-  return hip_status(copy_final_z(h, g, z, ws));
+  const ia::Layout lq = ia::head_major(d.n_q_heads, d.seq_len, d.d_k);
+  const ia::Layout lkv = ia::head_major(d.n_kv_heads, d.seq_len, d.d_k);
+  return forward_impl(h, q, k, v, beta, M, z, seg_len, update_mode, out, lq, lkv, lq);
 }
 
 int infini_attn_update(infini_attn_t *h, const void *k, const void *v, float *M, float *z,
@@ -386,6 +471,8 @@ int infini_attn_update(infini_attn_t *h, const void *k, const void *v, float *M,
   g.N = rows;  // one segment
   g.S = 1;
   g.eps = d.eps;
+  g.lkv = ia::head_major(d.n_kv_heads, rows, d.d_k);
+  g.lq = g.lo = ia::head_major(d.n_q_heads, rows, d.d_k);
   ia::Workspace ws;
   st = bind_workspace(h, g, &ws);
   if (st != INFINI_ATTN_OK) return st;
@@ -409,56 +496,16 @@ int infini_attn_decode_noalloc(infini_attn_t *h, const void *q, int32_t n_new,
 int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, const void *wq,
                               const void *wk, const void *wv, const void *wo, const float *beta,
                               float *M, float *z, int32_t seg_len, int32_t update_mode, void *y) {
-  if (!h) return INFINI_ATTN_ERR_INVALID;
-  const infini_attn_desc &d = h->desc;
-  int st = infini_attn_check(&d, seg_len, update_mode);
-  if (st != INFINI_ATTN_OK) return st;
-  if (d_model < 1) return INFINI_ATTN_ERR_INVALID;
-  if (d.batch == 0 || d.seq_len == 0) return INFINI_ATTN_OK;
-  if (!x || !wq || !wk || !wv || !wo || !beta || !M || !z || !y) return INFINI_ATTN_ERR_INVALID;
-  const int64_t rows = static_cast<int64_t>(d.batch) * d.seq_len;
-  if (rows > INT32_MAX) return INFINI_ATTN_ERR_UNSUPPORTED;
-  DeviceGuard guard(d.device);
-  if (guard.err != hipSuccess) return INFINI_ATTN_ERR_HIP;
-  if (!h->blas) {
-    st = ia::blas_create(&h->blas, h->stream);
-    if (st != INFINI_ATTN_OK) return st;
-  }
-  const size_t elt = d.dtype == INFINI_ATTN_BF16 ? 2 : 4;
-  const int D = d.d_k, L = d.seq_len;
-  const size_t per_head = static_cast<size_t>(L) * D * elt;
-  const size_t nq = static_cast<size_t>(d.batch) * d.n_q_heads * per_head;
-  const size_t nkv = static_cast<size_t>(d.batch) * d.n_kv_heads * per_head;
-  // Q, K, V head-major; O; O' regrouped by rows (each part 256-byte aligned).
-  const size_t oq = 0, ok = round_up(nq), ov = ok + round_up(nkv), oo = ov + round_up(nkv),
-               oo2 = oo + round_up(nq);
-  st = ensure_buffer(&h->blk_ws, &h->blk_ws_bytes, oo2 + round_up(nq));
-  if (st != INFINI_ATTN_OK) return st;
-  char *base = static_cast<char *>(h->blk_ws);
-  char *q = base + oq, *k = base + ok, *v = base + ov, *o = base + oo, *o2 = base + oo2;
-  // Each projection as one GEMM over all B * L rows into the O' area (large
-  // enough for any of them, Hq >= Hkv), then regrouped head-major.
-  const int row_bytes = D * static_cast<int>(elt);
-  const struct {
-    const void *w;
-    int heads;
-    char *dst;
-  } proj[3] = {{wq, d.n_q_heads, q}, {wk, d.n_kv_heads, k}, {wv, d.n_kv_heads, v}};
-  for (const auto &pj : proj) {
-    st = ia::blas_gemm_rowmajor(h->blas, d.dtype, static_cast<int>(rows), pj.heads * D, d_model,
-                                x, d_model, pj.w, pj.heads * D, o2, 1);
-    if (st != INFINI_ATTN_OK) return st;
-    const hipError_t e = ia::launch_rows_to_heads(o2, pj.dst, d.batch, pj.heads, L, row_bytes,
-                                                  h->stream);
-    if (e != hipSuccess) return hip_status(e);
-  }
-  st = infini_attn_forward(h, q, k, v, beta, M, z, seg_len, update_mode, o);
-  if (st != INFINI_ATTN_OK) return st;
-  const hipError_t e = ia::launch_heads_to_rows(o, o2, d.batch, d.n_q_heads, L, row_bytes,
-                                                h->stream);
-  if (e != hipSuccess) return hip_status(e);
-  return ia::blas_gemm_rowmajor(h->blas, d.dtype, static_cast<int>(rows), d_model,
-                                d.n_q_heads * D, o2, d.n_q_heads * D, wo, d_model, y, 1);
+  if (!wq || !wk || !wv) return INFINI_ATTN_ERR_INVALID;
+  return block_call(h, d_model, x, wq, wk, wv, nullptr, wo, beta, M, z, seg_len, update_mode, y);
+}
+
+int infini_attn_block_forward_qkv(infini_attn_t *h, int32_t d_model, const void *x,
+                                  const void *wqkv, const void *wo, const float *beta, float *M,
+                                  float *z, int32_t seg_len, int32_t update_mode, void *y) {
+  if (!wqkv) return INFINI_ATTN_ERR_INVALID;
+  return block_call(h, d_model, x, nullptr, nullptr, nullptr, wqkv, wo, beta, M, z, seg_len,
+                    update_mode, y);
 }
 
 int infini_attn_set_timing(infini_attn_t *h, int32_t enable) {
@@ -542,6 +589,8 @@ int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const v
   g.N = effective_seg(d.seq_len, seg_len);
   g.S = n_segments(d.seq_len, g.N);
   g.eps = d.eps;
+  g.lq = g.lo = ia::head_major(d.n_q_heads, d.seq_len, d.d_k);
+  g.lkv = ia::head_major(d.n_kv_heads, d.seq_len, d.d_k);
   const int delta = update_mode == INFINI_ATTN_DELTA;
 
   // Scratch layout (each part 256-byte aligned): z_pre, mt, dzs, lse, erow,

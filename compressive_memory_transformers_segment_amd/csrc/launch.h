@@ -10,12 +10,31 @@
 
 namespace ia {
 
+// Where row i of head h of batch b of a q / k / v / out tensor starts, in
+// elements: b * sb + h * sh + i * sr (its d elements are contiguous). The C
+// ABI's tensors are head-major [B, H, L, d] (sb = H L d, sh = L d, sr = d);
+// the block hands the kernels its row-major projections [B, L, ..., H, d]
+// (sb = L W, sh = d, sr = W for rows of W elements) without regrouping them.
+struct Layout {
+  long long sb, sh, sr;
+};
+
+__host__ __device__ inline Layout head_major(int H, int L, int D) {
+  return Layout{static_cast<long long>(H) * L * D, static_cast<long long>(L) * D, D};
+}
+
+// Offset of row 0 of flattened head bh = b * H + h.
+__host__ __device__ inline long long head_offset(const Layout &l, int bh, int H) {
+  return (bh / H) * l.sb + (bh % H) * l.sh;
+}
+
 // Problem geometry of one forward call, already validated on the host.
 struct Geometry {
   int B, Hq, Hkv, L, D;  // D = d_k = d_v
   int N;                 // segment length
   int S;                 // number of segments, ceil(L / N)
   float eps;
+  Layout lq, lkv, lo;    // of q, of k and v, of out
 };
 
 // Per-segment state snapshots written by the scan and read by the fused
@@ -140,16 +159,12 @@ hipError_t launch_decode_f32(const DecodeGeometry &g, const float *q, const floa
                              const float *vc, const float *beta, const float *M, const float *z,
                              float *part, float *out, hipStream_t stream);
 
-// Infini-attention block: regrouping between [B][H][L][row] and [B][L][H][row]
-// (row_bytes 64, 128, 256 or 512), and the dense projections through rocBLAS
-// (statuses are INFINI_ATTN_* codes).
-hipError_t launch_heads_to_rows(const void *src, void *dst, int B, int H, int L, int row_bytes,
-                                hipStream_t stream);
-hipError_t launch_rows_to_heads(const void *src, void *dst, int B, int H, int L, int row_bytes,
-                                hipStream_t stream);
+// Infini-attention block: the dense projections through rocBLAS (statuses
+// are INFINI_ATTN_* codes). Row-major C (rows x n, leading dimension ldc) =
+// X (rows x k, ldx) W (k x n, ldw).
 int blas_create(void **blas, hipStream_t stream);
 void blas_destroy(void *blas);
 int blas_gemm_rowmajor(void *blas, int dtype, int rows, int n, int k, const void *x, int ldx,
-                       const void *w, int ldw, void *c, int batch);
+                       const void *w, int ldw, void *c, int ldc);
 
 }  // namespace ia

@@ -37,8 +37,8 @@ constexpr int scan_cols() { return kThreads / D > 4 ? kThreads / D : 4; }
 
 template <typename T, int D, int kCB>
 __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
-    const T *__restrict__ k, const T *__restrict__ v, float *__restrict__ M,
-    const float *__restrict__ z, int L, int N, int S, float eps, int delta,
+    const T *__restrict__ k, const T *__restrict__ v, Layout lkv, int Hkv,
+    float *__restrict__ M, const float *__restrict__ z, int L, int N, int S, float eps, int delta,
     float *__restrict__ z_pre, float *__restrict__ mt_f32, uint16_t *__restrict__ mt_bf16) {
   static_assert(D <= kThreads && kThreads % D == 0 && D % kCB == 0, "tile shape");
   constexpr int JSTEP = kThreads / D;  // threads sharing one row k of the state
@@ -56,8 +56,9 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
   const int cb = blockIdx.x;
   const int bh = blockIdx.y;  // b * Hkv + j
   const int c0 = cb * kCB;
-  const T *kb = k + static_cast<size_t>(bh) * L * D;
-  const T *vb = v + static_cast<size_t>(bh) * L * D;
+  // Row i of this head's k, v starts i * lkv.sr elements after kb, vb.
+  const T *kb = k + head_offset(lkv, bh, Hkv);
+  const T *vb = v + head_offset(lkv, bh, Hkv);
   float *Mb = M + static_cast<size_t>(bh) * D * D;
 
   // Ownership: thread t holds state rows kk = t % D, columns c0 + j0 + JSTEP*r.
@@ -77,13 +78,13 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int idx = t + r * kThreads, i = idx / D, c = idx % D;
-      pk[r] = i < rows ? load_as_f32(kb, static_cast<size_t>(i0 + i) * D + c) : 0.f;
+      pk[r] = i < rows ? load_as_f32(kb, static_cast<size_t>((i0 + i) * lkv.sr + c)) : 0.f;
     }
 #pragma unroll
     for (int r = 0; r < VPT; ++r) {
       const int idx = t + r * kThreads, i = idx / kCB, c = idx % kCB;
       pv[r] = (idx < kR * kCB && i < rows)
-                  ? load_as_f32(vb, static_cast<size_t>(i0 + i) * D + c0 + c) : 0.f;
+                  ? load_as_f32(vb, static_cast<size_t>((i0 + i) * lkv.sr + c0 + c)) : 0.f;
     }
   };
   if (L > 0) fetch(0, min(kR, min(N, L)));
@@ -171,7 +172,7 @@ hipError_t launch_scan_t(const Geometry &g, const T *k, const T *v, float *M, co
   constexpr int CB = scan_cols<D>();
   dim3 grid(D / CB, g.B * g.Hkv);
   segment_scan_kernel<T, D, CB><<<grid, kThreads, 0, stream>>>(
-      k, v, M, z, g.L, g.N, g.S, g.eps, delta,
+      k, v, g.lkv, g.Hkv, M, z, g.L, g.N, g.S, g.eps, delta,
       ws.z_pre, ws.mt_pre_f32, ws.mt_pre_bf16);
   return hipGetLastError();
 }

@@ -80,9 +80,9 @@ __device__ __forceinline__ void lds_barrier() {
 // launches (few segments) still spread over the chip; zprefix adds the parts.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void zsum_kernel(const uint16_t *__restrict__ k,
-                                                   float *__restrict__ dz, int L, int N, int S,
-                                                   int parts) {
+__global__ __launch_bounds__(256) void zsum_kernel(const uint16_t *__restrict__ k, Layout lk,
+                                                   int Hkv, float *__restrict__ dz, int L, int N,
+                                                   int S, int parts) {
   constexpr int CCH = D / 8;      // 16-byte chunks per row
   constexpr int RG = 256 / CCH;   // rows in flight per pass
   constexpr int UNROLL = 4;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void zsum_kernel(const uint16_t *__restrict__ 
   const int span = (e - a + parts - 1) / parts;
   const int pa = min(a + part * span, e), pe = min(pa + span, e);
   const int t = threadIdx.x, cc = t % CCH, rg = t / CCH;
-  const uint16_t *kp = k + static_cast<size_t>(head) * L * D + cc * 8;
+  const uint16_t *kp = k + head_offset(lk, head, Hkv) + cc * 8;
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void zsum_kernel(const uint16_t *__restrict__ 
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int row = i + u * RG;
-      w[u] = row < pe ? *reinterpret_cast<const u32x4 *>(kp + static_cast<size_t>(row) * D)
+      w[u] = row < pe ? *reinterpret_cast<const u32x4 *>(kp + row * lk.sr)
                       : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
@@ -193,6 +193,7 @@ __global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restr
 template <int D, bool DELTA, int CS, int RG>
 __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not restrict:
                                                       const uint16_t *v,  // see load_chunk
+                                                      Layout lkv, int Hkv,
                                                       const float *__restrict__ z_pre,
                                                       float *__restrict__ gh,
                                                       uint16_t *__restrict__ vt, int vt_tiles,
@@ -233,8 +234,8 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
   uint16_t *sKt = sStage[grp][0];
   uint16_t *sVt = sStage[grp][1];
   uint16_t *sWt = sStage[grp][NB - 1];  // delta only
-  const uint16_t *kp = k + static_cast<size_t>(head) * L * D;
-  const uint16_t *vp = v + static_cast<size_t>(head) * L * D;
+  const uint16_t *kp = k + head_offset(lkv, head, Hkv);
+  const uint16_t *vp = v + head_offset(lkv, head, Hkv);
   if (tid < D) sZ[tid] = z_pre[(static_cast<size_t>(head) * (S + 1) + s) * D + tid];
 
   f32x16 acc[PPW][ND];
@@ -281,9 +282,9 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
       __asm__ volatile("" ::: "memory");
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const size_t row = min(i0 + 4 * kg + r, e - 1);
-        st.k[r] = *reinterpret_cast<const u32x4 *>(kp + row * D + cc * 8);
-        st.v[r] = *reinterpret_cast<const u32x4 *>(vp + row * D + cc * 8);
+        const long long row = min(i0 + 4 * kg + r, e - 1);
+        st.k[r] = *reinterpret_cast<const u32x4 *>(kp + row * lkv.sr + cc * 8);
+        st.v[r] = *reinterpret_cast<const u32x4 *>(vp + row * lkv.sr + cc * 8);
       }
       __asm__ volatile("" ::: "memory");
     }
@@ -657,22 +658,23 @@ hipError_t launch_d(const Geometry &g, const uint16_t *k, const uint16_t *v, flo
   const dim3 ghgrid(g.S * (split ? 2 : 1), heads), seqgrid(D / 32, heads);
   // With the column split, two row groups per workgroup (512 threads) fill
   // the CU's wave slots; without it the accumulators leave room for one.
-  zsum_kernel<D><<<dim3(g.S * parts, heads), 256, 0, stream>>>(k, ws.dz, g.L, g.N, g.S, parts);
+  zsum_kernel<D><<<dim3(g.S * parts, heads), 256, 0, stream>>>(k, g.lkv, g.Hkv, ws.dz, g.L, g.N,
+                                                                g.S, parts);
   zprefix_kernel<<<heads, kZThreads, 0, stream>>>(z, ws.dz, ws.z_pre, g.S, D, parts);
   if (delta) {
     if (split)
-      gh_kernel<D, true, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+      gh_kernel<D, true, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh, ws.vt,
                                                         ws.vt_tiles, g.L, g.N, g.S, g.eps);
     else
-      gh_kernel<D, true, 1, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+      gh_kernel<D, true, 1, 1><<<ghgrid, 256, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh, ws.vt,
                                                         ws.vt_tiles, g.L, g.N, g.S, g.eps);
     seq_kernel<D, true><<<seqgrid, 64 * (D / 32), 0, stream>>>(ws.gh, M, ws.mt_pre_bf16, g.S);
   } else {
     if (split)
-      gh_kernel<D, false, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+      gh_kernel<D, false, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh, ws.vt,
                                                          ws.vt_tiles, g.L, g.N, g.S, g.eps);
     else
-      gh_kernel<D, false, 1, 1><<<ghgrid, 256, 0, stream>>>(k, v, ws.z_pre, ws.gh, ws.vt,
+      gh_kernel<D, false, 1, 1><<<ghgrid, 256, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh, ws.vt,
                                                          ws.vt_tiles, g.L, g.N, g.S, g.eps);
     seq_kernel<D, false><<<seqgrid, 64 * (D / 32), 0, stream>>>(ws.gh, M, ws.mt_pre_bf16, g.S);
   }

@@ -2,7 +2,9 @@
 
     python -m compressive_memory_transformers_segment_amd.traffic \\
         --fetch FETCH_DIR --write WRITE_DIR --workload NAME --mode delta \\
-        --copy-bytes 1073741824 --command "<the profiled command>" > profiles/traffic_NAME_MODE.txt
+        --copy-bytes 1073741824 --command "<the profiled command>"
+    python -m compressive_memory_transformers_segment_amd.traffic --trace TRACE_DIR \\
+        --workload NAME --mode delta --command "<the profiled command>"
 
 Each directory holds the ``*counter_collection.csv`` of one ``rocprofv3 --pmc``
 run (``FETCH_SIZE`` in one, ``WRITE_SIZE`` in the other; the counters read KiB
@@ -152,16 +154,55 @@ def load(workload: str, mode: str) -> Optional[Dict[str, Dict[str, float]]]:
     return out or None
 
 
+def trace_table(directory: str, workload: str, mode: str, command: str) -> str:
+    """Markdown table of the library's kernels from a ``rocprofv3 --kernel-trace
+    --stats`` run (its ``*kernel_stats.csv``), longest first."""
+    files = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no kernel_stats.csv under {directory}")
+    rows = []
+    with open(files[0], newline="") as fh:
+        for r in csv.DictReader(fh):
+            name = short_name(r["Name"])
+            if _sources_for(name) is None:
+                continue
+            rows.append((float(r["TotalDurationNs"]), name, int(r["Calls"]),
+                         float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3))
+    rows.sort(reverse=True)
+    out = [f"# Kernel trace: workload {workload}, {mode} rule", "",
+           "Command (repository root, one MI355X, `rocprofv3`, `TMPDIR=/tmp`):", "", "```",
+           f"rocprofv3 --kernel-trace --stats {command}", "```", "",
+           "Library kernels from `kernel_stats.csv` (warm-up and timed calls; torch's own "
+           "kernels left out). The tracer slows the kernels down; bench lines are timed "
+           "without it.", "",
+           "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for _, name, calls, avg, mn, mx in rows:
+        out.append(f"| `{name}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--copy-bytes", type=int, required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-bytes", type=int)
+    ap.add_argument("--trace", help="format a --kernel-trace --stats run instead")
     ap.add_argument("--workload", required=True)
     ap.add_argument("--mode", required=True)
     ap.add_argument("--command", required=True)
-    ap.add_argument("--out", default=None, help="default: profiles/traffic_<workload>_<mode>.txt")
+    ap.add_argument("--out", default=None, help="default: profiles/traffic_<workload>_<mode>.txt "
+                                                 "(profiles/kernels_<workload>_<mode>.md with --trace)")
     a = ap.parse_args(argv)
+    if a.trace:
+        text = trace_table(a.trace, a.workload, a.mode, a.command)
+        dst = a.out or os.path.join(PROFILES, f"kernels_{a.workload}_{a.mode}.md")
+        with open(dst, "w") as fh:
+            fh.write(text)
+        sys.stdout.write(text)
+        return 0
+    if not (a.fetch and a.write and a.copy_bytes):
+        ap.error("--fetch, --write and --copy-bytes are required")
     text = summarize(a.fetch, a.write, a.copy_bytes, a.workload, a.mode, a.command)
     dst = a.out or path_for(a.workload, a.mode)
     with open(dst, "w") as fh:

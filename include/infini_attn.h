@@ -222,14 +222,29 @@ int infini_attn_update(infini_attn_t *h, const void *k, const void *v, float *M,
  *   beta, M, z, seg_len, update_mode as for infini_attn_forward (M, z in/out)
  *   y   [B, L, d_model]        dtype (device), written
  * The projections run on rocBLAS with fp32 accumulation, and Q, K, V, O are
- * rounded to dtype. The handle keeps Q, K, V, O and O' in its own scratch,
- * grown on demand, and a rocBLAS handle on its stream.
+ * rounded to dtype. Q, K and V land side by side in one row-major buffer
+ * [B, L, (Hq + 2 Hkv) d] that the attention kernels read in place, and O is
+ * written row-major [B, L, Hq d] for the output projection; nothing is
+ * regrouped. The handle keeps these two buffers in its own scratch, grown on
+ * demand, and a rocBLAS handle on its stream.
  * Errors: as infini_attn_forward; ERR_INVALID also for d_model < 1;
  * ERR_UNSUPPORTED for B * L > 2^31 - 1.
  */
 int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, const void *wq,
                               const void *wk, const void *wv, const void *wo, const float *beta,
                               float *M, float *z, int32_t seg_len, int32_t update_mode, void *y);
+
+/*
+ * The same block with the three projection weights fused into one matrix, as
+ * models that store a single query-key-value projection keep them:
+ *   wqkv [d_model, (Hq + 2 Hkv) d_k] dtype, row-major (device): columns
+ *        0 .. Hq d - 1 are Wq, then Hkv d columns of Wk, then Hkv d of Wv
+ * so that Q, K and V come from one GEMM. Every other argument, the result and
+ * the errors are those of infini_attn_block_forward.
+ */
+int infini_attn_block_forward_qkv(infini_attn_t *h, int32_t d_model, const void *x,
+                                  const void *wqkv, const void *wo, const float *beta, float *M,
+                                  float *z, int32_t seg_len, int32_t update_mode, void *y);
 
 /*
  * Backward pass of infini_attn_forward: the gradients of
