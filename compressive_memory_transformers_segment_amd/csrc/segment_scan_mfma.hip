@@ -128,22 +128,24 @@ __global__ __launch_bounds__(256) void zsum_kernel(const uint16_t *__restrict__ 
 
 // ---------------------------------------------------------------------------
 // zprefix: z_pre[head][s] = z_{s-1} (the state before segment s), slot S = z_S.
-// One workgroup per head; thread (grp, c) owns column c of a contiguous range
-// of segments. Pass 1 sums the range, the workgroup prefix-sums the ranges in
-// LDS, pass 2 writes the running value. dz is read in batches of kZB
-// independent loads so that the sequential part waits on memory only once
-// per batch.
+// One workgroup per (32-column block, head); thread (grp, c) owns column c of
+// a contiguous range of segments. Pass 1 sums the range, the workgroup
+// prefix-sums the ranges in LDS, pass 2 writes the running value. dz is read
+// in batches of kZB independent loads so that the sequential part waits on
+// memory only once per batch.
 // ---------------------------------------------------------------------------
 constexpr int kZB = 16;
 constexpr int kZThreads = 1024;
+constexpr int kZCols = 32;  // columns per workgroup
 
 __global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restrict__ z0,
                                                             const float *__restrict__ dz,
                                                             float *__restrict__ z_pre, int S,
                                                             int D, int parts) {
   __shared__ float tot[kZThreads];
-  const int head = blockIdx.x, G = kZThreads / D;
-  const int c = threadIdx.x % D, grp = threadIdx.x / D;
+  const int head = blockIdx.y, G = kZThreads / kZCols;
+  const int cl = threadIdx.x % kZCols, grp = threadIdx.x / kZCols;
+  const int c = blockIdx.x * kZCols + cl;
   const int per = (S + G - 1) / G;
   const int s0 = min(grp * per, S), s1 = min(s0 + per, S);
   const int f0 = s0 * parts, f1 = s1 * parts;  // flat (segment, part) range
@@ -157,10 +159,10 @@ __global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restr
 #pragma unroll
     for (int i = 0; i < kZB; ++i) sum += x[i];
   }
-  tot[grp * D + c] = sum;
+  tot[grp * kZCols + cl] = sum;
   __syncthreads();
   float z = z0[static_cast<size_t>(head) * D + c];
-  for (int q = 0; q < grp; ++q) z += tot[q * D + c];
+  for (int q = 0; q < grp; ++q) z += tot[q * kZCols + cl];
 
   float *out = z_pre + static_cast<size_t>(head) * (S + 1) * D + c;
   for (int f = f0; f < f1; f += kZB) {
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restr
   }
   if (grp == G - 1) {
     float zs = z0[static_cast<size_t>(head) * D + c];
-    for (int q = 0; q < G; ++q) zs += tot[q * D + c];
+    for (int q = 0; q < G; ++q) zs += tot[q * kZCols + cl];
     out[static_cast<size_t>(S) * D] = zs;
   }
 }
@@ -496,7 +498,16 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *gh,  //
   constexpr int MS = D + 4;  // sMh / sMl row stride (bf16)
   __shared__ __attribute__((aligned(16))) uint16_t sMh[DELTA ? 32 * MS : 4];
   __shared__ __attribute__((aligned(16))) uint16_t sMl[DELTA ? 32 * MS : 4];
-  const int jt = blockIdx.x, head = blockIdx.y;
+  // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
+  // All column tiles of a head read the whole G_s, so when the grid allows it
+  // they are placed on one XCD: linear id (8 (jt + ND h8) + h % 8), with h8 =
+  // h / 8, holds tile jt of head h.
+  int jt = blockIdx.x, head = blockIdx.y;
+  if (gridDim.y % 8 == 0) {
+    const int id = blockIdx.y * ND + blockIdx.x;
+    jt = (id >> 3) % ND;
+    head = (id & 7) + 8 * ((id >> 3) / ND);
+  }
   const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int j = 32 * jt + l32;
@@ -660,7 +671,8 @@ hipError_t launch_d(const Geometry &g, const uint16_t *k, const uint16_t *v, flo
   // the CU's wave slots; without it the accumulators leave room for one.
   zsum_kernel<D><<<dim3(g.S * parts, heads), 256, 0, stream>>>(k, g.lkv, g.Hkv, ws.dz, g.L, g.N,
                                                                 g.S, parts);
-  zprefix_kernel<<<heads, kZThreads, 0, stream>>>(z, ws.dz, ws.z_pre, g.S, D, parts);
+  zprefix_kernel<<<dim3(D / kZCols, heads), kZThreads, 0, stream>>>(z, ws.dz, ws.z_pre, g.S, D,
+                                                                     parts);
   if (delta) {
     if (split)
       gh_kernel<D, true, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh, ws.vt,
