@@ -86,8 +86,11 @@ int effective_seg(int L, int seg_len) { return (L > 0 && seg_len > L) ? L : seg_
 //   gh     [B*Hkv][S][2][D][D] fp32 (bf16 storage only)
 //   vt     [B*Hkv][S][T][D][64] bf16 (bf16 storage only; T = ceil(N / 64)
 //          64-key tiles per segment, V^T in the fused kernel's LDS layout)
+//   chain  (bf16 storage, chains of 64+ segments) per chunk: [P | h], the
+//          packed affine step and the state before the chunk, all fp32
 struct WsLayout {
-  size_t z, mt, dz, gh, vt, total;
+  size_t z, mt, dz, gh, vt, chain_x, chain_gh, chain_states, total;
+  int chunk_len;
 };
 
 int vt_tiles(int N) { return (N + 63) / 64; }
@@ -108,7 +111,12 @@ WsLayout ws_layout(const infini_attn_desc *d, int S, int N) {
   w.dz = bf16 ? round_up(heads * S * z_parts(N) * D * sizeof(float)) : 0;
   w.gh = bf16 ? round_up(heads * S * 2 * D * D * sizeof(float)) : 0;
   w.vt = bf16 ? round_up(heads * S * vt_tiles(N) * D * 64 * sizeof(uint16_t)) : 0;
-  w.total = w.z + w.mt + w.dz + w.gh + w.vt;
+  w.chunk_len = bf16 ? ia::chain_chunk_len(S, static_cast<int>(heads)) : 0;
+  const size_t nc = w.chunk_len > 0 ? (S + w.chunk_len - 1) / w.chunk_len : 0;
+  w.chain_x = round_up(heads * nc * D * 2 * D * sizeof(float));
+  w.chain_gh = round_up(heads * nc * 2 * D * D * sizeof(float));
+  w.chain_states = round_up(heads * nc * D * D * sizeof(float));
+  w.total = w.z + w.mt + w.dz + w.gh + w.vt + w.chain_x + w.chain_gh + w.chain_states;
   return w;
 }
 
@@ -167,6 +175,12 @@ int bind_workspace(infini_attn_handle *h, const ia::Geometry &g, ia::Workspace *
   ws->gh = bf16 ? reinterpret_cast<float *>(base + lay.z + lay.mt + lay.dz) : nullptr;
   ws->vt = bf16 ? reinterpret_cast<uint16_t *>(base + lay.z + lay.mt + lay.dz + lay.gh) : nullptr;
   ws->vt_tiles = vt_tiles(g.N);
+  char *chain = base + lay.z + lay.mt + lay.dz + lay.gh + lay.vt;
+  ws->chunk_len = lay.chunk_len;
+  ws->chain_x = lay.chunk_len > 0 ? reinterpret_cast<float *>(chain) : nullptr;
+  ws->chain_gh = lay.chunk_len > 0 ? reinterpret_cast<float *>(chain + lay.chain_x) : nullptr;
+  ws->chain_states =
+      lay.chunk_len > 0 ? reinterpret_cast<float *>(chain + lay.chain_x + lay.chain_gh) : nullptr;
   return INFINI_ATTN_OK;
 }
 

@@ -48,7 +48,21 @@ struct Workspace {
   float *gh;              // [B*Hkv][S][2][D*D] G_s, H_s in MFMA fragment order (bf16 path)
   uint16_t *vt;           // [B*Hkv][S][vt_tiles][D*64] V^T per 64-key tile (bf16 path)
   int vt_tiles;           // 64-key tiles per segment, ceil(N / 64)
+  // Chunked scan of the delta rule's chain (bf16 path, long chains only):
+  // chunk_len segments per chunk (0: one sequential chain), and per chunk
+  // [P | h] (D x 2D fp32), its packed affine step (G', H' fragments) and the
+  // fp32 state before it.
+  int chunk_len;
+  float *chain_x;       // [B*Hkv][chunks][D][2D]
+  float *chain_gh;      // [B*Hkv][chunks][2][D*D]
+  float *chain_states;  // [B*Hkv][chunks][D][D]
 };
+
+// Segments per chunk of the chunked chain scan for S segments of B * Hkv
+// heads, or 0 when one sequential chain is used: chains of at least 64
+// segments are split into about sqrt(S / 2) segments a chunk, which balances
+// the two chunk-parallel passes against the sequential pass over the chunks.
+int chain_chunk_len(int S, int heads);
 
 // Layout of one 64-key V^T tile (bf16 path), written by the scan and copied
 // verbatim into LDS by the fused kernel. Row d (one per value column) holds

@@ -488,34 +488,87 @@ __global__ __launch_bounds__(256 * RG) void gh_kernel(const uint16_t *k,  // not
 // The tile's current state is also kept in LDS, transposed, as bf16 hi and lo
 // parts (sMh[n][c], sMl[n][c]: column n of the tile, row c of M), which is the
 // B operand of G_s M_{s-1}. Its hi part is the bf16 snapshot M_{s-1}^T.
+//
+// The affine steps M_s = (I - G_s) M_{s-1} + H_s compose associatively, so a
+// long chain is also run as a chunked scan (modes below, chunks of C
+// segments): PRODUCT runs every chunk at once from the states [I | 0],
+// giving X_c = [P_c | h_c] with P_c the product of the chunk's (I - G_s) and
+// h_c its chain from zero; chain_pack_kernel turns each into one affine step
+// (G' = I - P_c, H' = h_c); CHAIN runs those steps over the chunks,
+// recording the fp32 state before each chunk; APPLY reruns every chunk at
+// once from its recorded state and writes the per-segment snapshots.
+//   FULL     grid (D/32, heads): segments 0 .. S - 1 from M, snapshots, M_S.
+//   PRODUCT  grid (2 D/32, heads x chunks): tile jt < D/32 is column tile jt
+//            of P_c (starts as I, no H), tile D/32 + jt that of h_c (starts
+//            at 0); writes X [heads][chunks][D][2D] (fp32, row-major).
+//   CHAIN    grid (D/32, heads): steps over the chunks (gh = packed steps),
+//            fp32 state before each chunk into states, M_S into M.
+//   APPLY    grid (D/32, heads x chunks): from states, the chunk's segments,
+//            snapshots.
 // ---------------------------------------------------------------------------
-template <int D, bool DELTA>
-__global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *gh,  // not restrict: see step()
-                                                           float *__restrict__ M,
-                                                           uint16_t *__restrict__ mt_pre,
-                                                           int S) {
+enum SeqMode { kSeqFull = 0, kSeqProduct = 1, kSeqChain = 2, kSeqApply = 3 };
+
+struct SeqArgs {
+  const float *gh;   // [heads][S][2][D*D] fragments of (G_s, H_s) (CHAIN: packed chunk steps)
+  int S;             // steps per head in gh
+  int C;             // segments per chunk (PRODUCT, APPLY)
+  int nchunks;       // chunks per head (PRODUCT, APPLY)
+  float *M;          // FULL, CHAIN: initial state in, final state out
+  uint16_t *mt_pre;  // FULL, APPLY: bf16 M^T before each segment [heads][S][D][D]
+  float *states;     // CHAIN (out), APPLY (in): fp32 state before each chunk [heads][chunks][D][D]
+  float *X;          // PRODUCT (out): [heads][chunks][D][2D]
+};
+
+template <int D, bool DELTA, int MODE>
+__global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(SeqArgs args) {
   constexpr int ND = D / 32;
   constexpr int MS = D + 4;  // sMh / sMl row stride (bf16)
+  static_assert(DELTA || MODE == kSeqFull, "chunked modes are for the delta rule");
   __shared__ __attribute__((aligned(16))) uint16_t sMh[DELTA ? 32 * MS : 4];
   __shared__ __attribute__((aligned(16))) uint16_t sMl[DELTA ? 32 * MS : 4];
+  // (gh is not restrict: see step().)
+  const float *gh = args.gh;
+  const int S = args.S;
   // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
   // All column tiles of a head read the whole G_s, so when the grid allows it
-  // they are placed on one XCD: linear id (8 (jt + ND h8) + h % 8), with h8 =
-  // h / 8, holds tile jt of head h.
-  int jt = blockIdx.x, head = blockIdx.y;
+  // they are placed on one XCD: linear id (8 (jt + nt u8) + u % 8), with u8 =
+  // u / 8, holds tile jt of unit u (a head, or a (head, chunk) pair).
+  // (PRODUCT and APPLY: the same for the tiles of one (head, chunk) unit.)
+  int jt = blockIdx.x, unit = blockIdx.y, chunk = 0;
   if (gridDim.y % 8 == 0) {
-    const int id = blockIdx.y * ND + blockIdx.x;
-    jt = (id >> 3) % ND;
-    head = (id & 7) + 8 * ((id >> 3) / ND);
+    const int nt = gridDim.x;  // column tiles per unit
+    const int id = blockIdx.y * nt + blockIdx.x;
+    jt = (id >> 3) % nt;
+    unit = (id & 7) + 8 * ((id >> 3) / nt);
   }
+  int head = unit;
+  if (MODE == kSeqProduct || MODE == kSeqApply) {
+    head = unit / args.nchunks;
+    chunk = unit % args.nchunks;
+  }
+  const int s_begin = (MODE == kSeqProduct || MODE == kSeqApply) ? chunk * args.C : 0;
+  const int s_end = (MODE == kSeqProduct || MODE == kSeqApply) ? min(s_begin + args.C, S) : S;
   const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
+  // This tile's columns of the state (PRODUCT: of [P | h]) and of H.
   const int j = 32 * jt + l32;
-  float *Mh = M + static_cast<size_t>(head) * D * D;
+  const int jh = (MODE == kSeqProduct) ? 32 * (jt % ND) + l32 : j;
+  const bool add_h = MODE != kSeqProduct || jt >= ND;
 
   f32x16 m;
+  if (MODE == kSeqFull || MODE == kSeqChain) {
+    const float *Mh = args.M + static_cast<size_t>(head) * D * D;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) m[r] = Mh[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j];
+    for (int r = 0; r < 16; ++r) m[r] = Mh[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j];
+  } else if (MODE == kSeqApply) {
+    const float *X0 =
+        args.states + (static_cast<size_t>(head) * args.nchunks + chunk) * D * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m[r] = X0[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m[r] = (jt < ND && 32 * ct + kappa(r, g) == j) ? 1.f : 0.f;
+  }
 
   // The state before segment st: the global bf16 snapshot M_{st-1}^T (st < S)
   // and, for the delta rule, the hi/lo operand copy in LDS. This lane holds
@@ -526,7 +579,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *gh,  //
   // second), so that each lane stores 8 contiguous values: rows
   // 32 ct + 16 p + 8 g + 0..7, one 16-byte store per p.
   auto snapshot = [&](int st) __attribute__((always_inline)) {
-    uint16_t *mt = mt_pre + (static_cast<size_t>(head) * S + st) * D * D +
+    if (MODE == kSeqChain) {
+      // fp32 state before chunk st, row-major.
+      float *xs = args.states + (static_cast<size_t>(head) * S + st) * D * D + j;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xs[static_cast<size_t>(32 * ct + kappa(r, g)) * D] = m[r];
+      return;
+    }
+    if (MODE == kSeqProduct) return;
+    uint16_t *mt = args.mt_pre + (static_cast<size_t>(head) * S + st) * D * D +
                    static_cast<size_t>(j) * D + 32 * ct + 8 * g;
     uint32_t wd[4][2];
 #pragma unroll
@@ -562,22 +623,26 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *gh,  //
 
   // G_s / H_s fragments of a step, loaded R - 1 steps ahead through a ring of
   // R register sets (the loop is unrolled R times, so the sets do not move):
-  // 3 for the delta rule (80 registers a set), 8 for the linear rule (16). G: 4
+  // 3 for the delta rule's chains (80 registers a set), 8 for the linear rule
+  // (16). G: 4
   // operand vectors (hi h = 0, 1, lo h = 0, 1) per 32-row tile kt of the
   // contraction; H: this lane's 16 values. Every step issues its loads (past
-  // the last segment it reloads the last one), so that the wait before a
-  // step's work covers exactly the loads R - 1 steps old.
+  // the last segment of the range it reloads the last one), so that the wait
+  // before a step's work covers exactly the loads R - 1 steps old.
+  // (The chunk-parallel passes run thousands of independent workgroups,
+  // whose latencies overlap each other: they keep a shorter ring, so that two
+  // waves fit on a SIMD.)
   constexpr int NG = DELTA ? ND : 1;
-  constexpr int R = DELTA ? 3 : 8;
+  constexpr int R = (MODE == kSeqProduct || MODE == kSeqApply) ? 2 : (DELTA ? 3 : 8);
   struct Frags {
     u32x4 g[NG][4];
     f32x4 h[4];
   };
   auto load_step = [&](int st, Frags &f) __attribute__((always_inline)) {
-    st = min(st, S - 1);
+    st = min(st, s_end - 1);
     const float *ghs = gh + (static_cast<size_t>(head) * S + st) * 2 * D * D;
     const f32x4 *hf = reinterpret_cast<const f32x4 *>(ghs + static_cast<size_t>(D) * D) +
-                      (ct * ND + jt) * 256 + lane;
+                      (ct * ND + jh / 32) * 256 + lane;
 #pragma unroll
     for (int q = 0; q < 4; ++q) f.h[q] = hf[64 * q];
     if constexpr (DELTA) {
@@ -621,8 +686,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *gh,  //
         }
       }
       lds_barrier();  // every wave has read M_{s-1} from LDS
+      if (add_h) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) m[r] = m[r] - acc[r] + cur.h[r / 4][r % 4];
+        for (int r = 0; r < 16; ++r) m[r] = m[r] - acc[r] + cur.h[r / 4][r % 4];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m[r] = m[r] - acc[r];
+      }
       operand();
       lds_barrier();
     } else {
@@ -632,9 +702,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *gh,  //
   };
 
   Frags f[R];
-  if (S > 0) {
+  if (s_end > s_begin) {
 #pragma unroll
-    for (int r = 0; r + 1 < R; ++r) load_step(r, f[r]);
+    for (int r = 0; r + 1 < R; ++r) load_step(s_begin + r, f[r]);
     if constexpr (DELTA) {
       operand();
       lds_barrier();
@@ -642,20 +712,69 @@ __global__ __launch_bounds__(64 * (D / 32)) void seq_kernel(const float *gh,  //
     // Whole rounds of R steps, then the rest (fewer than R). The rounds have
     // no exits inside, so every path into the loop head has the same loads in
     // flight and the waits stay exact.
-    int s = 0;
-    for (; s + R <= S; s += R) {
+    int s = s_begin;
+    for (; s + R <= s_end; s += R) {
 #pragma unroll
       for (int r = 0; r < R; ++r) step(s + r, f[r], f[(r + R - 1) % R]);
     }
 #pragma unroll
     for (int r = 0; r + 1 < R; ++r)
-      if (s + r < S) step(s + r, f[r], f[(r + R - 1) % R]);
+      if (s + r < s_end) step(s + r, f[r], f[(r + R - 1) % R]);
   }
+  if (MODE == kSeqFull || MODE == kSeqChain) {
+    float *Mh = args.M + static_cast<size_t>(head) * D * D;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) Mh[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j] = m[r];
+    for (int r = 0; r < 16; ++r) Mh[static_cast<size_t>(32 * ct + kappa(r, g)) * D + j] = m[r];
+  } else if (MODE == kSeqProduct) {
+    float *Xc = args.X + (static_cast<size_t>(head) * args.nchunks + chunk) * D * (2 * D) + j;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Xc[static_cast<size_t>(32 * ct + kappa(r, g)) * (2 * D)] = m[r];
+  }
   // The loads issued past the last segment land before the wave ends (vmcnt 0,
   // lgkmcnt 0, expcnt at its maximum; gfx9 s_waitcnt encoding).
   __builtin_amdgcn_s_waitcnt(7 << 4);
+}
+
+// One affine step per chunk from X_c = [P_c | h_c]: G' = I - P_c, stored
+// transposed in the G fragment format (the recurrence reads tile (kt, ct)
+// of G as its operand for output rows ct, contracting over the rows of tile
+// kt, i.e. it applies the transpose of what is stored), as bf16 hi/lo words;
+// H' = h_c in the H fragment format (fp32). One thread per (unit, tile, lane).
+template <int D>
+__global__ __launch_bounds__(256) void chain_pack_kernel(const float *__restrict__ X,
+                                                         float *__restrict__ gh2, int units) {
+  constexpr int ND = D / 32;
+  const long long tid = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (tid >= static_cast<long long>(units) * ND * ND * 64) return;
+  const int lane = static_cast<int>(tid % 64);
+  const int tile = static_cast<int>((tid / 64) % (ND * ND));
+  const size_t unit = static_cast<size_t>(tid / (64 * ND * ND));
+  const int rt = tile / ND, ct = tile % ND;
+  const int g = lane >> 5, l32 = lane & 31;
+  const float *Xu = X + unit * D * (2 * D);
+  float gv[16], hv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 32 * rt + kappa(r, g), col = 32 * ct + l32;
+    // stored element (row, col) of G' = (I - P)[col][row]
+    gv[r] = (row == col ? 1.f : 0.f) - Xu[static_cast<size_t>(col) * (2 * D) + row];
+    hv[r] = Xu[static_cast<size_t>(row) * (2 * D) + D + col];
+  }
+  float *base = gh2 + unit * 2 * D * D;
+  uint32_t wd[16];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t hw = pack_bf16x2(gv[2 * q], gv[2 * q + 1]);
+    wd[q] = hw;
+    wd[8 + q] = pack_bf16x2(gv[2 * q] - lo_bf16(hw), gv[2 * q + 1] - hi_bf16(hw));
+  }
+  u32x4 *fg = reinterpret_cast<u32x4 *>(base) + tile * 256 + lane;
+  f32x4 *fh = reinterpret_cast<f32x4 *>(base + static_cast<size_t>(D) * D) + tile * 256 + lane;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    fg[64 * q] = u32x4{wd[4 * q], wd[4 * q + 1], wd[4 * q + 2], wd[4 * q + 3]};
+    fh[64 * q] = f32x4{hv[4 * q], hv[4 * q + 1], hv[4 * q + 2], hv[4 * q + 3]};
+  }
 }
 
 template <int D>
@@ -675,25 +794,54 @@ hipError_t launch_d(const Geometry &g, const uint16_t *k, const uint16_t *v, flo
                                                                      parts);
   if (delta) {
     if (split)
-      gh_kernel<D, true, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh, ws.vt,
-                                                        ws.vt_tiles, g.L, g.N, g.S, g.eps);
+      gh_kernel<D, true, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh,
+                                                        ws.vt, ws.vt_tiles, g.L, g.N, g.S, g.eps);
     else
-      gh_kernel<D, true, 1, 1><<<ghgrid, 256, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh, ws.vt,
-                                                        ws.vt_tiles, g.L, g.N, g.S, g.eps);
-    seq_kernel<D, true><<<seqgrid, 64 * (D / 32), 0, stream>>>(ws.gh, M, ws.mt_pre_bf16, g.S);
+      gh_kernel<D, true, 1, 1><<<ghgrid, 256, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh,
+                                                        ws.vt, ws.vt_tiles, g.L, g.N, g.S, g.eps);
+    SeqArgs a{ws.gh, g.S, 0, 0, M, ws.mt_pre_bf16, nullptr, nullptr};
+    if (ws.chunk_len > 0) {
+      // Chunked scan of the affine chain (see seq_kernel).
+      const int C = ws.chunk_len, nc = (g.S + C - 1) / C;
+      const long long units = static_cast<long long>(heads) * nc;
+      a.C = C;
+      a.nchunks = nc;
+      a.X = ws.chain_x;
+      seq_kernel<D, true, kSeqProduct><<<dim3(2 * D / 32, static_cast<unsigned>(units)),
+                                         64 * (D / 32), 0, stream>>>(a);
+      const long long threads = units * (D / 32) * (D / 32) * 64;
+      chain_pack_kernel<D><<<static_cast<unsigned>((threads + 255) / 256), 256, 0, stream>>>(
+          ws.chain_x, ws.chain_gh, static_cast<int>(units));
+      SeqArgs c{ws.chain_gh, nc, 0, 0, M, nullptr, ws.chain_states, nullptr};
+      seq_kernel<D, true, kSeqChain><<<seqgrid, 64 * (D / 32), 0, stream>>>(c);
+      a.states = ws.chain_states;
+      seq_kernel<D, true, kSeqApply><<<dim3(D / 32, static_cast<unsigned>(units)), 64 * (D / 32),
+                                       0, stream>>>(a);
+    } else {
+      seq_kernel<D, true, kSeqFull><<<seqgrid, 64 * (D / 32), 0, stream>>>(a);
+    }
   } else {
     if (split)
-      gh_kernel<D, false, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh, ws.vt,
-                                                         ws.vt_tiles, g.L, g.N, g.S, g.eps);
+      gh_kernel<D, false, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh,
+                                                         ws.vt, ws.vt_tiles, g.L, g.N, g.S, g.eps);
     else
-      gh_kernel<D, false, 1, 1><<<ghgrid, 256, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh, ws.vt,
-                                                         ws.vt_tiles, g.L, g.N, g.S, g.eps);
-    seq_kernel<D, false><<<seqgrid, 64 * (D / 32), 0, stream>>>(ws.gh, M, ws.mt_pre_bf16, g.S);
+      gh_kernel<D, false, 1, 1><<<ghgrid, 256, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh,
+                                                         ws.vt, ws.vt_tiles, g.L, g.N, g.S, g.eps);
+    SeqArgs a{ws.gh, g.S, 0, 0, M, ws.mt_pre_bf16, nullptr, nullptr};
+    seq_kernel<D, false, kSeqFull><<<seqgrid, 64 * (D / 32), 0, stream>>>(a);
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+int chain_chunk_len(int S, int heads) {
+  if (S < 64) return 0;
+  int C = static_cast<int>(sqrtf(static_cast<float>(S) / 2.f) + 0.5f);
+  C = C < 4 ? 4 : C;
+  const long long units = static_cast<long long>(heads) * ((S + C - 1) / C);
+  return units > 65535 ? 0 : C;
+}
 
 hipError_t launch_segment_scan_bf16(const Geometry &g, const uint16_t *k, const uint16_t *v,
                                     float *M, const float *z, int delta, const Workspace &ws,

@@ -37,6 +37,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # Kernel name pattern -> sources it is built from (besides the shared headers).
 KERNEL_SOURCES = [
+    (r"chain_pack_kernel", ["segment_scan_mfma.hip"]),
     (r"fused_bf16_kernel", ["fused_bf16.hip"]),
     (r"fused_f32_kernel", ["fused_f32.hip"]),
     (r"segment_scan_kernel", ["segment_scan.hip"]),

@@ -136,6 +136,31 @@ def test_segment_counts_around_the_scan_ring(S, d, mode):
               run_oracle(inp, "bf16", 64, mode), "bf16")
 
 
+@pytest.mark.parametrize("S,d,hq,hkv", [(63, 64, 2, 1), (64, 32, 2, 2), (100, 64, 4, 2),
+                                         (131, 128, 2, 1), (200, 32, 2, 1)])
+def test_long_chains_take_the_chunked_scan(S, d, hq, hkv):
+    """Chains of 64 segments and more run the delta rule's recurrence as a
+    chunked scan (per-chunk products in parallel, a chain over the chunks,
+    then every chunk again from its start state): 63 segments (one chain),
+    64 (chunks of 6, a short last chunk), 100, 131 and 200 segments, grouped
+    heads and a short last segment, against the oracle's segment loop."""
+    inp = synth.random_case(450 + S + d, B=1, Hq=hq, Hkv=hkv, L=16 * S - 5, dk=d, dv=d,
+                            dtype="bf16", nonzero_state=True, scale=1.5 / np.sqrt(d) * 4)
+    log(f"chunked scan S={S} d={d} Hq={hq} Hkv={hkv}")
+    check_all(f"chunked S={S} d{d}", run_gpu(inp, "bf16", 16, "delta"),
+              run_oracle(inp, "bf16", 16, "delta"), "bf16")
+
+
+def test_long_chain_from_zero_state():
+    """A chunked chain from M0 = 0, z0 = 0, where the first write divides by
+    eps alone and the first chunk's product is huge, times a zero state."""
+    inp = synth.random_case(470, B=1, Hq=2, Hkv=1, L=16 * 96, dk=64, dv=64, dtype="bf16",
+                            scale=1.5 / 8.0 * 4)
+    log("chunked scan from zero state")
+    check_all("chunked zero state", run_gpu(inp, "bf16", 16, "delta"),
+              run_oracle(inp, "bf16", 16, "delta"), "bf16")
+
+
 @pytest.mark.parametrize("seg_len", [1, 5, 2000, 1 << 24, 2**31 - 1])
 def test_segment_length_extremes(seg_len):
     """N = 1 (every row its own segment), an odd N, and N > L (one short
