@@ -151,7 +151,7 @@ struct DecodeGeometry {
 };
 
 // Key splits (workgroups along the keys) for n_keys visible keys, and the
-// fp32 scratch the split partials need.
+// fp32 scratch the split partials and the retrieval slot need.
 int decode_splits(int n_keys);
 size_t decode_partial_floats(const DecodeGeometry &g);
 

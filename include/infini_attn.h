@@ -150,9 +150,10 @@ int infini_attn_forward(infini_attn_t *h, const void *q, const void *k, const vo
  *   M, z    [B, Hkv, d_k, d_v], [B, Hkv, d_k] fp32 (device), the state before
  *           the current segment; read only
  *   out     [B, Hq, n_new, d_v] dtype (device), written
- * The library keeps a scratch buffer for the key-split partials in the
- * handle, grown on demand: 4 (d_v + 2) B Hq n_new ceil((n_past + n_new) / 64)
- * bytes, small for a few new rows; a long chunk is better served by
+ * The library keeps a scratch buffer for the key-split partials and the
+ * retrieval in the handle, grown on demand:
+ * 4 (d_v + 2) B Hq n_new (ceil((n_past + n_new) / 64) + 1) bytes, small for a
+ * few new rows; a long chunk is better served by
  * infini_attn_forward. The chunk must not cross a segment boundary: at
  * the boundary, fold the finished segment into (M, z) with
  * infini_attn_update and start the cache again at row 0.
@@ -174,10 +175,10 @@ int infini_attn_decode(infini_attn_t *h, const void *q, int32_t n_new, const voi
  * ends), instead of a buffer the handle grows: the call allocates nothing and
  * calls no allocating library routine. Its address on a device is looked up
  * by infini_attn_create, with that device current.
- * The partials need 4 (d_v + 2) B Hq n_new ceil((n_past + n_new) / 64) bytes;
- * a larger request returns ERR_SCRATCH before anything is enqueued (one new
- * row against a full 2048-row segment of the Llama-3-8B attention shape takes
- * 532 KB). Every call on one device shares that device's array and overwrites
+ * The partials (one slot per 64-key split and one for the retrieval) need
+ * 4 (d_v + 2) B Hq n_new (ceil((n_past + n_new) / 64) + 1) bytes; a larger
+ * request returns ERR_SCRATCH before anything is enqueued (one new row against
+ * a full 2048-row segment of the Llama-3-8B attention shape takes 549 KB). Every call on one device shares that device's array and overwrites
  * what the previous call left there (nothing in it needs to start at zero):
  * calls that may overlap on one device, from any handle or stream, race and
  * must be serialised by the caller.

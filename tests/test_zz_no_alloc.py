@@ -82,10 +82,11 @@ def test_noalloc_decode_rejects_requests_beyond_its_scratch():
     import compressive_memory_transformers_segment_amd as ia
     from compressive_memory_transformers_segment_amd import _lib
     # 16 new rows of 32 heads against 2048 cached rows: 4 * 130 * 32 * 16 * 33
-    # bytes = 8.8 MB fits; 40 rows (22 MB) do not.
+    # bytes (32 key splits and the retrieval slot) = 8.8 MB fits; 40 rows
+    # (22 MB) do not.
     B, Hq, Hkv, cap, d = 1, 32, 8, 2048, 128
     for n_new, fits in ((16, True), (40, False)):
-        need = 4 * (d + 2) * B * Hq * n_new * -(-(cap - n_new + n_new) // 64)
+        need = 4 * (d + 2) * B * Hq * n_new * (-(-(cap - n_new + n_new) // 64) + 1)
         assert (need <= _lib.DECODE_SCRATCH_BYTES) == fits
         q, kc, vc, beta, M, z = _inputs(3, "bf16", B, Hq, Hkv, cap, d, cap - n_new, n_new)
         h = ia.handle_for(q, kc, 1e-6, seq_len=cap)
