@@ -62,6 +62,11 @@ _lock = threading.Lock()
 def load(path: Optional[str] = None) -> ctypes.CDLL:
     """Load the HIP library (once). Raises if it has not been built."""
     global _lib
+    # torch ships its own HIP runtime under the soname of ROCm's. Imported
+    # first, it is the one runtime the library binds to; a library loaded
+    # before torch binds to ROCm's copy instead, and then fails to create
+    # handles on the streams torch hands in.
+    import torch  # noqa: F401
     with _lock:
         if _lib is not None and path is None:
             return _lib

@@ -168,6 +168,15 @@ __device__ __forceinline__ bf16x8 gather_rows(const uint16_t (*tile)[PB], int st
   return a;
 }
 
+// Workgroup barrier that orders LDS only: __syncthreads() also waits for the
+// wave's outstanding global loads, which would drain the next tile's
+// prefetch.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -252,18 +261,41 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
     }
   }
 
+  // fp32 storage: the key tile j0 staged synchronously.
   auto load_kv = [&](int j0) {
     __syncthreads();
-    if constexpr (BF) {
-      load_rows_bf16<D, PB>(sKb, reinterpret_cast<const uint16_t *>(kb) + static_cast<size_t>(j0) * D,
-                            kKT, kend - j0);
-      load_rows_bf16<D, PB>(sVb, reinterpret_cast<const uint16_t *>(vb) + static_cast<size_t>(j0) * D,
-                            kKT, kend - j0);
-    } else {
-      load_rows<T, D, P>(sK, kb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
-      load_rows<T, D, P>(sV, vb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
-    }
+    load_rows<T, D, P>(sK, kb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
+    load_rows<T, D, P>(sV, vb + static_cast<size_t>(j0) * D, kKT, kend - j0, false);
     __syncthreads();
+  };
+  // bf16 storage: the next key tile's rows travel in registers (KVN 16-byte
+  // units of K and of V per thread) while the current tile is worked on.
+  constexpr int U16 = D / 8;
+  constexpr int KVN = (kKT * U16 + kThreads - 1) / kThreads;
+  u32x4 pk[BF ? KVN : 1], pv[BF ? KVN : 1];
+  auto fetch = [&](int j0) __attribute__((always_inline)) {
+    const uint16_t *k16 = reinterpret_cast<const uint16_t *>(kb);
+    const uint16_t *v16 = reinterpret_cast<const uint16_t *>(vb);
+#pragma unroll
+    for (int it = 0; it < KVN; ++it) {
+      const int idx = t + kThreads * it, r = idx / U16, c = 8 * (idx % U16);
+      if (idx < kKT * U16) {
+        const size_t o = static_cast<size_t>(min(j0 + r, kend - 1)) * D + c;
+        pk[it] = *reinterpret_cast<const u32x4 *>(k16 + o);
+        pv[it] = *reinterpret_cast<const u32x4 *>(v16 + o);
+      }
+    }
+  };
+  auto stage = [&](int j0) __attribute__((always_inline)) {  // rows past kend: zero
+#pragma unroll
+    for (int it = 0; it < KVN; ++it) {
+      const int idx = t + kThreads * it, r = idx / U16, c = 8 * (idx % U16);
+      if (idx < kKT * U16) {
+        const bool in = j0 + r < kend;
+        *reinterpret_cast<u32x4 *>(&sKb[r][c]) = in ? pk[it] : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(&sVb[r][c]) = in ? pv[it] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
   };
   auto scores = [&](f32x16 &st, f32x16 &ot) {
     st = zero16();
@@ -289,12 +321,31 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   };
   // Key tile j0 is visible to some row of this wave.
   auto wave_sees = [&](int j0) { return wave_live && j0 <= wq0 + 31; };
+  // One pass over the key tiles [a, kend): body(j0) for the tiles this wave
+  // sees. bf16: the tile is staged from registers between two LDS-only
+  // barriers, then the next tile's loads are issued, so they are in flight
+  // during the work and the next stage waits for them.
+  auto pass = [&](auto &&body) __attribute__((always_inline)) {
+    if constexpr (BF) {
+      fetch(a);
+      for (int j0 = a; j0 < kend; j0 += kKT) {
+        lds_barrier();
+        stage(j0);
+        lds_barrier();
+        if (j0 + kKT < kend) fetch(j0 + kKT);
+        if (wave_sees(j0)) body(j0);
+      }
+    } else {
+      for (int j0 = a; j0 < kend; j0 += kKT) {
+        load_kv(j0);
+        if (wave_sees(j0)) body(j0);
+      }
+    }
+  };
 
   // Pass 1: online max, sum and E = sum_j P_ij (dO_i . v_j) of each row.
   float m = -INFINITY, l = 0.f, ea = 0.f;
-  for (int j0 = a; j0 < kend; j0 += kKT) {
-    load_kv(j0);
-    if (!wave_sees(j0)) continue;
+  pass([&](int j0) __attribute__((always_inline)) {
     f32x16 st, ot;
     scores(st, ot);
     float x[16];
@@ -320,7 +371,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
     l = l * f + ps;
     ea = ea * f + pe;
     m = mn;
-  }
+  });
   const float lse = m + __logf(l);
   const float E = ea / l;
 
@@ -328,9 +379,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   f32x16 dqa[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) dqa[cb] = zero16();
-  for (int j0 = a; j0 < kend; j0 += kKT) {
-    load_kv(j0);
-    if (!wave_sees(j0)) continue;
+  pass([&](int j0) __attribute__((always_inline)) {
     f32x16 st, ot;
     scores(st, ot);
     float ds[16];
@@ -358,7 +407,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqa[cb] = mfma32(key_at(kappa(r, g), 32 * cb + l32), ds[r], dqa[cb]);
     }
-  }
+  });
 
   // Retrieval backward from the pre-segment snapshot (Mp^T in mt, zp in zpre).
   if constexpr (BF) {
@@ -521,74 +570,129 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
     gk[cb] = zero16();
     gv[cb] = zero16();
   }
-  for (int hl = 0; hl < grp; ++hl) {
+  // One chunk: query head hl of the group, rows i0 .. i0 + 31 (staged in
+  // sQb / sOb or sQ / sO, with their lse and E in sL / sE).
+  auto chunk = [&](int hl, int i0) __attribute__((always_inline)) {
     const int h = j * grp + hl;
     const float gam = gate(beta[h]);
-    const size_t hrow = (static_cast<size_t>(b) * Hq + h) * L;
-    for (int i0 = j0; i0 < e; i0 += 32) {
-      const int rows = min(32, e - i0);
-      __syncthreads();
-      if constexpr (BF) {
-        load_rows_bf16<D, PB>(sQb, reinterpret_cast<const uint16_t *>(q) + (hrow + i0) * D, 32, rows);
-        load_rows_bf16<D, PB>(sOb, reinterpret_cast<const uint16_t *>(dout) + (hrow + i0) * D, 32,
-                              rows);
-      } else {
-        load_rows<T, D, P>(sQ, q + (hrow + i0) * D, 32, rows, false);
-        load_rows<T, D, P>(sO, dout + (hrow + i0) * D, 32, rows, false);
+    f32x16 st = zero16(), ot = zero16();
+    if constexpr (BF) {
+#pragma unroll
+      for (int u = 0; u < D / 16; ++u) {
+        st = mfma32(ld_bf16x8(&sQb[l32][16 * u + 8 * g]), kb8[u], st);
+        ot = mfma32(ld_bf16x8(&sOb[l32][16 * u + 8 * g]), vb8[u], ot);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < D / 2; ++u) {
+        st = mfma32(sQ[l32][2 * u + g], kr[u], st);
+        ot = mfma32(sO[l32][2 * u + g], vr[u], ot);
+      }
+    }
+    float pw[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = kappa(r, g), row = i0 + qr;
+      const bool vis = key <= row && row < e && kvalid;
+      const float p = vis ? __expf(st[r] * scale - sL[qr]) : 0.f;
+      pw[r] = (1.f - gam) * p;
+      ds[r] = pw[r] * (ot[r] - sE[qr]);
+    }
+    if constexpr (BF) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        bf16x8 phi, plo, dhi, dlo;
+        split_bf16x8(pw + 8 * st, phi, plo);
+        split_bf16x8(ds + 8 * st, dhi, dlo);
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+          const bf16x8 ao = gather_rows<PB>(sOb, st, g, 32 * cb + l32);
+          const bf16x8 aq = gather_rows<PB>(sQb, st, g, 32 * cb + l32);
+          gv[cb] = mfma32(ao, phi, gv[cb]);
+          gv[cb] = mfma32(ao, plo, gv[cb]);
+          gk[cb] = mfma32(aq, dhi, gk[cb]);
+          gk[cb] = mfma32(aq, dlo, gk[cb]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          gv[cb] = mfma32(o_at(kappa(r, g), 32 * cb + l32), pw[r], gv[cb]);
+          gk[cb] = mfma32(q_at(kappa(r, g), 32 * cb + l32), ds[r], gk[cb]);
+        }
+    }
+  };
+  const int nci = (e - j0 + 31) / 32;  // row chunks per query head
+  if constexpr (BF) {
+    // The next chunk's rows travel in registers (KVN 16-byte units of q and
+    // of d_out per thread, lse and E for threads < 32) while the current one
+    // is worked on; it is staged between two LDS-only barriers.
+    constexpr int U16 = D / 8;
+    constexpr int KVN = (32 * U16 + kThreads - 1) / kThreads;
+    u32x4 pq[KVN], po[KVN];
+    float pl = 0.f, pe = 0.f;
+    const uint16_t *q16 = reinterpret_cast<const uint16_t *>(q);
+    const uint16_t *o16 = reinterpret_cast<const uint16_t *>(dout);
+    auto fetch = [&](int c) __attribute__((always_inline)) {
+      const int hl = c / nci, i0 = j0 + 32 * (c % nci);
+      const size_t hrow = (static_cast<size_t>(b) * Hq + j * grp + hl) * L;
+#pragma unroll
+      for (int it = 0; it < KVN; ++it) {
+        const int idx = t + kThreads * it, r = idx / U16, c8 = 8 * (idx % U16);
+        if (idx < 32 * U16) {
+          const size_t o = (hrow + min(i0 + r, e - 1)) * D + c8;
+          pq[it] = *reinterpret_cast<const u32x4 *>(q16 + o);
+          po[it] = *reinterpret_cast<const u32x4 *>(o16 + o);
+        }
       }
       if (t < 32) {
-        sL[t] = t < rows ? lse[hrow + i0 + t] : 0.f;
-        sE[t] = t < rows ? E[hrow + i0 + t] : 0.f;
+        pl = lse[hrow + min(i0 + t, e - 1)];
+        pe = E[hrow + min(i0 + t, e - 1)];
       }
-      __syncthreads();
-      if (!wave_live || wk0 > i0 + 31) continue;  // every key after every row
-      f32x16 st = zero16(), ot = zero16();
-      if constexpr (BF) {
+    };
+    auto stage = [&](int c) __attribute__((always_inline)) {  // rows past e: zero
+      const int rows = min(32, e - (j0 + 32 * (c % nci)));
 #pragma unroll
-        for (int u = 0; u < D / 16; ++u) {
-          st = mfma32(ld_bf16x8(&sQb[l32][16 * u + 8 * g]), kb8[u], st);
-          ot = mfma32(ld_bf16x8(&sOb[l32][16 * u + 8 * g]), vb8[u], ot);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < D / 2; ++u) {
-          st = mfma32(sQ[l32][2 * u + g], kr[u], st);
-          ot = mfma32(sO[l32][2 * u + g], vr[u], ot);
+      for (int it = 0; it < KVN; ++it) {
+        const int idx = t + kThreads * it, r = idx / U16, c8 = 8 * (idx % U16);
+        if (idx < 32 * U16) {
+          const bool in = r < rows;
+          *reinterpret_cast<u32x4 *>(&sQb[r][c8]) = in ? pq[it] : u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4 *>(&sOb[r][c8]) = in ? po[it] : u32x4{0u, 0u, 0u, 0u};
         }
       }
-      float pw[16], ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = kappa(r, g), row = i0 + qr;
-        const bool vis = key <= row && row < e && kvalid;
-        const float p = vis ? __expf(st[r] * scale - sL[qr]) : 0.f;
-        pw[r] = (1.f - gam) * p;
-        ds[r] = pw[r] * (ot[r] - sE[qr]);
+      if (t < 32) {
+        sL[t] = t < rows ? pl : 0.f;
+        sE[t] = t < rows ? pe : 0.f;
       }
-      if constexpr (BF) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          bf16x8 phi, plo, dhi, dlo;
-          split_bf16x8(pw + 8 * st, phi, plo);
-          split_bf16x8(ds + 8 * st, dhi, dlo);
-#pragma unroll
-          for (int cb = 0; cb < NB; ++cb) {
-            const bf16x8 ao = gather_rows<PB>(sOb, st, g, 32 * cb + l32);
-            const bf16x8 aq = gather_rows<PB>(sQb, st, g, 32 * cb + l32);
-            gv[cb] = mfma32(ao, phi, gv[cb]);
-            gv[cb] = mfma32(ao, plo, gv[cb]);
-            gk[cb] = mfma32(aq, dhi, gk[cb]);
-            gk[cb] = mfma32(aq, dlo, gk[cb]);
-          }
+    };
+    const int nch = grp * nci;
+    fetch(0);
+    for (int c = 0; c < nch; ++c) {
+      lds_barrier();
+      stage(c);
+      lds_barrier();
+      if (c + 1 < nch) fetch(c + 1);
+      const int i0 = j0 + 32 * (c % nci);
+      if (wave_live && wk0 <= i0 + 31) chunk(c / nci, i0);  // else: every key after every row
+    }
+  } else {
+    for (int hl = 0; hl < grp; ++hl) {
+      const size_t hrow = (static_cast<size_t>(b) * Hq + j * grp + hl) * L;
+      for (int i0 = j0; i0 < e; i0 += 32) {
+        const int rows = min(32, e - i0);
+        __syncthreads();
+        load_rows<T, D, P>(sQ, q + (hrow + i0) * D, 32, rows, false);
+        load_rows<T, D, P>(sO, dout + (hrow + i0) * D, 32, rows, false);
+        if (t < 32) {
+          sL[t] = t < rows ? lse[hrow + i0 + t] : 0.f;
+          sE[t] = t < rows ? E[hrow + i0 + t] : 0.f;
         }
-      } else {
-#pragma unroll
-        for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            gv[cb] = mfma32(o_at(kappa(r, g), 32 * cb + l32), pw[r], gv[cb]);
-            gk[cb] = mfma32(q_at(kappa(r, g), 32 * cb + l32), ds[r], gk[cb]);
-          }
+        __syncthreads();
+        if (!wave_live || wk0 > i0 + 31) continue;  // every key after every row
+        chunk(hl, i0);
       }
     }
   }
