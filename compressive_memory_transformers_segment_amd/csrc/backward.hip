@@ -932,8 +932,157 @@ __global__ void bwd_zprefix_kernel(const float *__restrict__ dz, const float *__
 // ---------------------------------------------------------------------------
 // update: the memory write's gradient into v and k (without the gz_s term,
 // added once the z chain is done), and qz_s = sk^T ddenk for the delta rule.
+// One workgroup per 32 rows of a segment. The four d x d products per chunk
+// run on the fp32 matrix cores (v_mfma_f32_32x32x2_f32): wave w computes the
+// 32-column block w of each result (d = 128: four blocks, one per wave), with
+// A = 32 rows of a chunk tile in LDS and B staged 32 rows at a time.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_update_kernel(
+    const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ mt,
+    const float *__restrict__ zpre, const float *__restrict__ gma, int L, int N, int S, float eps,
+    int delta, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ qz_part) {
+  constexpr int P = D + 1;
+  constexpr int NBC = D / 32;  // 32-column result blocks
+  constexpr int SU = kKT * D / kThreads;  // B elements staged per thread
+  __shared__ float sK[kKT][P];  // sigma(k)
+  __shared__ float sV[kKT][P];  // v, then W = v - numk / denk
+  __shared__ float sY[kKT][P];  // Y / denk
+  __shared__ float sB[kKT][P];  // 32 rows of gM_s, Mp or their transposes; Y * numk
+  __shared__ float sZ[D];
+  __shared__ float sDen[kKT], sDd[kKT];
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int s = blockIdx.y, kvh = blockIdx.z;
+  const int a = s * N, e = min(a + N, L);
+  const int i0 = a + blockIdx.x * kKT;
+  const size_t unit = static_cast<size_t>(kvh) * S + s;
+  // This chunk's partial of qz_s (delta rule), summed in chunk order later.
+  float *qzp = qz_part + (unit * gridDim.x + blockIdx.x) * D;
+  if (i0 >= e) {
+    if (delta)
+      for (int c = t; c < D; c += kThreads) qzp[c] = 0.f;
+    return;
+  }
+  const int rows = min(kKT, e - i0);
+  const size_t row0 = static_cast<size_t>(kvh) * L + i0;
+  const float *gm = gma + unit * D * D;
+  const float *mtp = mt + unit * D * D;  // M_{s-1}^T: mtp[j * D + c] = Mp[c][j]
+  load_rows<T, D, P>(sK, k + row0 * D, kKT, rows, true);
+  load_rows<T, D, P>(sV, v + row0 * D, kKT, rows, false);
+  for (int c = t; c < D; c += kThreads) sZ[c] = zpre[(static_cast<size_t>(kvh) * (S + 1) + s) * D + c];
+
+  const bool owns = w < NBC;     // this wave holds a result block
+  const int col = 32 * w + l32;  // its column (owners)
+  // Rows [r0, r0 + 32) of the B operand into sB: B(kk, c) = src(r0 + kk, c),
+  // every load issued before the first store.
+  auto stage = [&](auto &&src, int r0) __attribute__((always_inline)) {
+    __syncthreads();  // every wave is done with the previous chunk
+    float x[SU];
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int idx = t + kThreads * i;
+      x[i] = src(r0 + idx % kKT, idx / kKT);
+    }
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int idx = t + kThreads * i;
+      sB[idx % kKT][idx / kKT] = x[i];
+    }
+    __syncthreads();
+  };
+  // acc += sgn A[:, r0 .. r0 + 31] B (the staged chunk), A a 32-row LDS tile.
+  auto mm = [&](f32x16 &acc, const float (*A)[P], int r0, float sgn) __attribute__((always_inline)) {
+    if (!owns) return;
+#pragma unroll 8
+    for (int kk = 0; kk < kKT; kk += 2) acc = mfma32(sgn * A[l32][r0 + kk + g], sB[kk + g][col], acc);
+  };
+  auto gm_rows = [&](int kk, int c) { return gm[static_cast<size_t>(kk) * D + c]; };   // gM_s
+  auto gm_cols = [&](int kk, int c) { return gm[static_cast<size_t>(c) * D + kk]; };   // gM_s^T
+  auto mp_rows = [&](int kk, int c) { return mtp[static_cast<size_t>(c) * D + kk]; }; // Mp
+  auto mp_cols = [&](int kk, int c) { return mtp[static_cast<size_t>(kk) * D + c]; }; // Mp^T
+
+  // Y = sk gM_s; dv += Y.
+  f32x16 Y = zero16();
+  for (int k0 = 0; k0 < D; k0 += kKT) {
+    stage(gm_rows, k0);
+    mm(Y, sK, k0, 1.f);
+  }
+  if (owns) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = kappa(i, g);
+      if (r < rows) dv[(row0 + r) * D + col] += Y[i];
+    }
+  }
+
+  if (delta) {
+    // numk = sk Mp; denk = sk . zp + eps; W = v - numk / denk into sV,
+    // Y / denk into sY, Y * numk into sB, whose row sums give ddenk.
+    f32x16 nk = zero16();
+    for (int k0 = 0; k0 < D; k0 += kKT) {
+      stage(mp_rows, k0);
+      mm(nk, sK, k0, 1.f);
+    }
+    if (t < kKT) {
+      float d = eps;
+      for (int c = 0; c < D; ++c) d += sK[t][c] * sZ[c];
+      sDen[t] = d;
+    }
+    __syncthreads();  // sDen written; every wave is done with sB
+    if (owns) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = kappa(i, g);
+        const float den = sDen[r];
+        sV[r][col] -= nk[i] / den;  // owner-only element
+        sY[r][col] = Y[i] / den;
+        sB[r][col] = Y[i] * nk[i];
+      }
+    }
+    __syncthreads();
+    if (t < kKT) {
+      float part = 0.f;
+      for (int c = 0; c < D; ++c) part += sB[t][c];
+      const float den = sDen[t];
+      sDd[t] = t < rows ? part / (den * den) : 0.f;
+    }
+    __syncthreads();
+    if (t < D) {
+      float acc = 0.f;
+      for (int r = 0; r < kKT; ++r) acc += sK[r][t] * sDd[r];
+      qzp[t] = acc;
+    }
+  }
+
+  // dsk = W gM_s^T (linear: v gM_s^T) - (Y / denk) Mp^T + ddenk zp.
+  f32x16 dsk = zero16();
+  for (int j0 = 0; j0 < D; j0 += kKT) {
+    stage(gm_cols, j0);
+    mm(dsk, sV, j0, 1.f);
+  }
+  if (delta) {
+    for (int j0 = 0; j0 < D; j0 += kKT) {
+      stage(mp_cols, j0);
+      mm(dsk, sY, j0, -1.f);
+    }
+  }
+  if (owns) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = kappa(i, g);
+      if (r < rows) {
+        const float gr = dsk[i] + (delta ? sDd[r] * sZ[col] : 0.f);
+        dk[(row0 + r) * D + col] += gr * elu1_grad_from(sK[r][col]);
+      }
+    }
+  }
+}
+
+// The same update on the vector ALUs (d < 128: the matrix-core version
+// would leave waves idle with fewer than four 32-column blocks).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_update_valu_kernel(
     const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ mt,
     const float *__restrict__ zpre, const float *__restrict__ gma, int L, int N, int S, float eps,
     int delta, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ qz_part) {
@@ -1163,8 +1312,12 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
   bwd_gm_chain_kernel<D, false><<<dim3(D / kKT, kvheads), kThreads, 0, st>>>(w.R, w.G, dM, g.S, delta,
                                                                       w.gma, dM0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_update_kernel<T, D><<<dim3(nb.chunks, g.S, kvheads), kThreads, 0, st>>>(
-      k, v, w.mt, w.z_pre, w.gma, g.L, g.N, g.S, g.eps, delta, dk, dv, w.qz_part);
+  if (D == 128)
+    bwd_update_kernel<T, D><<<dim3(nb.chunks, g.S, kvheads), kThreads, 0, st>>>(
+        k, v, w.mt, w.z_pre, w.gma, g.L, g.N, g.S, g.eps, delta, dk, dv, w.qz_part);
+  else
+    bwd_update_valu_kernel<T, D><<<dim3(nb.chunks, g.S, kvheads), kThreads, 0, st>>>(
+        k, v, w.mt, w.z_pre, w.gma, g.L, g.N, g.S, g.eps, delta, dk, dv, w.qz_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (delta && (e = sum_parts(w.qz_part, units, nb.chunks, D, 0, w.qz, nullptr, st)) != hipSuccess)
     return e;
