@@ -59,9 +59,10 @@
 //     read one kv head's segment share that XCD's L2.
 //   * Epilogue: the pre-segment snapshot M^T (bf16, [d_v][d_k]) arrives as a
 //     ring slot, once for all heads of the workgroup, and is multiplied with
-//     sigma(Q) (computed in place of the Q registers) on MFMA; the
-//     denominator sigma(Q).z is a per-lane dot product plus one exchange (z
-//     and the gate parameters travel in a side area of the snapshot's slot).
+//     sigma(Q) (computed in place of the Q registers) on MFMA; so is the
+//     denominator sigma(Q).z, from the same bf16 sigma(Q) and z split into
+//     bf16 hi and lo parts (z and the gate parameters travel in a side area
+//     of the snapshot's slot).
 //     Rows are stored through a buffer resource that ends at the segment end,
 //     so every wave issues the same stores and the hardware drops those past
 //     it. The two lanes that hold one row exchange halves first, so that each
@@ -86,6 +87,16 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+// sigma(x) = ELU(x) + 1 without a compare and select: the exponential clamped
+// to [0, 1] (the clamp is a free output modifier of v_exp) is exp(x) for
+// x <= 0 and exactly 1 for x > 0, so adding max(x, 0) gives x + 1 there and
+// leaves exp(x) otherwise; the same values as the select form, bit for bit.
+// (A NaN in q may come out of it as a number, but its row's scores, and so
+// the row's output, are NaN regardless.)
+__device__ __forceinline__ float elu1_clamped(float x) {
+  return __builtin_amdgcn_fmed3f(__expf(x), 0.f, 1.f) + fmaxf(x, 0.f);
+}
 
 // Combine a lane's value with that of the lane 32 away. v_permlane32_swap
 // exchanges the two 32-lane halves between its two operands, so with both
@@ -127,7 +138,7 @@ struct Tile {
   static constexpr int KU = kBN * CPR;       // K units per tile
   static constexpr int VU = D * 8;           // V^T units per tile (64 keys per row)
   static constexpr int BUFU = KU + VU;       // 16-byte units per ring slot
-  static constexpr int SIDE = kWaves * 64;   // floats in a slot's side area (z, beta)
+  static constexpr int SIDE = kWaves * 64;   // words in a slot's side area (z, beta)
   static constexpr int BUF = BUFU * 8 + 2 * SIDE;  // bf16 per ring slot
   static constexpr int IPW = BUFU / kThreads;  // 16-byte direct loads per wave per slot
   static constexpr int MU = D * CPR;         // M^T units
@@ -205,7 +216,7 @@ template <int D, int HPW>
 __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ vt, int vt_tiles, const float *__restrict__ beta,
-    const float *__restrict__ z_pre, const uint16_t *__restrict__ mt_pre,
+    const uint16_t *__restrict__ z_hl, const uint16_t *__restrict__ mt_pre,
     uint16_t *__restrict__ out, Layout lq, Layout lkv, Layout lo, int Hq, int Hkv, int L, int N,
     int S, int n_qt, int n_items, float eps, float scale_log2) {
   using TL = Tile<D>;
@@ -246,9 +257,9 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   //   slots 3n-2, 3n-1      Q rows of the next item for waves 0..3, 4..7
   //                         (32 rows per wave, swizzled like K)
   // (the first item's Q slots come before its first tile). Every slot also
-  // carries a side area of one float per lane of every wave: z of the item's
-  // segment (waves 0..6) and beta of its heads (wave 7). Loads run two slots
-  // ahead of the work.
+  // carries a side area of one word per lane of every wave: z before the
+  // item's segment as bf16 hi and lo rows (waves 0..6) and beta of its heads
+  // (wave 7). Loads run two slots ahead of the work.
   FusedItem cur = item(0);
   if (cur.k < 0) return;
 
@@ -322,14 +333,16 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
                           __builtin_amdgcn_readfirstlane((t * D * 64 + 8 * (u0 - TL::KU)) * 2));
     }
   };
-  // M^T of an item's segment, swizzled like K, and the side area (one float
-  // per lane of every wave) with z of the segment (waves 0..6) and beta of the
-  // item's heads (wave 7).
+  // M^T of an item's segment, swizzled like K, and the side area (one word
+  // per lane of every wave) with z before the segment as bf16 hi and lo rows
+  // (waves 0..6) and beta of the item's heads (wave 7).
   auto dma_mem = [&](const FusedItem &it, uint16_t *buf) __attribute__((always_inline)) {
     const uint16_t *mt = mt_pre + (static_cast<size_t>(it.head) * S + it.s) * D * D;
 #pragma unroll
     for (int i = 0; i < TL::IPW; ++i) ld(rowsrc(mt, 32 * blk(i), D - 1, D), buf, i);  // rows past D (D < 128): unread copies
-    const float *zs = z_pre + (static_cast<size_t>(it.head) * (S + 1) + it.s) * D;
+    // z as hi and lo bf16 rows (2 D bf16 = D words), repeated over waves 0..6.
+    const float *zs = reinterpret_cast<const float *>(
+        z_hl + (static_cast<size_t>(it.head) * S + it.s) * 2 * D);
     const float *side = (w == kWaves - 1) ? beta + it.bq % Hq + (lane < HPW ? lane : 0)
                                           : zs + (64 * w + lane) % D;
     __builtin_amdgcn_global_load_lds(side, IA_LDS(buf + TL::BUFU * 8 + 128 * w), 4, 0, 0);
@@ -461,21 +474,25 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   auto epilogue = [&](const uint16_t *buf, int qw) __attribute__((always_inline)) {
     const float *side = reinterpret_cast<const float *>(buf + TL::BUFU * 8);
     // sigma(Q) as the B operand, computed in place of Q (the next item's Q
-    // slots reload every wave's registers before its first key tile), and
-    // this lane's part of sigma(q).z.
-    float den = 0.f;
+    // slots reload every wave's registers before its first key tile).
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float x0 = elu1(lo_bf16(qf[t][jj]));
-        const float x1 = elu1(hi_bf16(qf[t][jj]));
-        den += x0 * side[16 * t + 8 * g + 2 * jj] + x1 * side[16 * t + 8 * g + 2 * jj + 1];
-        qf[t][jj] = pack_bf16x2(x0, x1);
-      }
+      for (int jj = 0; jj < 4; ++jj)
+        qf[t][jj] = pack_bf16x2(elu1_clamped(lo_bf16(qf[t][jj])),
+                                elu1_clamped(hi_bf16(qf[t][jj])));
     }
-    den = sum_xor32(den) + eps;
-    const float inv_den = 1.f / den;
+    // sigma(q).z on the matrix cores, from the same bf16 sigma(q) as the
+    // numerator: row i of the A operand is z's hi part for even i and its lo
+    // part for odd i, so registers 0 and 1 of every lane (result rows 4 g and
+    // 4 g + 1) hold hi.sigma(q) and lo.sigma(q) of the lane's query.
+    const uint16_t *zrow = reinterpret_cast<const uint16_t *>(side) + (l32 & 1) * D + 8 * g;
+    f32x16 zacc = f32x16{};
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      zacc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(zrow + 16 * t)), as_bf16x8(qf[t]),
+                    zacc);
+    const float inv_den = 1.f / (zacc[0] + zacc[1] + eps);
     const float inv_l = 1.f / sum_xor32(lsum);  // both halves' key slots
     const float gam = 1.f / (1.f + __expf(-side[(kWaves - 1) * 64 + w / RW]));
     const float w_mem = gam * inv_den;
@@ -687,7 +704,7 @@ hipError_t launch_t(const Geometry &g, const uint16_t *q, const uint16_t *k, con
   const long long grid = n_items < slots ? n_items : slots;
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   fused_bf16_kernel<D, HPW><<<dim3(static_cast<unsigned>(grid)), kThreads, 0, stream>>>(
-      q, k, ws.vt, ws.vt_tiles, beta, ws.z_pre, ws.mt_pre_bf16, out, g.lq, g.lkv, g.lo, g.Hq,
+      q, k, ws.vt, ws.vt_tiles, beta, ws.z_hl, ws.mt_pre_bf16, out, g.lq, g.lkv, g.lo, g.Hq,
       g.Hkv, g.L, g.N, g.S, n_qt, static_cast<int>(n_items), g.eps, scale_log2);
   return hipGetLastError();
 }

@@ -88,8 +88,9 @@ int effective_seg(int L, int seg_len) { return (L > 0 && seg_len > L) ? L : seg_
 //          64-key tiles per segment, V^T in the fused kernel's LDS layout)
 //   chain  (bf16 storage, chains of 64+ segments) per chunk: [P | h], the
 //          packed affine step and the state before the chunk, all fp32
+//   zhl    [B*Hkv][S][2][D] bf16 (bf16 storage only): z_pre as hi + lo parts
 struct WsLayout {
-  size_t z, mt, dz, gh, vt, chain_x, chain_gh, chain_states, total;
+  size_t z, mt, dz, gh, vt, chain_x, chain_gh, chain_states, zhl, total;
   int chunk_len;
 };
 
@@ -116,7 +117,8 @@ WsLayout ws_layout(const infini_attn_desc *d, int S, int N) {
   w.chain_x = round_up(heads * nc * D * 2 * D * sizeof(float));
   w.chain_gh = round_up(heads * nc * 2 * D * D * sizeof(float));
   w.chain_states = round_up(heads * nc * D * D * sizeof(float));
-  w.total = w.z + w.mt + w.dz + w.gh + w.vt + w.chain_x + w.chain_gh + w.chain_states;
+  w.zhl = bf16 ? round_up(heads * S * 2 * D * sizeof(uint16_t)) : 0;
+  w.total = w.z + w.mt + w.dz + w.gh + w.vt + w.chain_x + w.chain_gh + w.chain_states + w.zhl;
   return w;
 }
 
@@ -181,6 +183,9 @@ int bind_workspace(infini_attn_handle *h, const ia::Geometry &g, ia::Workspace *
   ws->chain_gh = lay.chunk_len > 0 ? reinterpret_cast<float *>(chain + lay.chain_x) : nullptr;
   ws->chain_states =
       lay.chunk_len > 0 ? reinterpret_cast<float *>(chain + lay.chain_x + lay.chain_gh) : nullptr;
+  ws->z_hl = bf16 ? reinterpret_cast<uint16_t *>(chain + lay.chain_x + lay.chain_gh +
+                                                 lay.chain_states)
+                  : nullptr;
   return INFINI_ATTN_OK;
 }
 

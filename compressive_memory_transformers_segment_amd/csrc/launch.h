@@ -41,6 +41,8 @@ struct Geometry {
 // kernel. Index (b * Hkv + j) * S + s holds the state *before* segment s.
 struct Workspace {
   float *z_pre;           // [B*Hkv][S+1][D] fp32; slot S receives the final z
+  uint16_t *z_hl;         // [B*Hkv][S][2][D] bf16 (bf16 path): z before segment s as its
+                          // bf16 rounding (row 0) and the bf16 rounding of the rest (row 1)
   float *mt_pre_f32;      // [B*Hkv][S][D(v)][D(k)] fp32, M^T (fp32 storage path)
   uint16_t *mt_pre_bf16;  // [B*Hkv][S][D(v)][D(k)] bf16 bits, M^T (bf16 storage path)
   float *dz;              // [B*Hkv][S][z_parts][D] partial sums of sigma(k) (bf16 path)

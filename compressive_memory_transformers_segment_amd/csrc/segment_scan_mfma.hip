@@ -128,6 +128,9 @@ __global__ __launch_bounds__(256) void zsum_kernel(const uint16_t *__restrict__ 
 
 // ---------------------------------------------------------------------------
 // zprefix: z_pre[head][s] = z_{s-1} (the state before segment s), slot S = z_S.
+// With z_hl, also z_{s-1} as two bf16 rows: hi = bf16(z), lo = bf16(z - hi)
+// (about 16 significant bits together), the operand from which the fused
+// kernel forms sigma(q).z on the matrix cores.
 // One workgroup per (32-column block, head); thread (grp, c) owns column c of
 // a contiguous range of segments. Pass 1 sums the range, the workgroup
 // prefix-sums the ranges in LDS, pass 2 writes the running value. dz is read
@@ -140,7 +143,8 @@ constexpr int kZCols = 32;  // columns per workgroup
 
 __global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restrict__ z0,
                                                             const float *__restrict__ dz,
-                                                            float *__restrict__ z_pre, int S,
+                                                            float *__restrict__ z_pre,
+                                                            uint16_t *__restrict__ z_hl, int S,
                                                             int D, int parts) {
   __shared__ float tot[kZThreads];
   const int head = blockIdx.y, G = kZThreads / kZCols;
@@ -172,7 +176,17 @@ __global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restr
 #pragma unroll
     for (int i = 0; i < kZB; ++i) {
       if (f + i < f1) {
-        if ((f + i) % parts == 0) out[static_cast<size_t>((f + i) / parts) * D] = z;
+        if ((f + i) % parts == 0) {
+          const int s = (f + i) / parts;
+          out[static_cast<size_t>(s) * D] = z;
+          if (z_hl) {
+            const __bf16 hi = static_cast<__bf16>(z);
+            const __bf16 lo = static_cast<__bf16>(z - static_cast<float>(hi));
+            uint16_t *zh = z_hl + (static_cast<size_t>(head) * S + s) * 2 * D + c;
+            zh[0] = __builtin_bit_cast(uint16_t, hi);
+            zh[D] = __builtin_bit_cast(uint16_t, lo);
+          }
+        }
         z += x[i];
       }
     }
@@ -790,8 +804,8 @@ hipError_t launch_d(const Geometry &g, const uint16_t *k, const uint16_t *v, flo
   // the CU's wave slots; without it the accumulators leave room for one.
   zsum_kernel<D><<<dim3(g.S * parts, heads), 256, 0, stream>>>(k, g.lkv, g.Hkv, ws.dz, g.L, g.N,
                                                                 g.S, parts);
-  zprefix_kernel<<<dim3(D / kZCols, heads), kZThreads, 0, stream>>>(z, ws.dz, ws.z_pre, g.S, D,
-                                                                     parts);
+  zprefix_kernel<<<dim3(D / kZCols, heads), kZThreads, 0, stream>>>(z, ws.dz, ws.z_pre, ws.z_hl,
+                                                                     g.S, D, parts);
   if (delta) {
     if (split)
       gh_kernel<D, true, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh,

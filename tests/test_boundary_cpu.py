@@ -93,17 +93,20 @@ def test_workspace_size():
     S = math.ceil(700 / 300)
     up = lambda x: (x + 255) // 256 * 256
     heads = 2 * 2
-    # z snapshots, M^T snapshots (bf16), sigma(k) sums, G/H, V^T in 64-key tiles
+    # z snapshots, M^T snapshots (bf16), sigma(k) sums, G/H, V^T in 64-key tiles,
+    # z snapshots as bf16 hi/lo rows
     assert ia.infini_attn_workspace_size(d, 300) == (
         up(heads * (S + 1) * 64 * 4) + up(heads * S * 64 * 64 * 2) + up(heads * S * 1 * 64 * 4)
-        + up(heads * S * 2 * 64 * 64 * 4) + up(heads * S * math.ceil(300 / 64) * 64 * 64 * 2))
+        + up(heads * S * 2 * 64 * 64 * 4) + up(heads * S * math.ceil(300 / 64) * 64 * 64 * 2)
+        + up(heads * S * 2 * 64 * 2))
     d32 = desc(dtype=ia.F32, d_k=32, d_v=32, seq_len=256, n_q_heads=2, n_kv_heads=2)
     assert ia.infini_attn_workspace_size(d32, 64) == up(2 * 5 * 32 * 4) + up(2 * 4 * 32 * 32 * 4)
     # 2048-row segments: sigma(k) sums in 4 row ranges of 512
     d4 = desc(batch=1, n_q_heads=32, n_kv_heads=8, seq_len=32768, d_k=128, d_v=128)
     assert ia.infini_attn_workspace_size(d4, 2048) == (
         up(8 * 17 * 128 * 4) + up(8 * 16 * 128 * 128 * 2) + up(8 * 16 * 4 * 128 * 4)
-        + up(8 * 16 * 2 * 128 * 128 * 4) + up(8 * 16 * 32 * 128 * 64 * 2))
+        + up(8 * 16 * 2 * 128 * 128 * 4) + up(8 * 16 * 32 * 128 * 64 * 2)
+        + up(8 * 16 * 2 * 128 * 2))
     with pytest.raises(ia.InfiniAttnError):
         ia.infini_attn_workspace_size(desc(), 0)
 
