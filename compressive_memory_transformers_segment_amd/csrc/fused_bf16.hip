@@ -170,43 +170,81 @@ struct FusedItem {
   int s;     // segment index
 };
 
+// Unsigned division by a divisor fixed for the launch (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, the quotient of
+// any 32-bit x is (t + ((x - t) >> s1)) >> s2, t = the high word of m x,
+// s1 = min(l, 1), s2 = max(l - 1, 0). A multiply-high, a subtraction, two
+// shifts and an add, all scalar for uniform x, where a division would expand
+// into a vector sequence.
+struct FastDiv {
+  uint32_t d, m, s1, s2;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while (l < 32 && (uint64_t{1} << l) < d) ++l;
+  FastDiv f;
+  f.d = d;
+  f.m = static_cast<uint32_t>(((uint64_t{(uint64_t{1} << l) - d}) << 32) / d + 1);
+  f.s1 = l > 0 ? 1 : 0;
+  f.s2 = l > 0 ? l - 1 : 0;
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv &f) {
+  const uint32_t t = static_cast<uint32_t>((static_cast<uint64_t>(x) * f.m) >> 32);
+  return (t + ((x - t) >> f.s1)) >> f.s2;
+}
+
+// Divisors of the item index: query tiles per segment, segments, head units
+// per kv head, kv heads.
+struct ItemDivs {
+  FastDiv qt, seg, unit, hkv;
+};
+
 // Round k gives the workgroup in slot r item k G + r on even rounds and
 // k G + G - 1 - r on odd ones. Items are ordered with the query tile fastest
 // and longest first, so a workgroup alternates long and short query tiles;
-// items without rows (short last segment) are skipped.
+// items without rows (short last segment) are skipped. Every input is
+// uniform (readfirstlane states it for k), so the search runs on the scalar
+// unit.
 template <int HPW>
-__device__ __forceinline__ FusedItem fused_item(int k, int G, int r, int n_items, int n_qt, int S,
-                                                int N, int L, int Hq, int Hkv) {
+__device__ __forceinline__ FusedItem fused_item(int k, int G, int r, int n_items,
+                                                const ItemDivs &dv, int N, int L, int Hq,
+                                                int Hkv) {
   constexpr int BM = 32 * kWaves / HPW;
   const int grp = Hq / Hkv;
-  const int units = grp / HPW;
   FusedItem it;
-  for (;; ++k) {
-    const long long jl = static_cast<long long>(k) * G + ((k & 1) ? G - 1 - r : r);
-    if (jl >= n_items) {
+  for (uint32_t kk = __builtin_amdgcn_readfirstlane(k);; ++kk) {
+    // Below 2^32: n_items < 2^31 and kk G is at most n_items + 2 G.
+    const uint32_t j = kk * static_cast<uint32_t>(G) + static_cast<uint32_t>((kk & 1) ? G - 1 - r : r);
+    if (j >= static_cast<uint32_t>(n_items)) {
       it.k = -1;
       it.a = it.e = it.q0 = it.T = it.bq = it.head = it.s = 0;
       return it;
     }
-    const int j = static_cast<int>(jl);
-    const int qt = n_qt - 1 - j % n_qt;
-    const int s = (j / n_qt) % S;
-    const int unit = j / (n_qt * S);
+    const uint32_t j1 = fdiv(j, dv.qt);        // (unit, segment) index
+    const uint32_t unit = fdiv(j1, dv.seg);     // head unit
+    const uint32_t u1 = fdiv(unit, dv.unit);    // b * Hkv + kv head
+    const int qt = static_cast<int>(dv.qt.d - 1 - (j - j1 * dv.qt.d));
+    const int s = static_cast<int>(j1 - unit * dv.seg.d);
     const int a = s * N;
     const int e = min(a + N, L);
     const int q0 = a + qt * BM;
     if (q0 >= e) continue;
-    const int b = unit / (Hkv * units);
-    const int hk = (unit / units) % Hkv;
+    const uint32_t b = fdiv(u1, dv.hkv);
+    const int hk = static_cast<int>(u1 - b * dv.hkv.d);
+    const int hu = static_cast<int>(unit - u1 * dv.unit.d);  // head unit within the kv head
     // The fields are uniform by construction; readfirstlane states it, so
     // that they live in scalar registers.
-    it.k = __builtin_amdgcn_readfirstlane(k);
+    it.k = __builtin_amdgcn_readfirstlane(static_cast<int>(kk));
     it.a = __builtin_amdgcn_readfirstlane(a);
     it.e = __builtin_amdgcn_readfirstlane(e);
     it.q0 = __builtin_amdgcn_readfirstlane(q0);
     it.T = __builtin_amdgcn_readfirstlane((min(q0 + BM, e) - a + kBN - 1) / kBN);
-    it.bq = __builtin_amdgcn_readfirstlane(b * Hq + hk * grp + (unit % units) * HPW);
-    it.head = __builtin_amdgcn_readfirstlane(b * Hkv + hk);
+    it.bq = __builtin_amdgcn_readfirstlane(static_cast<int>(b) * Hq + hk * grp + hu * HPW);
+    it.head = __builtin_amdgcn_readfirstlane(static_cast<int>(b) * Hkv + hk);
     it.s = __builtin_amdgcn_readfirstlane(s);
     return it;
   }
@@ -218,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
     const uint16_t *__restrict__ vt, int vt_tiles, const float *__restrict__ beta,
     const uint16_t *__restrict__ z_hl, const uint16_t *__restrict__ mt_pre,
     uint16_t *__restrict__ out, Layout lq, Layout lkv, Layout lo, int Hq, int Hkv, int L, int N,
-    int S, int n_qt, int n_items, float eps, float scale_log2) {
+    int S, ItemDivs dv, int n_items, int G, float eps, float scale_log2) {
   using TL = Tile<D>;
   constexpr int NT = D / 16;          // k-steps over d
   constexpr int ND = D / 32;          // 32-row d tiles of O^T
@@ -241,11 +279,10 @@ __global__ __launch_bounds__(kThreads, 2) void fused_bf16_kernel(
   // contiguous, so in every round an XCD works on consecutive items (the
   // query tiles of one head unit and segment, which read the same K / V
   // tiles and share that XCD's L2).
-  const int G = gridDim.x;
   const int r = (G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds
                                  : static_cast<int>(blockIdx.x);
   auto item = [&](int kk) __attribute__((always_inline)) {
-    return fused_item<HPW>(kk, G, r, n_items, n_qt, S, N, L, Hq, Hkv);
+    return fused_item<HPW>(kk, G, r, n_items, dv, N, L, Hq, Hkv);
   };
 
   // The workgroup's items form one stream of ring slots. Item i with T key
@@ -703,9 +740,14 @@ hipError_t launch_t(const Geometry &g, const uint16_t *q, const uint16_t *k, con
   const long long slots = static_cast<long long>(fused_per_cu<D, HPW>(dev)) * device_cus(dev);
   const long long grid = n_items < slots ? n_items : slots;
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  const ItemDivs dv{make_fastdiv(static_cast<uint32_t>(n_qt)),
+                    make_fastdiv(static_cast<uint32_t>(g.S)),
+                    make_fastdiv(static_cast<uint32_t>(g.Hq / g.Hkv / HPW)),
+                    make_fastdiv(static_cast<uint32_t>(g.Hkv))};
   fused_bf16_kernel<D, HPW><<<dim3(static_cast<unsigned>(grid)), kThreads, 0, stream>>>(
       q, k, ws.vt, ws.vt_tiles, beta, ws.z_hl, ws.mt_pre_bf16, out, g.lq, g.lkv, g.lo, g.Hq,
-      g.Hkv, g.L, g.N, g.S, n_qt, static_cast<int>(n_items), g.eps, scale_log2);
+      g.Hkv, g.L, g.N, g.S, dv, static_cast<int>(n_items), static_cast<int>(grid), g.eps,
+      scale_log2);
   return hipGetLastError();
 }
 
