@@ -409,10 +409,11 @@ def block_forward(x, wq, wk, wv, wo, beta, M, z, seg_len: int, update_mode="line
                   n_q_heads: int = 1, n_kv_heads: int = 1, out=None, eps: float = 1e-6,
                   wqkv=None):
     """The Infini-attention block on x [B, L, d_model]: Q/K/V projections
-    (wq [d_model, Hq d], wk / wv [d_model, Hkv d], or instead wqkv [d_model,
-    (Hq + 2 Hkv) d] with wq = wk = wv = None: the three side by side), the
-    forward pass, and the output projection wo [Hq d, d_model]. (M, z) are
-    updated in place. Returns y [B, L, d_model]."""
+    (wq [Hq d, d_model], wk / wv [Hkv d, d_model], or instead wqkv
+    [(Hq + 2 Hkv) d, d_model] with wq = wk = wv = None: the three stacked),
+    the forward pass, and the output projection wo [d_model, Hq d]; weights are
+    [out, in], as a linear layer keeps them (y = x W^T). (M, z) are updated in
+    place. Returns y [B, L, d_model]."""
     import torch
 
     fused = wqkv is not None
@@ -423,14 +424,14 @@ def block_forward(x, wq, wk, wv, wo, beta, M, z, seg_len: int, update_mode="line
             raise TypeError(f"{name} must have the dtype of x")
     B, L, dm = x.shape
     Hq, Hkv = int(n_q_heads), int(n_kv_heads)
-    width = wo.shape[0]
+    width = wo.shape[1]
     if Hq < 1 or Hkv < 1 or Hq % Hkv or width % Hq:
         raise ValueError("inconsistent head counts")
     D = width // Hq
-    wshapes = ((tuple(wqkv.shape) == (dm, (Hq + 2 * Hkv) * D)) if fused else
-               (tuple(wq.shape) == (dm, Hq * D) and tuple(wk.shape) == (dm, Hkv * D)
-                and tuple(wv.shape) == (dm, Hkv * D)))
-    if (not wshapes or tuple(wo.shape) != (Hq * D, dm)
+    wshapes = ((tuple(wqkv.shape) == ((Hq + 2 * Hkv) * D, dm)) if fused else
+               (tuple(wq.shape) == (Hq * D, dm) and tuple(wk.shape) == (Hkv * D, dm)
+                and tuple(wv.shape) == (Hkv * D, dm)))
+    if (not wshapes or tuple(wo.shape) != (dm, Hq * D)
             or tuple(beta.shape) != (Hq,) or tuple(M.shape) != (B, Hkv, D, D)
             or tuple(z.shape) != (B, Hkv, D)):
         raise ValueError("inconsistent shapes")

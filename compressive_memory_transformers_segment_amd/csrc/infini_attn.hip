@@ -340,10 +340,11 @@ int decode_call(infini_attn_handle *h, const void *q, int32_t n_new, const void 
   return hip_status(e);
 }
 
-// The Infini-attention block. The projections land row-major in one buffer,
-// QKV [B, L, W] with W = (Hq + 2 Hkv) d (the query heads' columns, then the
-// key heads', then the value heads'): one GEMM against a fused [Wq|Wk|Wv]
-// weight, or one GEMM per weight writing its column block. The attention
+// The Infini-attention block. Weights are [out][in] row-major. The
+// projections land row-major in one buffer, QKV [B, L, W] with W = (Hq +
+// 2 Hkv) d (the query heads' columns, then the key heads', then the value
+// heads'): one GEMM against a fused weight (Wq's rows, then Wk's, then Wv's),
+// or one GEMM per weight writing its column block. The attention
 // kernels read their heads' rows of it in place (row stride W) and write O
 // row-major [B, L, Hq d], the output projection's input; nothing is
 // regrouped.
@@ -377,8 +378,8 @@ int block_call(infini_attn_handle *h, int32_t d_model, const void *x, const void
   char *o = qkv + o_off;
   const int n = static_cast<int>(rows);
   if (wqkv) {
-    st = ia::blas_gemm_rowmajor(h->blas, d.dtype, n, static_cast<int>(W), d_model, x, d_model,
-                                wqkv, static_cast<int>(W), qkv, static_cast<int>(W));
+    st = ia::blas_gemm_xwt(h->blas, d.dtype, n, static_cast<int>(W), d_model, x, d_model, wqkv,
+                           d_model, qkv, static_cast<int>(W));
     if (st != INFINI_ATTN_OK) return st;
   } else {
     const struct {
@@ -386,9 +387,8 @@ int block_call(infini_attn_handle *h, int32_t d_model, const void *x, const void
       int64_t col, width;
     } proj[3] = {{wq, 0, Hq * D}, {wk, Hq * D, Hkv * D}, {wv, (Hq + Hkv) * D, Hkv * D}};
     for (const auto &pj : proj) {
-      st = ia::blas_gemm_rowmajor(h->blas, d.dtype, n, static_cast<int>(pj.width), d_model, x,
-                                  d_model, pj.w, static_cast<int>(pj.width),
-                                  qkv + pj.col * elt, static_cast<int>(W));
+      st = ia::blas_gemm_xwt(h->blas, d.dtype, n, static_cast<int>(pj.width), d_model, x,
+                             d_model, pj.w, d_model, qkv + pj.col * elt, static_cast<int>(W));
       if (st != INFINI_ATTN_OK) return st;
     }
   }
@@ -397,8 +397,8 @@ int block_call(infini_attn_handle *h, int32_t d_model, const void *x, const void
   st = forward_impl(h, qkv, qkv + Hq * D * elt, qkv + (Hq + Hkv) * D * elt, beta, M, z, seg_len,
                     update_mode, o, lrow, lrow, lout);
   if (st != INFINI_ATTN_OK) return st;
-  return ia::blas_gemm_rowmajor(h->blas, d.dtype, n, d_model, static_cast<int>(Hq * D), o,
-                                static_cast<int>(Hq * D), wo, d_model, y, d_model);
+  return ia::blas_gemm_xwt(h->blas, d.dtype, n, d_model, static_cast<int>(Hq * D), o,
+                           static_cast<int>(Hq * D), wo, static_cast<int>(Hq * D), y, d_model);
 }
 
 }  // namespace

@@ -177,10 +177,10 @@ hipError_t launch_decode_f32(const DecodeGeometry &g, const float *q, const floa
 
 // Infini-attention block: the dense projections through rocBLAS (statuses
 // are INFINI_ATTN_* codes). Row-major C (rows x n, leading dimension ldc) =
-// X (rows x k, ldx) W (k x n, ldw).
+// X (rows x k, ldx) W^T, W row-major n x k (ldw).
 int blas_create(void **blas, hipStream_t stream);
 void blas_destroy(void *blas);
-int blas_gemm_rowmajor(void *blas, int dtype, int rows, int n, int k, const void *x, int ldx,
-                       const void *w, int ldw, void *c, int ldc);
+int blas_gemm_xwt(void *blas, int dtype, int rows, int n, int k, const void *x, int ldx,
+                  const void *w, int ldw, void *c, int ldc);
 
 }  // namespace ia

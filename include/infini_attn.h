@@ -211,15 +211,17 @@ int infini_attn_update(infini_attn_t *h, const void *k, const void *v, float *M,
  * メカニズム": the mechanism takes the layer's own query, key and value
  * states; [LNCB-review] "基本アイデア": it stands in for the attention of each
  * layer's block):
- *   Q = x Wq, K = x Wk, V = x Wv (head h takes columns h d .. h d + d - 1),
- *   O = infini_attn_forward(Q, K, V, beta, M, z, seg_len, update_mode),
- *   y = O' Wo, with O' the heads of each row side by side [B, L, Hq d].
+ *   Q = x Wq^T, K = x Wk^T, V = x Wv^T (head h takes columns h d .. h d + d - 1
+ *   of the product), O = infini_attn_forward(Q, K, V, beta, M, z, seg_len,
+ *   update_mode), y = O' Wo^T, with O' the heads of each row side by side
+ *   [B, L, Hq d]. Weights are [out, in] row-major, the layout a linear layer
+ *   usually keeps (and the one the library GEMM runs fastest on):
  *   d_model  >= 1 width of the layer input and output
  *   x   [B, L, d_model]        dtype, contiguous (device)
- *   wq  [d_model, Hq * d_k]    dtype, row-major (device)
- *   wk  [d_model, Hkv * d_k]   dtype, row-major (device)
- *   wv  [d_model, Hkv * d_v]   dtype, row-major (device)
- *   wo  [Hq * d_v, d_model]    dtype, row-major (device)
+ *   wq  [Hq * d_k, d_model]    dtype, row-major (device)
+ *   wk  [Hkv * d_k, d_model]   dtype, row-major (device)
+ *   wv  [Hkv * d_v, d_model]   dtype, row-major (device)
+ *   wo  [d_model, Hq * d_v]    dtype, row-major (device)
  *   beta, M, z, seg_len, update_mode as for infini_attn_forward (M, z in/out)
  *   y   [B, L, d_model]        dtype (device), written
  * The projections run on rocBLAS with fp32 accumulation, and Q, K, V, O are
@@ -238,8 +240,8 @@ int infini_attn_block_forward(infini_attn_t *h, int32_t d_model, const void *x, 
 /*
  * The same block with the three projection weights fused into one matrix, as
  * models that store a single query-key-value projection keep them:
- *   wqkv [d_model, (Hq + 2 Hkv) d_k] dtype, row-major (device): columns
- *        0 .. Hq d - 1 are Wq, then Hkv d columns of Wk, then Hkv d of Wv
+ *   wqkv [(Hq + 2 Hkv) d_k, d_model] dtype, row-major (device): rows
+ *        0 .. Hq d - 1 are Wq, then Hkv d rows of Wk, then Hkv d of Wv
  * so that Q, K and V come from one GEMM. Every other argument, the result and
  * the errors are those of infini_attn_block_forward.
  */

@@ -46,11 +46,14 @@ def block_case(seed, dtype, B, L, dm, Hq, Hkv, d, N, mode, fused=False):
     beta = rng.standard_normal(Hq).astype(np.float32)
     M0 = (0.05 * rng.standard_normal((B, Hkv, d, d))).astype(np.float32)
     z0 = rng.uniform(1.0, 20.0, (B, Hkv, d)).astype(np.float32)
-    dev = {n: to_device(a, dtype) for n, a in st.items()}
+    # The library takes weights [out, in]; the oracle takes them [in, out].
+    dev = {n: to_device(a if n == "x" else np.ascontiguousarray(a.T), dtype)
+           for n, a in st.items()}
     M = torch.from_numpy(M0).cuda()
     z = torch.from_numpy(z0).cuda()
     if fused:
-        wqkv = to_device(np.concatenate([st["wq"], st["wk"], st["wv"]], axis=1), dtype)
+        wqkv = to_device(np.ascontiguousarray(
+            np.concatenate([st["wq"], st["wk"], st["wv"]], axis=1).T), dtype)
         y = ia.block_forward(dev["x"], None, None, None, dev["wo"],
                              torch.from_numpy(beta).cuda(), M, z, N, mode, n_q_heads=Hq,
                              n_kv_heads=Hkv, wqkv=wqkv)
