@@ -341,6 +341,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 // workgroup computes the retrieval of its four queries itself (blocks of more
 // than four queries per kv head, whose split launch already fills the chip);
 // otherwise it reads the retrieval slot the split launch wrote.
+constexpr int kCB = 32;  // key splits merged per batch in the combine kernel
+
 template <typename T, int D, bool RET>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const T *__restrict__ q, const float *__restrict__ M, const float *__restrict__ z,
@@ -379,24 +381,40 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   const int h = kvh * g + hh;
   const size_t qrow = (static_cast<size_t>(b * Hq + h) * C + i) * D;
 
-  // A_dot: merge the splits (every query sees key 0, so the merged max is
-  // finite). Lane s0 + lane reads split s0 + lane's max.
-  float mt = -INFINITY;
-  for (int s0 = 0; s0 < n_splits; s0 += 64) {
-    const int sl = s0 + lane;
-    mt = fmaxf(mt, sl < n_splits ? pp[sl * sstride + D] : -INFINITY);
-  }
-  mt = wave_max(mt);
-  float lt = 0.f, a[NE];
+  // A_dot: merge the splits, kCB at a time. Every load of a batch is issued
+  // before the first use (one memory round trip per batch): lane j < kCB
+  // reads split s0 + j's max and sum, and every lane reads its columns of
+  // every split of the batch. Batches merge with the usual rescaling; every
+  // query sees key 0, so the final max is finite.
+  float mt = -INFINITY, lt = 0.f, a[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) a[e] = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < n_splits; ++s) {
-    const float *ps = pp + s * sstride;
-    const float wgt = __expf(ps[D] - mt);  // 0 for a split that saw no key
-    lt += wgt * ps[D + 1];
+  for (int s0 = 0; s0 < n_splits; s0 += kCB) {
+    const int nb = min(kCB, n_splits - s0);
+    const float *pb = pp + static_cast<size_t>(s0) * sstride;
+    const int sj = min(lane, nb - 1);
+    const float ms = pb[sj * sstride + D], ls = pb[sj * sstride + D + 1];
+    float vb[kCB][NE];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) a[e] += wgt * ps[dec_col<D>(lane, e)];
+    for (int j = 0; j < kCB; ++j)
+#pragma unroll
+      for (int e = 0; e < NE; ++e) vb[j][e] = pb[min(j, nb - 1) * sstride + dec_col<D>(lane, e)];
+    const float mb = wave_max(lane < nb ? ms : -INFINITY);
+    const float mn = fmaxf(mt, mb);
+    // weight of split s0 + lane (0 for lanes past the batch and for splits
+    // that saw no key); the running sums rescale to the new max
+    const float wl = (lane < nb && ms != -INFINITY) ? __expf(ms - mn) : 0.f;
+    const float sc = mt == -INFINITY ? 0.f : __expf(mt - mn);
+    lt = lt * sc + wave_sum(wl * ls);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) a[e] *= sc;
+#pragma unroll
+    for (int j = 0; j < kCB; ++j) {
+      const float wj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), j));
+#pragma unroll
+      for (int e = 0; e < NE; ++e) a[e] += wj * vb[j][e];
+    }
+    mt = mn;
   }
 
   // A_mem = sigma(q) M / (sigma(q) z + eps), gate, store.
