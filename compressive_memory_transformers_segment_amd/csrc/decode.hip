@@ -276,18 +276,27 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   __syncthreads();
 
   // Scores: lane j takes key k0 + j against the wave's queries w, w + 4, ...
-  float s[QPW];
+  // Four independent partial sums per query (one per column of a 4-column
+  // group), so that the dependent chain is D / 4 long instead of D: with a
+  // single wave per SIMD nothing else hides its latency.
+  float s4[QPW][4];
 #pragma unroll
-  for (int r = 0; r < QPW; ++r) s[r] = 0.f;
+  for (int r = 0; r < QPW; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s4[r][i] = 0.f;
 #pragma unroll 8
   for (int c = 0; c < D; c += 4) {
     const f32x4 kk = *reinterpret_cast<const f32x4 *>(&sK[lane][c]);
 #pragma unroll
     for (int r = 0; r < QPW; ++r) {
       const f32x4 qq = *reinterpret_cast<const f32x4 *>(&sQ[w + 4 * r][c]);
-      s[r] += kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s4[r][i] = __builtin_fmaf(kk[i], qq[i], s4[r][i]);
     }
   }
+  float s[QPW];
+#pragma unroll
+  for (int r = 0; r < QPW; ++r) s[r] = (s4[r][0] + s4[r][1]) + (s4[r][2] + s4[r][3]);
   const int key = k0 + lane;
   float m[QPW], l[QPW];
 #pragma unroll
@@ -300,24 +309,41 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     l[r] = wave_sum(p);
     sP[w][lane][r] = p;
   }
-  __syncthreads();
+  // (sP[w] is written and read by wave w only: the wave's own LDS ordering
+  // suffices, no workgroup barrier.)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  // P V with keys j and j + kDecKeys / 2 in separate partial sums (two
+  // dependent chains of half the length per value).
+  float acc2[2][QPW][NE];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int r = 0; r < QPW; ++r)
+#pragma unroll
+      for (int e = 0; e < NE; ++e) acc2[h][r][e] = 0.f;
+#pragma unroll 8
+  for (int j = 0; j < kDecKeys / 2; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int jj = j + h * (kDecKeys / 2);
+      float pj[QPW];
+#pragma unroll
+      for (int r = 0; r < QPW; ++r) pj[r] = sP[w][jj][r];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const float vv = sV[jj][dec_col<D>(lane, e)];
+#pragma unroll
+        for (int r = 0; r < QPW; ++r) acc2[h][r][e] = __builtin_fmaf(pj[r], vv, acc2[h][r][e]);
+      }
+    }
+  }
   float acc[QPW][NE];
 #pragma unroll
   for (int r = 0; r < QPW; ++r)
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[r][e] = 0.f;
-#pragma unroll 8
-  for (int j = 0; j < kDecKeys; ++j) {
-    float pj[QPW];
-#pragma unroll
-    for (int r = 0; r < QPW; ++r) pj[r] = sP[w][j][r];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const float vv = sV[j][dec_col<D>(lane, e)];
-#pragma unroll
-      for (int r = 0; r < QPW; ++r) acc[r][e] += pj[r] * vv;
-    }
-  }
+    for (int e = 0; e < NE; ++e) acc[r][e] = acc2[0][r][e] + acc2[1][r][e];
 
 #pragma unroll
   for (int r = 0; r < QPW; ++r) {
