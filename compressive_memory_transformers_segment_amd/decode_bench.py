@@ -12,11 +12,14 @@ the last row of a segment (the most keys) and the middle, with C = 1 and a
 device; (M, z) random with z > 0.
 
 Each case prints one JSON line: microseconds per call (HIP events on the
-launch stream around K calls), decoded tokens/s (B * C per call), and the
-algorithmic HBM bytes per call (the visible cache rows of K and V, q, out, M,
-z) divided by the call time, against the 8 TB/s HBM peak: decode reads every
-visible cache row once, so it is bound by memory (and, at these sizes, by
-launch latency).
+launch stream around K back-to-back calls) through the C entry point with its
+arguments marshalled once (`us_per_call`: the library's own cost per token)
+and through the Python binding, which checks the tensors on every call
+(`us_per_call_binding`: the host then sets the pace), decoded tokens/s
+(B * C per call), and the algorithmic HBM bytes per call (the visible cache
+rows of K and V, q, out, M, z) divided by the C-entry-point call time,
+against the 8 TB/s HBM peak: decode reads every visible cache row once, so it
+is bound by memory (and, at these sizes, by launch latency).
 """
 
 from __future__ import annotations
@@ -56,16 +59,33 @@ def case(shape, n_past, C, steps, warmup=20, seed=0):
     z = 1.0 + 49.0 * torch.rand((B, Hkv, D), generator=g, device=dev)
     beta = torch.randn((Hq,), generator=g, device=dev)
     out = torch.empty_like(q)
-    for _ in range(warmup):
-        _lib.decode(q, kc, vc, n_past, beta, M, z, out=out)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        _lib.decode(q, kc, vc, n_past, beta, M, z, out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+
+    def timed(call):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    us_binding = timed(lambda: _lib.decode(q, kc, vc, n_past, beta, M, z, out=out))
+    # The same call with its arguments marshalled once (the handle is the
+    # binding's cached one for these shapes and this stream).
+    lib = _lib.load()
+    h = _lib.handle_for(q, kc, 1e-6, seq_len=CAP)
+    args = (h, q.data_ptr(), C, kc.data_ptr(), vc.data_ptr(), n_past, beta.data_ptr(),
+            M.data_ptr(), z.data_ptr(), out.data_ptr())
+    fn = lib.infini_attn_decode
+
+    def direct():
+        if fn(*args) != 0:
+            raise RuntimeError("infini_attn_decode failed")
+
+    us = timed(direct)
     if not bool(torch.isfinite(out.float()).all()):
         raise RuntimeError("non-finite output")
     nbytes = algorithmic_bytes(B, Hq, Hkv, D, C, n_past)
@@ -74,7 +94,8 @@ def case(shape, n_past, C, steps, warmup=20, seed=0):
     return {
         "workload": shape, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "d": D,
         "seg_len": CAP, "n_past": n_past, "new_rows": C, "steps": steps,
-        "us_per_call": us, "tokens_per_s": B * C / (us * 1e-6),
+        "us_per_call": us, "us_per_call_binding": us_binding,
+        "tokens_per_s": B * C / (us * 1e-6),
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "bytes_per_call": nbytes},
     }
