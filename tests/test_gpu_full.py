@@ -1,8 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
 times. The oracle recomputes the whole (M, z) chain of every kv head (so the
-final state is compared element by element) and, on sampled rows, the output
-one row at a time: local attention from the definition and retrieval from the
-oracle's own state before that row's segment."""
+final state is compared element by element) and, on sampled rows of every
+query head, the output one row at a time: local attention from the
+definition and retrieval from the oracle's own state before that row's
+segment."""
 
 import numpy as np
 import pytest
@@ -27,11 +28,15 @@ def _gpu():
 
 
 def sample_plan(w, rng):
+    """Every (batch, query head) pair; four segments (first, second, middle,
+    last); rows at the boundaries of the kernel's 32-row wave strips and 64-
+    and 256-row work items, the segment's last row, and six random ones."""
     S = w.n_segments
     segs = sorted({0, 1, S // 2, S - 1})
-    heads = sorted({(0, 0), (w.batch - 1, w.n_q_heads - 1), (0, w.n_q_heads // 2 + 1)})
-    rows = sorted({0, 1, 127, 128, 129, w.seg_len - 1} |
-                  set(int(x) for x in rng.integers(0, w.seg_len, 4)))
+    heads = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)]
+    edges = {0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, w.seg_len - 1}
+    rows = sorted({r for r in edges if r < w.seg_len} |
+                  set(int(x) for x in rng.integers(0, w.seg_len, 6)))
     return segs, heads, rows
 
 
