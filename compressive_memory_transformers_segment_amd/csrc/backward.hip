@@ -159,13 +159,26 @@ __device__ __forceinline__ void split_bf16x8(const float *x, bf16x8 &hi, bf16x8 
 
 // The 8 values of column c at rows kappa(8 st + e, g), e < 8, of a bf16 LDS
 // tile: the A operand matching a result block's registers 8 st .. 8 st + 7
-// used as the B operand (the contraction runs over the block's rows).
+// used as the B operand (the contraction runs over the block's rows). Those
+// rows are R .. R + 3 and R + 8 .. R + 11 with R = 16 st + 4 g, so two
+// transposing LDS reads (ds_read_b64_tr_b16) fetch them. In each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte pieces addressed by
+// lanes i / 4 + 4 j, j = 0 .. 3, in that order; lane A of the group addresses
+// row R + A / 4, columns c0 + 4 (A % 4) .. + 3, so lane i receives rows
+// R .. R + 3 of column c0 + i. The caller passes c = (a multiple of 32) +
+// lane % 32, and the whole wave takes part.
 template <int PB>
 __device__ __forceinline__ bf16x8 gather_rows(const uint16_t (*tile)[PB], int st, int g, int c) {
-  bf16x8 a;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) a[e] = __builtin_bit_cast(__bf16, tile[kappa(8 * st + e, g)][c]);
-  return a;
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const int A = static_cast<int>(threadIdx.x) & 15;
+  const int c0 = c - A;
+  auto rd = [&](int R) __attribute__((always_inline)) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s *)(&tile[R + A / 4][c0 + 4 * (A % 4)]));
+  };
+  const u32x2 lo = __builtin_bit_cast(u32x2, rd(16 * st + 4 * g));
+  const u32x2 hi = __builtin_bit_cast(u32x2, rd(16 * st + 8 + 4 * g));
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 // Workgroup barrier that orders LDS only: __syncthreads() also waits for the
