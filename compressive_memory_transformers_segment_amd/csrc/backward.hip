@@ -82,6 +82,21 @@ __device__ __forceinline__ float sum16(float x) {
 
 __device__ __forceinline__ float gate(float beta) { return 1.f / (1.f + expf(-beta)); }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// A lane's value combined with that of the lane 32 away (v_permlane32_swap
+// returns {x, x of lane ^ 32} in some order; max and sum are symmetric).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // sigma'(x) from sigma(x): 1 where x > 0 (sigma > 1), sigma itself elsewhere.
 __device__ __forceinline__ float elu1_grad_from(float s) { return fminf(s, 1.f); }
 
@@ -357,30 +372,41 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   };
 
   // Pass 1: online max, sum and E = sum_j P_ij (dO_i . v_j) of each row.
-  float m = -INFINITY, l = 0.f, ea = 0.f;
+  // Scores are masked only on tiles that hold a key some row of the wave must
+  // not see (the diagonal tile, keys past the segment end); elsewhere every
+  // key is visible to every row of the wave (rows past the segment end are
+  // never stored). The exponentials take the scale and log2(e) in one FMA.
+  const float sc2 = scale * kLog2e;
+  auto mask_scores = [&](f32x16 &st, int j0) __attribute__((always_inline)) {
+    if (j0 + kKT - 1 > wq0 || j0 + kKT > e) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + kappa(r, g);
+        if (!(key <= qi && key < e)) st[r] = -INFINITY;
+      }
+    }
+  };
+  float m = -INFINITY, l = 0.f, ea = 0.f;  // m: running max of the scaled scores
   pass([&](int j0) __attribute__((always_inline)) {
     f32x16 st, ot;
     scores(st, ot);
-    float x[16];
-    float mx = -INFINITY;
+    mask_scores(st, j0);
+    float mx = fmaxf(st[0], st[1]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = j0 + kappa(r, g);
-      x[r] = (key <= qi && key < e) ? st[r] * scale : -INFINITY;
-      mx = fmaxf(mx, x[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st[r], st[r + 1]));
+    mx = max_xor32(mx) * scale;  // the scale is positive: max(s) scale = max(s scale)
     const float mn = fmaxf(m, mx);
+    const float nb = -mn * kLog2e;
     float ps = 0.f, pe = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __expf(x[r] - mn);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sc2, nb));
       ps += p;
-      pe += p * ot[r];
+      pe = __builtin_fmaf(p, ot[r], pe);
     }
-    ps += __shfl_xor(ps, 32);
-    pe += __shfl_xor(pe, 32);
-    const float f = __expf(m - mn);
+    ps = sum_xor32(ps);
+    pe = sum_xor32(pe);
+    const float f = __builtin_amdgcn_exp2f((m - mn) * kLog2e);
     l = l * f + ps;
     ea = ea * f + pe;
     m = mn;
@@ -392,16 +418,17 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   f32x16 dqa[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) dqa[cb] = zero16();
+  // (1 - g) P in one exponential: log2(1 - g) joins the row's shift (-inf,
+  // and so zero probabilities, when the gate is fully open).
+  const float bq = __log2f(1.f - gam) - lse * kLog2e;
   pass([&](int j0) __attribute__((always_inline)) {
     f32x16 st, ot;
     scores(st, ot);
+    mask_scores(st, j0);
     float ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = j0 + kappa(r, g);
-      const float p = (key <= qi && key < e) ? __expf(st[r] * scale - lse) : 0.f;
-      ds[r] = (1.f - gam) * p * (ot[r] - E);
-    }
+    for (int r = 0; r < 16; ++r)
+      ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sc2, bq)) * (ot[r] - E);
     if constexpr (BF) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -535,7 +562,8 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   __shared__ float sO[BF ? 1 : 32][P];
   __shared__ __attribute__((aligned(16))) uint16_t sQb[BF ? 32 : 1][PB];
   __shared__ __attribute__((aligned(16))) uint16_t sOb[BF ? 32 : 1][PB];
-  __shared__ float sL[32], sE[32];
+  __shared__ __attribute__((aligned(16))) float sL[32];
+  __shared__ __attribute__((aligned(16))) float sE[32];
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -550,7 +578,12 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   const int key = wk0 + l32;    // this lane's key
   const bool kvalid = key < e;
   const float scale = 1.f / sqrtf(static_cast<float>(D));
+  const float sc2 = scale * kLog2e;
   const size_t krow = static_cast<size_t>(kvh) * L + key;
+  // Row shift of a chunk's rows as kept in sL: log2(1 - g) - lse log2(e).
+  auto row_shift = [&](int hl, float lse_row) __attribute__((always_inline)) {
+    return __log2f(1.f - gate(beta[j * grp + hl])) - lse_row * kLog2e;
+  };
 
   float kr[BF ? 1 : D / 2], vr[BF ? 1 : D / 2];
   bf16x8 kb8[BF ? D / 16 : 1], vb8[BF ? D / 16 : 1];
@@ -586,8 +619,6 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   // One chunk: query head hl of the group, rows i0 .. i0 + 31 (staged in
   // sQb / sOb or sQ / sO, with their lse and E in sL / sE).
   auto chunk = [&](int hl, int i0) __attribute__((always_inline)) {
-    const int h = j * grp + hl;
-    const float gam = gate(beta[h]);
     f32x16 st = zero16(), ot = zero16();
     if constexpr (BF) {
 #pragma unroll
@@ -602,14 +633,28 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
         ot = mfma32(sO[l32][2 * u + g], vr[u], ot);
       }
     }
+    // Masked only where some key of the wave is after some row of the chunk
+    // or past the segment end, or some row is past it. sL holds each row's
+    // log2(1 - g) - lse log2(e), so one FMA and one exponential give (1 - g) P.
+    if (wk0 + 31 > i0 || i0 + 32 > e || wk0 + 32 > e) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i0 + kappa(r, g);
+        if (!(key <= row && row < e && kvalid)) st[r] = -INFINITY;
+      }
+    }
     float pw[16], ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qr = kappa(r, g), row = i0 + qr;
-      const bool vis = key <= row && row < e && kvalid;
-      const float p = vis ? __expf(st[r] * scale - sL[qr]) : 0.f;
-      pw[r] = (1.f - gam) * p;
-      ds[r] = pw[r] * (ot[r] - sE[qr]);
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 bl = *reinterpret_cast<const float4 *>(&sL[8 * r4 + 4 * g]);
+      const float4 ee = *reinterpret_cast<const float4 *>(&sE[8 * r4 + 4 * g]);
+      const float blv[4] = {bl.x, bl.y, bl.z, bl.w}, eev[4] = {ee.x, ee.y, ee.z, ee.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * r4 + i;
+        pw[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sc2, blv[i]));
+        ds[r] = pw[r] * (ot[r] - eev[i]);
+      }
     }
     if constexpr (BF) {
 #pragma unroll
@@ -677,7 +722,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
         }
       }
       if (t < 32) {
-        sL[t] = t < rows ? pl : 0.f;
+        sL[t] = t < rows ? row_shift(c / nci, pl) : 0.f;
         sE[t] = t < rows ? pe : 0.f;
       }
     };
@@ -700,7 +745,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
         load_rows<T, D, P>(sQ, q + (hrow + i0) * D, 32, rows, false);
         load_rows<T, D, P>(sO, dout + (hrow + i0) * D, 32, rows, false);
         if (t < 32) {
-          sL[t] = t < rows ? lse[hrow + i0 + t] : 0.f;
+          sL[t] = t < rows ? row_shift(hl, lse[hrow + i0 + t]) : 0.f;
           sE[t] = t < rows ? E[hrow + i0 + t] : 0.f;
         }
         __syncthreads();
