@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   constexpr int QT = 128;
   constexpr bool BF = std::is_same<T, uint16_t>::value;
   constexpr int PB = D + 8;   // bf16 row stride: 16-byte aligned rows
-  __shared__ float sK[kKT][P];  // fp32 storage: key tile; both: 32-row chunks of Mp^T
+  __shared__ float sK[BF ? 1 : kKT][P];  // fp32 storage: key tile, 32-row chunks of Mp^T
   __shared__ float sV[BF ? 1 : kKT][P];
   __shared__ __attribute__((aligned(16))) uint16_t sKb[BF ? kKT : 1][PB];  // bf16 key tile
   __shared__ __attribute__((aligned(16))) uint16_t sVb[BF ? kKT : 1][PB];
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
 
   // This lane's query row and d_out row as B operands: element 2 u + g (fp32
   // storage), elements 16 t + 8 g + e (bf16 storage).
-  float qr[D / 2], orow[BF ? 1 : D / 2];
+  float qr[BF ? 1 : D / 2], orow[BF ? 1 : D / 2];
   bf16x8 qb8[BF ? D / 16 : 1], ob8[BF ? D / 16 : 1];
   if constexpr (BF) {
     const bf16x8 z8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
@@ -450,56 +450,145 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   });
 
   // Retrieval backward from the pre-segment snapshot (Mp^T in mt, zp in zpre).
-  if constexpr (BF) {
-#pragma unroll
-    for (int u = 0; u < D / 2; ++u) qr[u] = qvalid ? load_as_f32(q, (qbase + qi) * D + 2 * u + g) : 0.f;
-  }
-#pragma unroll
-  for (int u = 0; u < D / 2; ++u) qr[u] = elu1(qr[u]);  // sigma(q), element 2 u + g
-  float den = 0.f;
-#pragma unroll
-  for (int u = 0; u < D / 2; ++u) den += qr[u] * sZ[2 * u + g];
-  den += __shfl_xor(den, 32) + eps;
   const float *mtp = mt + (kvh * S + s) * D * D;
   f32x16 dsq[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) dsq[cb] = zero16();
   float s1 = 0.f;  // dO_i . num_i, this lane's part
-  for (int jb = 0; jb < NB; ++jb) {
-    __syncthreads();
-    for (int idx = t; idx < kKT * D; idx += kThreads) {
-      const int jj = idx / D, c = idx % D;  // sK[jj][c] = Mp^T[32 jb + jj][c]
-      sK[jj][c] = mtp[static_cast<size_t>(32 * jb + jj) * D + c];
-    }
-    __syncthreads();
-    if (!wave_live) continue;
-    f32x16 num = zero16();  // num^T rows 32 jb + kappa, column = this lane's query
+  float den = 0.f;
+  if constexpr (BF) {
+    // bf16 storage: both products of the retrieval backward run on the bf16
+    // matrix cores. Their fp32 factors (sigma(q), Mp, dnum) are carried as
+    // bf16 pairs hi + lo, and each product takes hi.hi + hi.lo + lo.hi
+    // (about 2^-16 relative; the lo.lo term is below that).
+    //   num^T = Mp^T sigma(Q)^T: sigma(q) of this lane's query at d =
+    //   16 t + 8 g + e is the B operand of step t;
+    //   dsq^T = Mp dnum^T: dnum from registers, as dS in the dq product.
+    const uint16_t *q16 = reinterpret_cast<const uint16_t *>(q);
+    const uint16_t *o16 = reinterpret_cast<const uint16_t *>(dout);
+    bf16x8 sqh[D / 16], sql[D / 16];
 #pragma unroll
-    for (int u = 0; u < D / 2; ++u) num = mfma32(sK[l32][2 * u + g], qr[u], num);
-    float dn[16];
+    for (int u = 0; u < D / 16; ++u) {
+      const u32x4 wq = qvalid ? *reinterpret_cast<const u32x4 *>(q16 + (qbase + qi) * D + 16 * u +
+                                                                  8 * g)
+                              : u32x4{0u, 0u, 0u, 0u};
+      float x[8];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int j = 32 * jb + 8 * r4 + 4 * g;
-      float o4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o4[i] = qvalid ? load_as_f32(dout, (qbase + qi) * D + j + i) : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s1 += o4[i] * num[4 * r4 + i];
-        dn[4 * r4 + i] = gam * o4[i] / den;
+      for (int e2 = 0; e2 < 4; ++e2) {
+        x[2 * e2] = elu1(lo_bf16(wq[e2]));
+        x[2 * e2 + 1] = elu1(hi_bf16(wq[e2]));
       }
-      if (qvalid) {
-        float *dst = dnum_out + (qbase + qi) * D + j;
-        *reinterpret_cast<float4 *>(dst) = make_float4(dn[4 * r4], dn[4 * r4 + 1],
-                                                       dn[4 * r4 + 2], dn[4 * r4 + 3]);
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) den += x[e2] * sZ[16 * u + 8 * g + e2];
+      split_bf16x8(x, sqh[u], sql[u]);
+    }
+    den = sum_xor32(den) + eps;
+    const float gd = gam / den;
+    for (int jb = 0; jb < NB; ++jb) {
+      __syncthreads();
+      // Rows 32 jb .. 32 jb + 31 of Mp^T as bf16 hi (sKb) and lo (sVb) parts.
+      for (int idx = t; idx < kKT * D / 4; idx += kThreads) {
+        const int jj = idx / (D / 4), c = 4 * (idx % (D / 4));
+        const float4 m4 = *reinterpret_cast<const float4 *>(mtp + static_cast<size_t>(32 * jb + jj) *
+                                                                      D + c);
+        const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const __bf16 h0 = static_cast<__bf16>(mv[2 * i]), h1 = static_cast<__bf16>(mv[2 * i + 1]);
+          hw[i] = pack_bf16x2(static_cast<float>(h0), static_cast<float>(h1));
+          lw[i] = pack_bf16x2(mv[2 * i] - static_cast<float>(h0), mv[2 * i + 1] - static_cast<float>(h1));
+        }
+        *reinterpret_cast<u32x2 *>(&sKb[jj][c]) = u32x2{hw[0], hw[1]};
+        *reinterpret_cast<u32x2 *>(&sVb[jj][c]) = u32x2{lw[0], lw[1]};
+      }
+      __syncthreads();
+      if (!wave_live) continue;
+      f32x16 num = zero16();  // num^T rows 32 jb + kappa, column = this lane's query
+#pragma unroll
+      for (int u = 0; u < D / 16; ++u) {
+        const bf16x8 mh = ld_bf16x8(&sKb[l32][16 * u + 8 * g]);
+        const bf16x8 ml = ld_bf16x8(&sVb[l32][16 * u + 8 * g]);
+        num = mfma32(mh, sqh[u], num);
+        num = mfma32(mh, sql[u], num);
+        num = mfma32(ml, sqh[u], num);
+      }
+      float dn[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int j = 32 * jb + 8 * r4 + 4 * g;
+        const u32x2 wo = qvalid ? *reinterpret_cast<const u32x2 *>(o16 + (qbase + qi) * D + j)
+                                : u32x2{0u, 0u};
+        const float o4[4] = {lo_bf16(wo[0]), hi_bf16(wo[0]), lo_bf16(wo[1]), hi_bf16(wo[1])};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s1 += o4[i] * num[4 * r4 + i];
+          dn[4 * r4 + i] = gd * o4[i];
+        }
+        if (qvalid) {
+          float *dst = dnum_out + (qbase + qi) * D + j;
+          *reinterpret_cast<float4 *>(dst) = make_float4(dn[4 * r4], dn[4 * r4 + 1],
+                                                         dn[4 * r4 + 2], dn[4 * r4 + 3]);
+        }
+      }
+      // dsq^T[c][i] += sum_j Mp[c][j] dnum[i][j], j = 32 jb + kappa(r, g).
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        bf16x8 dh, dl;
+        split_bf16x8(dn + 8 * st, dh, dl);
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+          const bf16x8 mh = gather_rows<PB>(sKb, st, g, 32 * cb + l32);
+          const bf16x8 ml = gather_rows<PB>(sVb, st, g, 32 * cb + l32);
+          dsq[cb] = mfma32(mh, dh, dsq[cb]);
+          dsq[cb] = mfma32(mh, dl, dsq[cb]);
+          dsq[cb] = mfma32(ml, dh, dsq[cb]);
+        }
       }
     }
-    // dsq^T[c][i] += sum_j Mp[c][j] dnum[i][j], j = 32 jb + kappa(r, g).
+  } else {
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb)
+    for (int u = 0; u < D / 2; ++u) qr[u] = elu1(qr[u]);  // sigma(q), element 2 u + g
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dsq[cb] = mfma32(sK[kappa(r, g)][32 * cb + l32], dn[r], dsq[cb]);
+    for (int u = 0; u < D / 2; ++u) den += qr[u] * sZ[2 * u + g];
+    den += __shfl_xor(den, 32) + eps;
+    for (int jb = 0; jb < NB; ++jb) {
+      __syncthreads();
+      for (int idx = t; idx < kKT * D; idx += kThreads) {
+        const int jj = idx / D, c = idx % D;  // sK[jj][c] = Mp^T[32 jb + jj][c]
+        sK[jj][c] = mtp[static_cast<size_t>(32 * jb + jj) * D + c];
+      }
+      __syncthreads();
+      if (!wave_live) continue;
+      f32x16 num = zero16();  // num^T rows 32 jb + kappa, column = this lane's query
+#pragma unroll
+      for (int u = 0; u < D / 2; ++u) num = mfma32(sK[l32][2 * u + g], qr[u], num);
+      float dn[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int j = 32 * jb + 8 * r4 + 4 * g;
+        float o4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o4[i] = qvalid ? load_as_f32(dout, (qbase + qi) * D + j + i) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s1 += o4[i] * num[4 * r4 + i];
+          dn[4 * r4 + i] = gam * o4[i] / den;
+        }
+        if (qvalid) {
+          float *dst = dnum_out + (qbase + qi) * D + j;
+          *reinterpret_cast<float4 *>(dst) = make_float4(dn[4 * r4], dn[4 * r4 + 1],
+                                                         dn[4 * r4 + 2], dn[4 * r4 + 3]);
+        }
+      }
+      // dsq^T[c][i] += sum_j Mp[c][j] dnum[i][j], j = 32 jb + kappa(r, g).
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          dsq[cb] = mfma32(sK[kappa(r, g)][32 * cb + l32], dn[r], dsq[cb]);
+    }
   }
   s1 += __shfl_xor(s1, 32);
   const float dden = -gam * s1 / (den * den);
