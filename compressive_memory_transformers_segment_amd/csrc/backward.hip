@@ -871,14 +871,29 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
     const T *__restrict__ x, const T *__restrict__ x2, const float *__restrict__ dnum,
     const float *__restrict__ dden, const float *__restrict__ zpre, int Hq, int Hkv, int L, int N,
     int S, float eps, int rows_per_block, float *__restrict__ part) {
-  constexpr int P = D + 1;
-  constexpr int MI = D / 16;
-  __shared__ float sA[kKT][P];
-  __shared__ float sB[kKT][P];
+  // The D x D sum of outer products over a range of rows runs on the bf16
+  // matrix cores: each fp32 factor is staged as a bf16 pair hi + lo, and each
+  // product takes hi.hi + hi.lo + lo.hi (about 2^-16 relative; kind 2 with
+  // bf16 storage has an exact bf16 v, so its lo part is zero and skipped).
+  // A 32-row chunk is staged row-major; the MFMA operands read it with
+  // transposing LDS reads, both sides in the same row order, so the
+  // contraction runs over the chunk's rows. The 32 x 32 output blocks are
+  // split over the four waves.
+  constexpr bool BF = std::is_same<T, uint16_t>::value;
+  constexpr bool B_EXACT = KIND == 2 && BF;
+  constexpr int PB = D + 8;
+  constexpr int NC = D / 32;                        // 32-wide blocks per side
+  constexpr int NBLK = NC * NC;
+  constexpr int BPW = NBLK >= 4 ? NBLK / 4 : 1;     // output blocks per wave
+  __shared__ __attribute__((aligned(16))) uint16_t sAh[kKT][PB];
+  __shared__ __attribute__((aligned(16))) uint16_t sAl[kKT][PB];
+  __shared__ __attribute__((aligned(16))) uint16_t sBh[kKT][PB];
+  __shared__ __attribute__((aligned(16))) uint16_t sBl[B_EXACT ? 1 : kKT][PB];
   __shared__ float sX[kKT];
   __shared__ float sZ[D];
 
-  const int t = threadIdx.x, r0 = t >> 4, c0 = t & 15;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
   const int s = blockIdx.y, kvh = blockIdx.z;
   const int b = kvh / Hkv, j = kvh % Hkv;
   const int grp = Hq / Hkv;
@@ -904,46 +919,113 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
     }
     return static_cast<size_t>(kvh) * L + a + u;
   };
+  // Four consecutive elements of row `row` of a [rows][D] tensor as fp32.
+  auto load4 = [&](const T *src, size_t row, int c) __attribute__((always_inline)) {
+    float4 r;
+    if constexpr (BF) {
+      const u32x2 w2 = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(src) +
+                                                        row * D + c);
+      r = make_float4(lo_bf16(w2[0]), hi_bf16(w2[0]), lo_bf16(w2[1]), hi_bf16(w2[1]));
+    } else {
+      r = *reinterpret_cast<const float4 *>(src + row * D + c);
+    }
+    return r;
+  };
+  // Split four values into bf16 hi and lo parts and store them at (r, c).
+  auto put4 = [&](uint16_t (*th)[PB], uint16_t (*tl)[PB], int r, int c, const float (&v)[4])
+                  __attribute__((always_inline)) {
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float h0 = static_cast<float>(static_cast<__bf16>(v[2 * i]));
+      const float h1 = static_cast<float>(static_cast<__bf16>(v[2 * i + 1]));
+      hw[i] = pack_bf16x2(h0, h1);
+      lw[i] = pack_bf16x2(v[2 * i] - h0, v[2 * i + 1] - h1);
+    }
+    *reinterpret_cast<u32x2 *>(&th[r][c]) = u32x2{hw[0], hw[1]};
+    if (tl != nullptr) *reinterpret_cast<u32x2 *>(&tl[r][c]) = u32x2{lw[0], lw[1]};
+  };
 
-  float acc[MI][MI];
-  zero(acc);
+  f32x16 acc[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) acc[i] = zero16();
   float racc = 0.f;
   for (int c0u = u0; c0u < u1; c0u += kKT) {
     const int cnt = min(kKT, u1 - c0u);
     __syncthreads();
-    for (int idx = t; idx < kKT * D; idx += kThreads) {
-      const int r = idx / D, c = idx % D;
-      float av = 0.f, bv = 0.f;
+    for (int idx = t; idx < kKT * D / 4; idx += kThreads) {
+      const int r = idx / (D / 4), c = 4 * (idx % (D / 4));
+      float av[4] = {0.f, 0.f, 0.f, 0.f}, bv[4] = {0.f, 0.f, 0.f, 0.f};
       if (r < cnt) {
         const size_t row = src_row(c0u + r);
-        av = elu1(load_as_f32(x, row * D + c));
-        bv = KIND == 0 ? dnum[row * D + c] : (KIND == 2 ? load_as_f32(x2, row * D + c) : av);
+        const float4 xa = load4(x, row, c);
+        av[0] = elu1(xa.x);
+        av[1] = elu1(xa.y);
+        av[2] = elu1(xa.z);
+        av[3] = elu1(xa.w);
+        if (KIND == 0) {
+          const float4 d4 = *reinterpret_cast<const float4 *>(dnum + row * D + c);
+          bv[0] = d4.x; bv[1] = d4.y; bv[2] = d4.z; bv[3] = d4.w;
+        } else if (KIND == 2) {
+          const float4 v4 = load4(x2, row, c);
+          bv[0] = v4.x; bv[1] = v4.y; bv[2] = v4.z; bv[3] = v4.w;
+        }
       }
-      sA[r][c] = av;
-      sB[r][c] = bv;
+      put4(sAh, sAl, r, c, av);
+      if (KIND != 1) put4(sBh, B_EXACT ? nullptr : sBl, r, c, bv);
     }
     if (KIND == 0 && t < kKT) sX[t] = t < cnt ? dden[src_row(c0u + t)] : 0.f;
     __syncthreads();
     if (KIND == 1) {
+      // B = sigma(k) / (sigma(k) . z + eps), row by row.
       if (t < kKT) {
         float d = eps;
-        for (int c = 0; c < D; ++c) d += sA[t][c] * sZ[c];
+        for (int c = 0; c < D; ++c)
+          d += (bf16_to_f32(sAh[t][c]) + bf16_to_f32(sAl[t][c])) * sZ[c];
         sX[t] = 1.f / d;
       }
       __syncthreads();
-      mm16<MI, MI>(acc, kKT, [&](int r, int kk) { return sA[kk][r]; },
-                   [&](int kk, int c) { return sB[kk][c] * sX[kk]; });
-    } else {
-      mm16<MI, MI>(acc, kKT, [&](int r, int kk) { return sA[kk][r]; },
-                   [&](int kk, int c) { return sB[kk][c]; });
-      if (KIND == 0 && t < D)
-        for (int kk = 0; kk < kKT; ++kk) racc += sA[kk][t] * sX[kk];
+      for (int idx = t; idx < kKT * D / 4; idx += kThreads) {
+        const int r = idx / (D / 4), c = 4 * (idx % (D / 4));
+        float bv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bv[i] = (bf16_to_f32(sAh[r][c + i]) + bf16_to_f32(sAl[r][c + i])) * sX[r];
+        put4(sBh, sBl, r, c, bv);
+      }
+      __syncthreads();
+    }
+    if (KIND == 0 && t < D)
+      for (int kk = 0; kk < kKT; ++kk)
+        racc += (bf16_to_f32(sAh[kk][t]) + bf16_to_f32(sAl[kk][t])) * sX[kk];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int ib = w * BPW + i;
+      if (ib >= NBLK) break;
+      const int rb = ib / NC, cb = ib % NC;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 ah = gather_rows<PB>(sAh, st, g, 32 * rb + l32);
+        const bf16x8 al = gather_rows<PB>(sAl, st, g, 32 * rb + l32);
+        const bf16x8 bh = gather_rows<PB>(sBh, st, g, 32 * cb + l32);
+        acc[i] = mfma32(ah, bh, acc[i]);
+        acc[i] = mfma32(al, bh, acc[i]);
+        if constexpr (!B_EXACT) {
+          const bf16x8 bl = gather_rows<PB>(sBl, st, g, 32 * cb + l32);
+          acc[i] = mfma32(ah, bl, acc[i]);
+        }
+      }
     }
   }
+  // Lane (l32, g) holds output column 32 cb + l32, rows 32 rb + kappa(r, g).
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < BPW; ++i) {
+    const int ib = w * BPW + i;
+    if (ib >= NBLK) break;
+    const int rb = ib / NC, cb = ib % NC;
 #pragma unroll
-    for (int jj = 0; jj < MI; ++jj) o[(r0 + 16 * i) * D + c0 + 16 * jj] = acc[i][jj];
+    for (int r = 0; r < 16; ++r) o[(32 * rb + kappa(r, g)) * D + 32 * cb + l32] = acc[i][r];
+  }
   if (KIND == 0 && t < D) o[D * D + t] = racc;
 }
 
