@@ -651,6 +651,9 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   __shared__ float sO[BF ? 1 : 32][P];
   __shared__ __attribute__((aligned(16))) uint16_t sQb[BF ? 32 : 1][PB];
   __shared__ __attribute__((aligned(16))) uint16_t sOb[BF ? 32 : 1][PB];
+  // bf16: the workgroup's V rows (each lane reads back only the row it wrote),
+  // which keeps them out of the register file.
+  __shared__ __attribute__((aligned(16))) uint16_t sVw[BF ? KT : 1][PB];
   __shared__ __attribute__((aligned(16))) float sL[32];
   __shared__ __attribute__((aligned(16))) float sE[32];
 
@@ -675,14 +678,15 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   };
 
   float kr[BF ? 1 : D / 2], vr[BF ? 1 : D / 2];
-  bf16x8 kb8[BF ? D / 16 : 1], vb8[BF ? D / 16 : 1];
+  bf16x8 kb8[BF ? D / 16 : 1];
   if constexpr (BF) {
     const bf16x8 z8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
     for (int u = 0; u < D / 16; ++u) {
       const size_t o = krow * D + 16 * u + 8 * g;
       kb8[u] = kvalid ? ld_bf16x8(reinterpret_cast<const uint16_t *>(k) + o) : z8;
-      vb8[u] = kvalid ? ld_bf16x8(reinterpret_cast<const uint16_t *>(v) + o) : z8;
+      *reinterpret_cast<bf16x8 *>(&sVw[32 * w + l32][16 * u + 8 * g]) =
+          kvalid ? ld_bf16x8(reinterpret_cast<const uint16_t *>(v) + o) : z8;
     }
   } else {
 #pragma unroll
@@ -713,7 +717,8 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
 #pragma unroll
       for (int u = 0; u < D / 16; ++u) {
         st = mfma32(ld_bf16x8(&sQb[l32][16 * u + 8 * g]), kb8[u], st);
-        ot = mfma32(ld_bf16x8(&sOb[l32][16 * u + 8 * g]), vb8[u], ot);
+        ot = mfma32(ld_bf16x8(&sOb[l32][16 * u + 8 * g]), ld_bf16x8(&sVw[32 * w + l32][16 * u + 8 * g]),
+                    ot);
       }
     } else {
 #pragma unroll
