@@ -236,6 +236,9 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   __shared__ float sV[BF ? 1 : kKT][P];
   __shared__ __attribute__((aligned(16))) uint16_t sKb[BF ? kKT : 1][PB];  // bf16 key tile
   __shared__ __attribute__((aligned(16))) uint16_t sVb[BF ? kKT : 1][PB];
+  // bf16: the workgroup's d_out rows (each lane reads back only the row it
+  // wrote), which keeps them out of the register file.
+  __shared__ __attribute__((aligned(16))) uint16_t sOw[BF ? QT : 1][PB];
   __shared__ float sZ[D];
   __shared__ float sAcc[kThreads / 64];
 
@@ -271,14 +274,15 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   // This lane's query row and d_out row as B operands: element 2 u + g (fp32
   // storage), elements 16 t + 8 g + e (bf16 storage).
   float qr[BF ? 1 : D / 2], orow[BF ? 1 : D / 2];
-  bf16x8 qb8[BF ? D / 16 : 1], ob8[BF ? D / 16 : 1];
+  bf16x8 qb8[BF ? D / 16 : 1];
   if constexpr (BF) {
     const bf16x8 z8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
     for (int u = 0; u < D / 16; ++u) {
       const size_t o = (qbase + qi) * D + 16 * u + 8 * g;
       qb8[u] = qvalid ? ld_bf16x8(reinterpret_cast<const uint16_t *>(q) + o) : z8;
-      ob8[u] = qvalid ? ld_bf16x8(reinterpret_cast<const uint16_t *>(dout) + o) : z8;
+      *reinterpret_cast<bf16x8 *>(&sOw[32 * w + l32][16 * u + 8 * g]) =
+          qvalid ? ld_bf16x8(reinterpret_cast<const uint16_t *>(dout) + o) : z8;
     }
   } else {
 #pragma unroll
@@ -332,7 +336,8 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
 #pragma unroll
       for (int u = 0; u < D / 16; ++u) {
         st = mfma32(ld_bf16x8(&sKb[l32][16 * u + 8 * g]), qb8[u], st);
-        ot = mfma32(ld_bf16x8(&sVb[l32][16 * u + 8 * g]), ob8[u], ot);
+        ot = mfma32(ld_bf16x8(&sVb[l32][16 * u + 8 * g]),
+                    ld_bf16x8(&sOw[32 * w + l32][16 * u + 8 * g]), ot);
       }
     } else {
 #pragma unroll
