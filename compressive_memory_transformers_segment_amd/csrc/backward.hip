@@ -1133,19 +1133,53 @@ __global__ __launch_bounds__(kThreads) void bwd_gm_chain_kernel(
 
 // Per-segment column sums of sigma(k): dz[unit][c] = sum over the segment's
 // rows of sigma(k[i][c]).
+constexpr int kZsumThreads = 512;
+
+// Column sums of sigma(k) over one segment's rows. Each thread reads 8
+// columns of a row (16 bytes for bf16 storage) and walks rows with a stride
+// of RG = 512 / (D / 8) row groups, four rows in flight; the row groups are
+// then added in index order, so the result does not depend on timing.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_zsum_kernel(const T *__restrict__ k, int L, int N,
-                                                            int S, float *__restrict__ dz) {
-  constexpr int RG = kThreads / D;  // row groups
-  __shared__ float part[RG][D];
-  const int t = threadIdx.x, c = t % D, rg = t / D;
+__global__ __launch_bounds__(kZsumThreads) void bwd_zsum_kernel(const T *__restrict__ k, int L,
+                                                                int N, int S, float *__restrict__ dz) {
+  constexpr int CPR = D / 8;                 // threads per row
+  constexpr int RG = kZsumThreads / CPR;     // row groups
+  __shared__ float part[RG][D + 1];
+  const int t = threadIdx.x, c8 = 8 * (t % CPR), rg = t / CPR;
   const int s = blockIdx.x;
   const size_t kvh = blockIdx.y;
   const int a = s * N, e = min(a + N, L);
   const T *kb = k + kvh * L * D;
-  float acc = 0.f;
-  for (int i = a + rg; i < e; i += RG) acc += elu1(load_as_f32(kb, static_cast<size_t>(i) * D + c));
-  part[rg][c] = acc;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add_row = [&](int i) __attribute__((always_inline)) {
+    float x[8];
+    if constexpr (std::is_same<T, uint16_t>::value) {
+      const u32x4 w4 = *reinterpret_cast<const u32x4 *>(
+          reinterpret_cast<const uint16_t *>(kb) + static_cast<size_t>(i) * D + c8);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        x[2 * h] = lo_bf16(w4[h]);
+        x[2 * h + 1] = hi_bf16(w4[h]);
+      }
+    } else {
+      const float4 f0 = *reinterpret_cast<const float4 *>(kb + static_cast<size_t>(i) * D + c8);
+      const float4 f1 = *reinterpret_cast<const float4 *>(kb + static_cast<size_t>(i) * D + c8 + 4);
+      x[0] = f0.x; x[1] = f0.y; x[2] = f0.z; x[3] = f0.w;
+      x[4] = f1.x; x[5] = f1.y; x[6] = f1.z; x[7] = f1.w;
+    }
+#pragma unroll
+    for (int h = 0; h < 8; ++h) acc[h] += elu1(x[h]);
+  };
+  int i = a + rg;
+  for (; i + 3 * RG < e; i += 4 * RG) {
+    add_row(i);
+    add_row(i + RG);
+    add_row(i + 2 * RG);
+    add_row(i + 3 * RG);
+  }
+  for (; i < e; i += RG) add_row(i);
+#pragma unroll
+  for (int h = 0; h < 8; ++h) part[rg][c8 + h] = acc[h];
   __syncthreads();
   if (t < D) {
     float z = 0.f;
@@ -1513,7 +1547,7 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
     return hipErrorInvalidConfiguration;
   // The forward's state before every segment: z prefix, then G_s (delta) and
   // H_s in parallel, then the d x d chain.
-  bwd_zsum_kernel<T, D><<<dim3(g.S, kvheads), kThreads, 0, st>>>(k, g.L, g.N, g.S, w.dzs);
+  bwd_zsum_kernel<T, D><<<dim3(g.S, kvheads), kZsumThreads, 0, st>>>(k, g.L, g.N, g.S, w.dzs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   bwd_zprefix_kernel<<<kvheads, D, 0, st>>>(w.dzs, z0, g.S, D, w.z_pre);
