@@ -1352,6 +1352,254 @@ __global__ __launch_bounds__(kThreads) void bwd_update_kernel(
   }
 }
 
+// update on the bf16 matrix cores (bf16 storage, d = 128): the same
+// gradients as bwd_update_kernel for 128 rows of a segment (32 per wave).
+// Every product is taken transposed, so that its result sits with one row
+// per lane, which is the B-operand layout of the next product:
+//   Y^T  = gM^T sk^T,  nk^T = Mp^T sk^T       (sk = sigma(k) of the rows)
+//   dsk^T = gM W^T - Mp (Y / denk)^T           (linear: gM v^T)
+// with W = v - nk / denk. The fp32 factors are bf16 pairs hi + lo and each
+// product takes hi.hi + hi.lo + lo.hi (about 2^-16 relative); v is exact in
+// bf16. gM_s and M_{s-1}^T are staged once per workgroup as bf16 hi / lo
+// tiles; A operands that contract over a tile's rows use transposing LDS
+// reads, those along a row two 8-byte reads (contraction index kappa order
+// on both sides). One workgroup per CU (139 KB of LDS).
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_update_mfma_kernel(
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const float *__restrict__ mt,
+    const float *__restrict__ zpre, const float *__restrict__ gma, int L, int N, int S, float eps,
+    int delta, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ qz_part) {
+  constexpr int PB = D + 8;
+  constexpr int NC = D / 32;  // 32-wide blocks along d
+  constexpr int RW = 32 * (kThreads / 64);  // rows per workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t sGh[D][PB];  // gM_s, hi
+  __shared__ __attribute__((aligned(16))) uint16_t sGl[D][PB];  // gM_s, lo
+  __shared__ __attribute__((aligned(16))) uint16_t sMh[D][PB];  // M_{s-1}^T, hi
+  __shared__ __attribute__((aligned(16))) uint16_t sMl[D][PB];  // M_{s-1}^T, lo
+  __shared__ float sZ[D];
+  static_assert(static_cast<size_t>(RW) * (D + 1) * 4 <= sizeof(sGh) + sizeof(sGl),
+                "the qz reduction reuses the gM tiles");
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int s = blockIdx.y, kvh = blockIdx.z;
+  const int a = s * N, e = min(a + N, L);
+  const int i0 = a + blockIdx.x * RW;
+  const size_t unit = static_cast<size_t>(kvh) * S + s;
+  float *qzp = qz_part + (unit * gridDim.x + blockIdx.x) * D;
+  if (i0 >= e) {
+    if (delta)
+      for (int c = t; c < D; c += kThreads) qzp[c] = 0.f;
+    return;
+  }
+  const int r = i0 + 32 * w + l32;  // this lane's row
+  const bool rvalid = r < e;
+  const size_t roff = (static_cast<size_t>(kvh) * L + r) * D;
+  const float *gm = gma + unit * D * D;
+  const float *mtp = mt + unit * D * D;
+  for (int c = t; c < D; c += kThreads) sZ[c] = zpre[(static_cast<size_t>(kvh) * (S + 1) + s) * D + c];
+  // gM_s and M_{s-1}^T as bf16 hi / lo tiles (row-major, as stored).
+  auto split4 = [](const float4 &x, u32x2 &h, u32x2 &l) __attribute__((always_inline)) {
+    const float xv[4] = {x.x, x.y, x.z, x.w};
+    float hf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hf[i] = static_cast<float>(static_cast<__bf16>(xv[i]));
+    h = u32x2{pack_bf16x2(hf[0], hf[1]), pack_bf16x2(hf[2], hf[3])};
+    l = u32x2{pack_bf16x2(xv[0] - hf[0], xv[1] - hf[1]), pack_bf16x2(xv[2] - hf[2], xv[3] - hf[3])};
+  };
+  for (int idx = t; idx < D * D / 4; idx += kThreads) {
+    const int row = idx / (D / 4), c = 4 * (idx % (D / 4));
+    u32x2 h, l;
+    split4(*reinterpret_cast<const float4 *>(gm + static_cast<size_t>(row) * D + c), h, l);
+    *reinterpret_cast<u32x2 *>(&sGh[row][c]) = h;
+    *reinterpret_cast<u32x2 *>(&sGl[row][c]) = l;
+    if (delta) {
+      split4(*reinterpret_cast<const float4 *>(mtp + static_cast<size_t>(row) * D + c), h, l);
+      *reinterpret_cast<u32x2 *>(&sMh[row][c]) = h;
+      *reinterpret_cast<u32x2 *>(&sMl[row][c]) = l;
+    }
+  }
+
+  // This lane's row of k (sk = sigma(k)) and v at columns 32 kb + kappa(8 st + e, g):
+  // the B operand of contraction step (kb, st), and the result registers of
+  // block kb (register 8 st + e).
+  auto row8 = [&](const uint16_t *src, int kb, int st) __attribute__((always_inline)) {
+    const int c0 = 32 * kb + 16 * st + 4 * g;
+    const u32x2 lo = rvalid ? *reinterpret_cast<const u32x2 *>(src + roff + c0) : u32x2{0u, 0u};
+    const u32x2 hi = rvalid ? *reinterpret_cast<const u32x2 *>(src + roff + c0 + 8) : u32x2{0u, 0u};
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  auto unpack8 = [](const u32x4 &w4, float (&x)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      x[2 * h] = lo_bf16(w4[h]);
+      x[2 * h + 1] = hi_bf16(w4[h]);
+    }
+  };
+  bf16x8 skh[NC][2], skl[NC][2];
+  float skv[NC][16];  // sigma(k) in result-register order
+  float dpart = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NC; ++kb)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      float x[8];
+      unpack8(row8(k, kb, st), x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i] = rvalid ? elu1(x[i]) : 0.f;  // rows past the segment end: zero
+        skv[kb][8 * st + i] = x[i];
+        dpart += x[i] * sZ[32 * kb + kappa(8 * st + i, g)];
+      }
+      split_bf16x8(x, skh[kb][st], skl[kb][st]);
+    }
+  const float denk = sum_xor32(dpart) + eps;
+  __syncthreads();  // the tiles are staged
+
+  // A operand of output block cb, contraction step (kb, st): rows 32 cb + l32
+  // of a tile taken along its row (two 8-byte reads), or its column 32 cb +
+  // l32 taken over rows 32 kb + kappa (transposing reads).
+  auto along = [&](const uint16_t (*tile)[PB], int cb, int kb, int st) __attribute__((always_inline)) {
+    const uint16_t *p = &tile[32 * cb + l32][32 * kb + 16 * st + 4 * g];
+    const u32x2 lo = *reinterpret_cast<const u32x2 *>(p);
+    const u32x2 hi = *reinterpret_cast<const u32x2 *>(p + 8);
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
+  auto across = [&](const uint16_t (*tile)[PB], int cb, int kb, int st) __attribute__((always_inline)) {
+    return gather_rows<PB>(tile + 32 * kb, st, g, 32 * cb + l32);
+  };
+
+  // Y^T = gM^T sk^T (A = gM over rows: transposing reads).
+  f32x16 Y[NC];
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb) {
+    Y[cb] = zero16();
+#pragma unroll
+    for (int kb = 0; kb < NC; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 ah = across(sGh, cb, kb, st), al = across(sGl, cb, kb, st);
+        Y[cb] = mfma32(ah, skh[kb][st], Y[cb]);
+        Y[cb] = mfma32(ah, skl[kb][st], Y[cb]);
+        Y[cb] = mfma32(al, skh[kb][st], Y[cb]);
+      }
+  }
+  // dv += Y (four consecutive columns per register group).
+  if (rvalid) {
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4 *p = reinterpret_cast<float4 *>(dv + roff + 32 * cb + 8 * r4 + 4 * g);
+        float4 x = *p;
+        x.x += Y[cb][4 * r4];
+        x.y += Y[cb][4 * r4 + 1];
+        x.z += Y[cb][4 * r4 + 2];
+        x.w += Y[cb][4 * r4 + 3];
+        *p = x;
+      }
+  }
+
+  // B operands of dsk^T, contraction over c: W^T and -(Y / denk)^T (delta),
+  // or v^T (linear), from this lane's result registers.
+  bf16x8 bwh[NC][2], bwl[NC][2], byh[NC][2], byl[NC][2];
+  float ddenk = 0.f;
+  if (delta) {
+    // nk^T = Mp^T sk^T (A = M_{s-1}^T along rows).
+    float yn = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      f32x16 nk = zero16();
+#pragma unroll
+      for (int kb = 0; kb < NC; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 ah = along(sMh, cb, kb, st), al = along(sMl, cb, kb, st);
+          nk = mfma32(ah, skh[kb][st], nk);
+          nk = mfma32(ah, skl[kb][st], nk);
+          nk = mfma32(al, skh[kb][st], nk);
+        }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float vx[8], wx[8], yx[8];
+        unpack8(row8(v, cb, st), vx);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float nki = nk[8 * st + i], yi = Y[cb][8 * st + i];
+          yn += yi * nki;
+          wx[i] = vx[i] - nki / denk;
+          yx[i] = -(yi / denk);
+        }
+        split_bf16x8(wx, bwh[cb][st], bwl[cb][st]);
+        split_bf16x8(yx, byh[cb][st], byl[cb][st]);
+      }
+    }
+    ddenk = sum_xor32(yn) / (denk * denk);
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) bwh[cb][st] = __builtin_bit_cast(bf16x8, row8(v, cb, st));
+  }
+
+  // dsk^T = gM W^T - Mp (Y / denk)^T (A = gM along rows, Mp = (M^T)^T over rows).
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb) {
+    f32x16 ds = zero16();
+#pragma unroll
+    for (int kb = 0; kb < NC; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 gh = along(sGh, cb, kb, st), gl = along(sGl, cb, kb, st);
+        ds = mfma32(gh, bwh[kb][st], ds);
+        ds = mfma32(gl, bwh[kb][st], ds);
+        if (delta) {
+          ds = mfma32(gh, bwl[kb][st], ds);
+          const bf16x8 mh = across(sMh, cb, kb, st), ml = across(sMl, cb, kb, st);
+          ds = mfma32(mh, byh[kb][st], ds);
+          ds = mfma32(mh, byl[kb][st], ds);
+          ds = mfma32(ml, byh[kb][st], ds);
+        }
+      }
+    // dk += (dsk + ddenk zp) sigma'(k).
+    if (rvalid) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int c = 32 * cb + 8 * r4 + 4 * g;
+        float4 *p = reinterpret_cast<float4 *>(dk + roff + c);
+        float4 x = *p;
+        float gr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          gr[i] = (ds[4 * r4 + i] + (delta ? ddenk * sZ[c + i] : 0.f)) *
+                  elu1_grad_from(skv[cb][4 * r4 + i]);
+        x.x += gr[0];
+        x.y += gr[1];
+        x.z += gr[2];
+        x.w += gr[3];
+        *p = x;
+      }
+    }
+  }
+
+  if (delta) {
+    // qz_s partial over the workgroup's rows, added in row order: the gM
+    // tiles' LDS (no longer read) holds sk * ddenk row by row.
+    float (*sQ)[D + 1] = reinterpret_cast<float (*)[D + 1]>(&sGh[0][0]);
+    __syncthreads();  // every wave is done with the tiles
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sQ[32 * w + l32][32 * cb + kappa(i, g)] = skv[cb][i] * ddenk;
+    __syncthreads();
+    if (t < D) {
+      float acc = 0.f;
+      for (int rr = 0; rr < RW; ++rr) acc += sQ[rr][t];
+      qzp[t] = acc;
+    }
+  }
+}
+
 // The same update on the vector ALUs (d < 128: the matrix-core version
 // would leave waves idle with fewer than four 32-column blocks).
 template <typename T, int D>
@@ -1585,14 +1833,22 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
   bwd_gm_chain_kernel<D, false><<<dim3(D / kKT, kvheads), kThreads, 0, st>>>(w.R, w.G, dM, g.S, delta,
                                                                       w.gma, dM0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (D == 128)
+  // Blocks of qz_s partials per unit: 128-row blocks on the matrix-core
+  // path for bf16 storage at d = 128, 32-row chunks otherwise.
+  int upd_blocks = nb.chunks;
+  if constexpr (D == 128 && std::is_same<T, uint16_t>::value) {
+    upd_blocks = nb.qblocks;
+    bwd_update_mfma_kernel<D><<<dim3(nb.qblocks, g.S, kvheads), kThreads, 0, st>>>(
+        k, v, w.mt, w.z_pre, w.gma, g.L, g.N, g.S, g.eps, delta, dk, dv, w.qz_part);
+  } else if constexpr (D == 128) {
     bwd_update_kernel<T, D><<<dim3(nb.chunks, g.S, kvheads), kThreads, 0, st>>>(
         k, v, w.mt, w.z_pre, w.gma, g.L, g.N, g.S, g.eps, delta, dk, dv, w.qz_part);
-  else
+  } else {
     bwd_update_valu_kernel<T, D><<<dim3(nb.chunks, g.S, kvheads), kThreads, 0, st>>>(
         k, v, w.mt, w.z_pre, w.gma, g.L, g.N, g.S, g.eps, delta, dk, dv, w.qz_part);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (delta && (e = sum_parts(w.qz_part, units, nb.chunks, D, 0, w.qz, nullptr, st)) != hipSuccess)
+  if (delta && (e = sum_parts(w.qz_part, units, upd_blocks, D, 0, w.qz, nullptr, st)) != hipSuccess)
     return e;
   bwd_gz_chain_kernel<<<kvheads, D, 0, st>>>(w.r, w.qz, dz, g.S, D, w.gza, dz0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
