@@ -1084,9 +1084,30 @@ __global__ __launch_bounds__(kThreads) void bwd_gm_chain_kernel(
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
       g[i][jj] = dM ? dM[kvh * D * D + (r0 + 16 * i) * D + col0 + c0 + 16 * jj] : 0.f;
+  // G chunks travel through registers one chunk ahead of their use (the next
+  // step's first chunk during the last chunk of a step), and each step's R
+  // is loaded before its G product: the chain's steps are otherwise bound by
+  // the latency of these loads.
+  constexpr int SU = kKT * D / kThreads;  // G elements per thread and chunk
+  float pre[SU];
+  auto base_of = [&](int step) {
+    return (kvh * S + static_cast<size_t>(FWD ? step : S - 1 - step)) * D * D;
+  };
+  auto fetch_g = [&](size_t gbase, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int idx = t + kThreads * i;
+      pre[i] = G[gbase + static_cast<size_t>(idx / kKT) * D + k0 + idx % kKT];
+    }
+  };
+  if (delta && S > 0) fetch_g(base_of(0), 0);
   for (int step = 0; step < S; ++step) {
-    const int s = FWD ? step : S - 1 - step;
-    const size_t base = (kvh * S + s) * D * D;
+    const size_t base = base_of(step);
+    float rv[MI][2];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) rv[i][jj] = R[base + (r0 + 16 * i) * D + col0 + c0 + 16 * jj];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -1102,13 +1123,17 @@ __global__ __launch_bounds__(kThreads) void bwd_gm_chain_kernel(
         for (int jj = 0; jj < 2; ++jj) sM[r0 + 16 * i][c0 + 16 * jj] = g[i][jj];
       float acc[MI][2];
       zero(acc);
+#pragma unroll 1
       for (int k0 = 0; k0 < D; k0 += kKT) {
         __syncthreads();
-        for (int idx = t; idx < kKT * D; idx += kThreads) {
-          const int kk = idx % kKT, r = idx / kKT;
-          sG[kk][r] = G[base + static_cast<size_t>(r) * D + k0 + kk];
+#pragma unroll
+        for (int i = 0; i < SU; ++i) {
+          const int idx = t + kThreads * i;
+          sG[idx % kKT][idx / kKT] = pre[i];
         }
         __syncthreads();
+        if (k0 + kKT < D) fetch_g(base, k0 + kKT);
+        else if (step + 1 < S) fetch_g(base_of(step + 1), 0);
         mm16<MI, 2>(acc, kKT, [&](int r, int kk) { return sG[kk][r]; },
                     [&](int kk, int c) { return sM[k0 + kk][c]; });
       }
@@ -1120,7 +1145,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gm_chain_kernel(
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) g[i][jj] += R[base + (r0 + 16 * i) * D + col0 + c0 + 16 * jj];
+      for (int jj = 0; jj < 2; ++jj) g[i][jj] += rv[i][jj];
   }
   if (!FWD) {
 #pragma unroll
@@ -1755,20 +1780,45 @@ __global__ void bwd_gz_chain_kernel(const float *__restrict__ rvec, const float 
   }
 }
 
-// dk += gz_s sigma'(k) for every row of segment s.
+// dk += gz_s sigma'(k) for every row of segment s, four consecutive
+// elements per thread (D is a multiple of 4, so they share a row).
 template <typename T>
 __global__ void bwd_dk_gz_kernel(const T *__restrict__ k, const float *__restrict__ gza, int L,
-                                 int N, int S, int D, size_t total, float *__restrict__ dk) {
-  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
+                                 int N, int S, int D, size_t total4, float *__restrict__ dk) {
+  const size_t idx4 = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx4 >= total4) return;
+  const size_t idx = 4 * idx4;
   const int c = static_cast<int>(idx % D);
   const size_t row = idx / D;
   const size_t kvh = row / L;
   const int i = static_cast<int>(row % L);
   const int s = i / N;
-  const float kv = load_as_f32(k, idx);
-  const float sg = kv > 0.f ? 1.f : __expf(kv);
-  dk[idx] += gza[(kvh * S + s) * D + c] * sg;
+  float kv[4];
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    const u32x2 w2 = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(k) + idx);
+    kv[0] = lo_bf16(w2[0]);
+    kv[1] = hi_bf16(w2[0]);
+    kv[2] = lo_bf16(w2[1]);
+    kv[3] = hi_bf16(w2[1]);
+  } else {
+    const float4 f = *reinterpret_cast<const float4 *>(k + idx);
+    kv[0] = f.x;
+    kv[1] = f.y;
+    kv[2] = f.z;
+    kv[3] = f.w;
+  }
+  const float4 gz = *reinterpret_cast<const float4 *>(gza + (kvh * S + s) * D + c);
+  const float gv[4] = {gz.x, gz.y, gz.z, gz.w};
+  float4 *p = reinterpret_cast<float4 *>(dk + idx);
+  float4 x = *p;
+  float r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = gv[j] * (kv[j] > 0.f ? 1.f : __expf(kv[j]));
+  x.x += r[0];
+  x.y += r[1];
+  x.z += r[2];
+  x.w += r[3];
+  *p = x;
 }
 
 // Sum the per-block partials of `units` units in block order (see
@@ -1852,10 +1902,10 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
     return e;
   bwd_gz_chain_kernel<<<kvheads, D, 0, st>>>(w.r, w.qz, dz, g.S, D, w.gza, dz0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t total = static_cast<size_t>(kvheads) * g.L * D;
-  const size_t blocks = (total + 255) / 256;
+  const size_t total4 = static_cast<size_t>(kvheads) * g.L * D / 4;
+  const size_t blocks = (total4 + 255) / 256;
   bwd_dk_gz_kernel<T><<<static_cast<unsigned>(blocks), 256, 0, st>>>(k, w.gza, g.L, g.N, g.S, D,
-                                                                      total, dk);
+                                                                      total4, dk);
   return hipGetLastError();
 }
 
