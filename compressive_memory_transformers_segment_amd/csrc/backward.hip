@@ -792,8 +792,9 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
     float pl = 0.f, pe = 0.f;
     const uint16_t *q16 = reinterpret_cast<const uint16_t *>(q);
     const uint16_t *o16 = reinterpret_cast<const uint16_t *>(dout);
-    auto fetch = [&](int c) __attribute__((always_inline)) {
-      const int hl = c / nci, i0 = j0 + 32 * (c % nci);
+    // Chunk (hl, ci): query head hl of the group, rows j0 + 32 ci .. + 31.
+    auto fetch = [&](int hl, int ci) __attribute__((always_inline)) {
+      const int i0 = j0 + 32 * ci;
       const size_t hrow = (static_cast<size_t>(b) * Hq + j * grp + hl) * L;
 #pragma unroll
       for (int it = 0; it < KVN; ++it) {
@@ -809,8 +810,8 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
         pe = E[hrow + min(i0 + t, e - 1)];
       }
     };
-    auto stage = [&](int c) __attribute__((always_inline)) {  // rows past e: zero
-      const int rows = min(32, e - (j0 + 32 * (c % nci)));
+    auto stage = [&](int hl, int ci) __attribute__((always_inline)) {  // rows past e: zero
+      const int rows = min(32, e - (j0 + 32 * ci));
 #pragma unroll
       for (int it = 0; it < KVN; ++it) {
         const int idx = t + kThreads * it, r = idx / U16, c8 = 8 * (idx % U16);
@@ -821,19 +822,26 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
         }
       }
       if (t < 32) {
-        sL[t] = t < rows ? row_shift(c / nci, pl) : 0.f;
+        sL[t] = t < rows ? row_shift(hl, pl) : 0.f;
         sE[t] = t < rows ? pe : 0.f;
       }
     };
-    const int nch = grp * nci;
-    fetch(0);
-    for (int c = 0; c < nch; ++c) {
+    // (The chunk index advances as a (head, row chunk) pair: no divisions.)
+    fetch(0, 0);
+    for (int hl = 0, ci = 0; hl < grp;) {
       lds_barrier();
-      stage(c);
+      stage(hl, ci);
       lds_barrier();
-      if (c + 1 < nch) fetch(c + 1);
-      const int i0 = j0 + 32 * (c % nci);
-      if (wave_live && wk0 <= i0 + 31) chunk(c / nci, i0);  // else: every key after every row
+      int nhl = hl, nci2 = ci + 1;
+      if (nci2 == nci) {
+        nci2 = 0;
+        ++nhl;
+      }
+      if (nhl < grp) fetch(nhl, nci2);
+      const int i0 = j0 + 32 * ci;
+      if (wave_live && wk0 <= i0 + 31) chunk(hl, i0);  // else: every key after every row
+      hl = nhl;
+      ci = nci2;
     }
   } else {
     for (int hl = 0; hl < grp; ++hl) {
