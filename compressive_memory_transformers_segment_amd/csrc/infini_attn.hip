@@ -190,7 +190,7 @@ int bind_workspace(infini_attn_handle *h, const ia::Geometry &g, ia::Workspace *
 }
 
 hipError_t launch_scan(const infini_attn_handle *h, const ia::Geometry &g, const void *k,
-                       const void *v, float *M, const float *z, int delta,
+                       const void *v, float *M, float *z, int delta,
                        const ia::Workspace &ws) {
   return h->desc.dtype == INFINI_ATTN_BF16
              ? ia::launch_segment_scan_bf16(g, static_cast<const uint16_t *>(k),
@@ -201,9 +201,11 @@ hipError_t launch_scan(const infini_attn_handle *h, const ia::Geometry &g, const
                                            h->stream);
 }
 
-// Final z: slot S of every head's snapshot row -> z [B*Hkv][D].
+// Final z: slot S of every head's snapshot row -> z [B*Hkv][D]. (The bf16
+// scan's z prefix kernel writes it in place; the fp32 scan leaves it here.)
 hipError_t copy_final_z(const infini_attn_handle *h, const ia::Geometry &g, float *z,
                         const ia::Workspace &ws) {
+  if (h->desc.dtype == INFINI_ATTN_BF16) return hipSuccess;
   const size_t row = static_cast<size_t>(g.D) * sizeof(float);
   return hipMemcpy2DAsync(z, row, ws.z_pre + static_cast<size_t>(g.S) * g.D, (g.S + 1) * row, row,
                           static_cast<size_t>(g.B) * g.Hkv, hipMemcpyDeviceToDevice, h->stream);

@@ -83,9 +83,10 @@ hipError_t launch_segment_scan_f32(const Geometry &g, const float *k, const floa
                                    hipStream_t stream);
 
 // Segment scan, bf16 storage: per-segment statistics on MFMA in parallel, then
-// the fp32 recurrence; writes z_pre (slot S = final z), mt_pre_bf16 and M.
+// the fp32 recurrence; writes z_pre (slot S = final z), mt_pre_bf16, and the
+// final M and z in place (z is read as z_0 first).
 hipError_t launch_segment_scan_bf16(const Geometry &g, const uint16_t *k, const uint16_t *v,
-                                    float *M, const float *z, int delta, const Workspace &ws,
+                                    float *M, float *z, int delta, const Workspace &ws,
                                     hipStream_t stream);
 
 // Fused per-segment kernel: local causal attention, retrieval from the

@@ -141,11 +141,14 @@ constexpr int kZB = 16;
 constexpr int kZThreads = 1024;
 constexpr int kZCols = 32;  // columns per workgroup
 
-__global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restrict__ z0,
+// The final z also goes to z_final, which may be z0 itself (the caller's
+// in/out state): every thread reads z0 before the barrier that precedes that
+// store, and each workgroup touches only its own columns.
+__global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *z0,
                                                             const float *__restrict__ dz,
                                                             float *__restrict__ z_pre,
                                                             uint16_t *__restrict__ z_hl, int S,
-                                                            int D, int parts) {
+                                                            int D, int parts, float *z_final) {
   __shared__ float tot[kZThreads];
   const int head = blockIdx.y, G = kZThreads / kZCols;
   const int cl = threadIdx.x % kZCols, grp = threadIdx.x / kZCols;
@@ -191,11 +194,14 @@ __global__ __launch_bounds__(kZThreads) void zprefix_kernel(const float *__restr
       }
     }
   }
+  float zs = 0.f;
   if (grp == G - 1) {
-    float zs = z0[static_cast<size_t>(head) * D + c];
+    zs = z0[static_cast<size_t>(head) * D + c];
     for (int q = 0; q < G; ++q) zs += tot[q * kZCols + cl];
     out[static_cast<size_t>(S) * D] = zs;
   }
+  __syncthreads();  // every read of z0 in this workgroup is done
+  if (grp == G - 1) z_final[static_cast<size_t>(head) * D + c] = zs;
 }
 
 // ---------------------------------------------------------------------------
@@ -793,7 +799,7 @@ __global__ __launch_bounds__(256) void chain_pack_kernel(const float *__restrict
 
 template <int D>
 hipError_t launch_d(const Geometry &g, const uint16_t *k, const uint16_t *v, float *M,
-                    const float *z, int delta, const Workspace &ws, hipStream_t stream) {
+                    float *z, int delta, const Workspace &ws, hipStream_t stream) {
   const int heads = g.B * g.Hkv;
   const int parts = ws.z_parts;
   // Few (segment, head) pairs: split each one's output tiles over two
@@ -805,7 +811,7 @@ hipError_t launch_d(const Geometry &g, const uint16_t *k, const uint16_t *v, flo
   zsum_kernel<D><<<dim3(g.S * parts, heads), 256, 0, stream>>>(k, g.lkv, g.Hkv, ws.dz, g.L, g.N,
                                                                 g.S, parts);
   zprefix_kernel<<<dim3(D / kZCols, heads), kZThreads, 0, stream>>>(z, ws.dz, ws.z_pre, ws.z_hl,
-                                                                     g.S, D, parts);
+                                                                     g.S, D, parts, z);
   if (delta) {
     if (split)
       gh_kernel<D, true, 2, 2><<<ghgrid, 512, 0, stream>>>(k, v, g.lkv, g.Hkv, ws.z_pre, ws.gh,
@@ -858,7 +864,7 @@ int chain_chunk_len(int S, int heads) {
 }
 
 hipError_t launch_segment_scan_bf16(const Geometry &g, const uint16_t *k, const uint16_t *v,
-                                    float *M, const float *z, int delta, const Workspace &ws,
+                                    float *M, float *z, int delta, const Workspace &ws,
                                     hipStream_t stream) {
   switch (g.D) {
     case 32: return launch_d<32>(g, k, v, M, z, delta, ws, stream);
