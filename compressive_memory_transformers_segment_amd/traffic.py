@@ -8,7 +8,8 @@
 
 Each directory holds the ``*counter_collection.csv`` of one ``rocprofv3 --pmc``
 run (``FETCH_SIZE`` in one, ``WRITE_SIZE`` in the other; the counters read KiB
-per dispatch). The same run also copies ``--copy-bytes`` bytes with a plain
+per dispatch); in ``--command`` (the arguments after ``rocprofv3 --pmc NAME``)
+the word COUNTER stands for the counter's name. The same run also copies ``--copy-bytes`` bytes with a plain
 device-to-device copy kernel: the factor that maps its counted bytes onto the
 bytes it actually moved calibrates the counters of every other kernel.
 
@@ -104,8 +105,8 @@ def summarize(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str, mo
     lines = [
         f"# HBM traffic per launch, workload {workload}, {mode} rule",
         "# Commands (repository root, one MI355X, rocprofv3, TMPDIR=/tmp), one counter per run:",
-        f"#   rocprofv3 --pmc FETCH_SIZE {command}",
-        f"#   rocprofv3 --pmc WRITE_SIZE {command}",
+        f"#   rocprofv3 --pmc FETCH_SIZE {command.replace('COUNTER', 'FETCH_SIZE')}",
+        f"#   rocprofv3 --pmc WRITE_SIZE {command.replace('COUNTER', 'WRITE_SIZE')}",
         f"# Calibration: a {copy_bytes} byte device-to-device copy reads FETCH_SIZE {cf:.1f} KiB"
         f" and WRITE_SIZE {cw:.1f} KiB;",
         f"# FETCH_SIZE is scaled by {fscale:.4f} and WRITE_SIZE by {wscale:.4f}.",
