@@ -220,8 +220,14 @@ __device__ __forceinline__ f32x16 zero16() {
 //   dq^T = K^T dS^T takes dS^T from registers;
 //   retrieval: num^T = Mp^T sigma(Q)^T and dsq^T = Mp dnum^T, one 32-row
 //   chunk of Mp^T in LDS at a time.
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1)) void bwd_query_kernel(
+// MODE 0 runs both passes over the keys in one launch. For bf16 storage they
+// are two launches over the same grid: MODE 1 (statistics only: lse and E,
+// 120 registers, three workgroups per CU) and MODE 2 (reads them back, then
+// dq, the retrieval and d beta, two workgroups per CU); the pair is about 3%
+// faster at the Llama-3-8B shape than the single launch, whose register
+// budget the second pass sets for the first as well.
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? (MODE == 1 ? 3 : 2) : 1)) void bwd_query_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ beta, const float *__restrict__ mt,
     const float *__restrict__ zpre, int Hq, int Hkv, int L, int N, int S, float eps,
@@ -256,7 +262,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
       dbeta_part + static_cast<size_t>(h) * (static_cast<size_t>(gridDim.z / Hq) * S * gridDim.x) +
       (static_cast<size_t>(b) * S + s) * gridDim.x + blockIdx.x;
   if (i0 >= e) {
-    if (t == 0) *dbeta_slot = 0.f;
+    if (MODE != 1 && t == 0) *dbeta_slot = 0.f;
     return;
   }
   const int kend = min(i0 + QT, e);  // keys this tile's rows can see: [a, kend)
@@ -391,33 +397,48 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
       }
     }
   };
-  float m = -INFINITY, l = 0.f, ea = 0.f;  // m: running max of the scaled scores
-  pass([&](int j0) __attribute__((always_inline)) {
-    f32x16 st, ot;
-    scores(st, ot);
-    mask_scores(st, j0);
-    float mx = fmaxf(st[0], st[1]);
+  float lse, E;
+  if constexpr (MODE == 2) {
+    // The statistics launch stored them; rows past the segment end take a
+    // shift of -inf, so their (never stored) dS is zero.
+    lse = qvalid ? lse_out[qbase + qi] : INFINITY;
+    E = qvalid ? e_out[qbase + qi] : 0.f;
+  } else {
+    float m = -INFINITY, l = 0.f, ea = 0.f;  // m: running max of the scaled scores
+    pass([&](int j0) __attribute__((always_inline)) {
+      f32x16 st, ot;
+      scores(st, ot);
+      mask_scores(st, j0);
+      float mx = fmaxf(st[0], st[1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st[r], st[r + 1]));
-    mx = max_xor32(mx) * scale;  // the scale is positive: max(s) scale = max(s scale)
-    const float mn = fmaxf(m, mx);
-    const float nb = -mn * kLog2e;
-    float ps = 0.f, pe = 0.f;
+      for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st[r], st[r + 1]));
+      mx = max_xor32(mx) * scale;  // the scale is positive: max(s) scale = max(s scale)
+      const float mn = fmaxf(m, mx);
+      const float nb = -mn * kLog2e;
+      float ps = 0.f, pe = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sc2, nb));
-      ps += p;
-      pe = __builtin_fmaf(p, ot[r], pe);
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sc2, nb));
+        ps += p;
+        pe = __builtin_fmaf(p, ot[r], pe);
+      }
+      ps = sum_xor32(ps);
+      pe = sum_xor32(pe);
+      const float f = __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+      l = l * f + ps;
+      ea = ea * f + pe;
+      m = mn;
+    });
+    lse = m + __logf(l);
+    E = ea / l;
+  }
+  if constexpr (MODE == 1) {
+    if (qvalid && g == 0) {
+      lse_out[qbase + qi] = lse;
+      e_out[qbase + qi] = E;
     }
-    ps = sum_xor32(ps);
-    pe = sum_xor32(pe);
-    const float f = __builtin_amdgcn_exp2f((m - mn) * kLog2e);
-    l = l * f + ps;
-    ea = ea * f + pe;
-    m = mn;
-  });
-  const float lse = m + __logf(l);
-  const float E = ea / l;
+    return;
+  }
 
   // Pass 2: dS^T = (1 - g) P^T (dO V^T - E)^T, dq^T += K^T dS^T.
   f32x16 dqa[NB];
@@ -599,8 +620,10 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
   const float dden = -gam * s1 / (den * den);
   if (qvalid && g == 0) {
     dden_out[qbase + qi] = dden;
-    lse_out[qbase + qi] = lse;
-    e_out[qbase + qi] = E;
+    if constexpr (MODE == 0) {
+      lse_out[qbase + qi] = lse;
+      e_out[qbase + qi] = E;
+    }
   }
   if (qvalid) {
 #pragma unroll
@@ -1873,9 +1896,19 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
   bwd_gm_chain_kernel<D, true><<<dim3(D / kKT, kvheads), kThreads, 0, st>>>(w.H, w.G, M0, g.S,
                                                                            delta, w.mt, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_query_kernel<T, D><<<dim3(nb.qblocks, g.S, g.B * g.Hq), kThreads, 0, st>>>(
-      q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
-      w.dnum, w.dden, w.dbeta_part);
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    bwd_query_kernel<T, D, 1><<<dim3(nb.qblocks, g.S, g.B * g.Hq), kThreads, 0, st>>>(
+        q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
+        w.dnum, w.dden, w.dbeta_part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    bwd_query_kernel<T, D, 2><<<dim3(nb.qblocks, g.S, g.B * g.Hq), kThreads, 0, st>>>(
+        q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
+        w.dnum, w.dden, w.dbeta_part);
+  } else {
+    bwd_query_kernel<T, D, 0><<<dim3(nb.qblocks, g.S, g.B * g.Hq), kThreads, 0, st>>>(
+        q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
+        w.dnum, w.dden, w.dbeta_part);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = sum_parts(w.dbeta_part, g.Hq, g.B * g.S * nb.qblocks, 1, 0, dbeta, nullptr, st)) !=
       hipSuccess)
