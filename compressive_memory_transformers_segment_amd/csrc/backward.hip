@@ -212,7 +212,7 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// query: dq, the softmax row statistics (lse, E) and dnum / dden for the
+// query: dq, the softmax row statistics (lse, E) and gamma / den, dden for the
 // outer products, and the gate's contribution to d beta. 128 query rows per
 // workgroup, 32 per wave; key tiles of 32.
 //   S^T = K Q^T and (dO V^T)^T = V dO^T put one query per lane, so the row
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? (MODE
     const T *__restrict__ dout, const float *__restrict__ beta, const float *__restrict__ mt,
     const float *__restrict__ zpre, int Hq, int Hkv, int L, int N, int S, float eps,
     float *__restrict__ dq, float *__restrict__ lse_out, float *__restrict__ e_out,
-    float *__restrict__ dnum_out, float *__restrict__ dden_out, float *__restrict__ dbeta_part) {
+    float *__restrict__ gd_out, float *__restrict__ dden_out, float *__restrict__ dbeta_part) {
   constexpr int P = D + 1;
   constexpr int NB = D / 32;  // 32-wide blocks along d
   constexpr int QT = 128;
@@ -510,6 +510,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? (MODE
     }
     den = sum_xor32(den) + eps;
     const float gd = gam / den;
+    if (qvalid && g == 0) gd_out[qbase + qi] = gd;
     for (int jb = 0; jb < NB; ++jb) {
       __syncthreads();
       // Rows 32 jb .. 32 jb + 31 of Mp^T as bf16 hi (sKb) and lo (sVb) parts.
@@ -551,11 +552,6 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? (MODE
           s1 += o4[i] * num[4 * r4 + i];
           dn[4 * r4 + i] = gd * o4[i];
         }
-        if (qvalid) {
-          float *dst = dnum_out + (qbase + qi) * D + j;
-          *reinterpret_cast<float4 *>(dst) = make_float4(dn[4 * r4], dn[4 * r4 + 1],
-                                                         dn[4 * r4 + 2], dn[4 * r4 + 3]);
-        }
       }
       // dsq^T[c][i] += sum_j Mp[c][j] dnum[i][j], j = 32 jb + kappa(r, g).
 #pragma unroll
@@ -578,6 +574,8 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? (MODE
 #pragma unroll
     for (int u = 0; u < D / 2; ++u) den += qr[u] * sZ[2 * u + g];
     den += __shfl_xor(den, 32) + eps;
+    const float gd = gam / den;
+    if (qvalid && g == 0) gd_out[qbase + qi] = gd;
     for (int jb = 0; jb < NB; ++jb) {
       __syncthreads();
       for (int idx = t; idx < kKT * D; idx += kThreads) {
@@ -600,12 +598,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? (MODE
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           s1 += o4[i] * num[4 * r4 + i];
-          dn[4 * r4 + i] = gam * o4[i] / den;
-        }
-        if (qvalid) {
-          float *dst = dnum_out + (qbase + qi) * D + j;
-          *reinterpret_cast<float4 *>(dst) = make_float4(dn[4 * r4], dn[4 * r4 + 1],
-                                                         dn[4 * r4 + 2], dn[4 * r4 + 3]);
+          dn[4 * r4 + i] = gd * o4[i];
         }
       }
       // dsq^T[c][i] += sum_j Mp[c][j] dnum[i][j], j = 32 jb + kappa(r, g).
@@ -901,7 +894,9 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
 // ---------------------------------------------------------------------------
 // outer: per (b, kv head, segment), out += A^T B over a range of rows.
 //   kind 0 (R): rows = (query head of the group, row of the segment),
-//               A = sigma(q), B = dnum; r_s = sum A^T dden as well.
+//               A = sigma(q), B = dnum = gd dO (x2 = d_out, gd = gamma / den
+//               per row, the product formed as in the query kernel);
+//               r_s = sum A^T dden as well.
 //   kind 1 (G): rows = rows of the segment, A = sigma(k), B = sigma(k) / denk.
 //   kind 2 (H): rows = rows of the segment, A = sigma(k), B = v (x2).
 // Each block writes the partial sum of its row range, D x D floats and then
@@ -909,7 +904,7 @@ __global__ __launch_bounds__(kThreads, (std::is_same<T, uint16_t>::value ? 2 : 1
 // blocks of a unit in index order, so the result does not depend on timing.
 template <typename T, int D, int KIND>
 __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
-    const T *__restrict__ x, const T *__restrict__ x2, const float *__restrict__ dnum,
+    const T *__restrict__ x, const T *__restrict__ x2, const float *__restrict__ gd,
     const float *__restrict__ dden, const float *__restrict__ zpre, int Hq, int Hkv, int L, int N,
     int S, float eps, int rows_per_block, float *__restrict__ part) {
   // The D x D sum of outer products over a range of rows runs on the bf16
@@ -952,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
   if (KIND == 1)
     for (int c = t; c < D; c += kThreads) sZ[c] = zpre[(static_cast<size_t>(kvh) * (S + 1) + s) * D + c];
 
-  // Source row (of x, and of dnum / dden for kind 0) of unit row u.
+  // Source row (of x, and of d_out, gd and dden for kind 0) of unit row u.
   auto src_row = [&](int u) -> size_t {
     if (KIND == 0) {
       const int hl = u / n, i = a + u % n;
@@ -1005,8 +1000,9 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
         av[2] = elu1(xa.z);
         av[3] = elu1(xa.w);
         if (KIND == 0) {
-          const float4 d4 = *reinterpret_cast<const float4 *>(dnum + row * D + c);
-          bv[0] = d4.x; bv[1] = d4.y; bv[2] = d4.z; bv[3] = d4.w;
+          const float gr = gd[row];
+          const float4 o4 = load4(x2, row, c);
+          bv[0] = gr * o4.x; bv[1] = gr * o4.y; bv[2] = gr * o4.z; bv[3] = gr * o4.w;
         } else if (KIND == 2) {
           const float4 v4 = load4(x2, row, c);
           bv[0] = v4.x; bv[1] = v4.y; bv[2] = v4.z; bv[3] = v4.w;
@@ -1899,15 +1895,15 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
   if constexpr (std::is_same<T, uint16_t>::value) {
     bwd_query_kernel<T, D, 1><<<dim3(nb.qblocks, g.S, g.B * g.Hq), kThreads, 0, st>>>(
         q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
-        w.dnum, w.dden, w.dbeta_part);
+        w.gd, w.dden, w.dbeta_part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_query_kernel<T, D, 2><<<dim3(nb.qblocks, g.S, g.B * g.Hq), kThreads, 0, st>>>(
         q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
-        w.dnum, w.dden, w.dbeta_part);
+        w.gd, w.dden, w.dbeta_part);
   } else {
     bwd_query_kernel<T, D, 0><<<dim3(nb.qblocks, g.S, g.B * g.Hq), kThreads, 0, st>>>(
         q, k, v, dout, beta, w.mt, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, dq, w.lse, w.erow,
-        w.dnum, w.dden, w.dbeta_part);
+        w.gd, w.dden, w.dbeta_part);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = sum_parts(w.dbeta_part, g.Hq, g.B * g.S * nb.qblocks, 1, 0, dbeta, nullptr, st)) !=
@@ -1917,7 +1913,7 @@ hipError_t launch_bwd_t(const Geometry &g, const T *q, const T *k, const T *v, c
       q, k, v, dout, beta, w.lse, w.erow, g.Hq, g.Hkv, g.L, g.N, dk, dv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bwd_outer_kernel<T, D, 0><<<dim3(nb.group_rows, g.S, kvheads), kThreads, 0, st>>>(
-      q, nullptr, w.dnum, w.dden, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, nb.rows_per, w.part);
+      q, dout, w.gd, w.dden, w.z_pre, g.Hq, g.Hkv, g.L, g.N, g.S, g.eps, nb.rows_per, w.part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = sum_parts(w.part, units, nb.group_rows, D * D, D, w.R, w.r, st)) != hipSuccess)
     return e;

@@ -615,7 +615,7 @@ int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const v
   const int delta = update_mode == INFINI_ATTN_DELTA;
 
   // Scratch layout (each part 256-byte aligned): z_pre, mt, dzs, lse, erow,
-  // dnum, dden, R, r, G (delta only), qz, H, gma, gza, and the per-block
+  // gd, dden, R, r, G (delta only), qz, H, gma, gza, and the per-block
   // partial sums (products, qz, dbeta).
   const size_t units = kvheads * g.S;
   const size_t qrows = static_cast<size_t>(g.B) * g.Hq * g.L;
@@ -626,7 +626,7 @@ int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const v
   const size_t sz[17] = {
       round_up(kvheads * (g.S + 1) * D * sizeof(float)), round_up(units * D * D * sizeof(float)),
       round_up(units * D * sizeof(float)), round_up(qrows * sizeof(float)),
-      round_up(qrows * sizeof(float)), round_up(qrows * D * sizeof(float)),
+      round_up(qrows * sizeof(float)), round_up(qrows * sizeof(float)),
       round_up(qrows * sizeof(float)), round_up(units * D * D * sizeof(float)),
       round_up(units * D * sizeof(float)), delta ? round_up(units * D * D * sizeof(float)) : 0,
       round_up(units * D * sizeof(float)), round_up(units * D * D * sizeof(float)),
@@ -650,7 +650,7 @@ int infini_attn_backward(infini_attn_t *h, const void *q, const void *k, const v
   w.dzs = part[2];
   w.lse = part[3];
   w.erow = part[4];
-  w.dnum = part[5];
+  w.gd = part[5];
   w.dden = part[6];
   w.R = part[7];
   w.r = part[8];

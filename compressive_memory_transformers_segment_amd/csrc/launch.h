@@ -107,9 +107,10 @@ struct BwdWorkspace {
   float *mt;     // [B*Hkv][S][D(v)][D(k)] M^T before every segment (scan output)
   float *lse;    // [B*Hq*L] log-sum-exp of each query row's causal softmax
   float *erow;   // [B*Hq*L] dO_i . A_dot_i
-  float *dnum;   // [B*Hq*L][D] gradient of the retrieval numerator
+  float *gd;     // [B*Hq*L] gamma / den of each query row: the retrieval numerator's
+                 // gradient is gd dO_i, formed again where it is needed
   float *dden;   // [B*Hq*L] gradient of the retrieval denominator
-  float *R;      // [units][D][D] sum of sigma(q)^T dnum over the group (zeroed)
+  float *R;      // [units][D][D] sum of sigma(q)^T (gd dO) over the group (zeroed)
   float *r;      // [units][D] sum of sigma(q)^T dden over the group (zeroed)
   float *G;      // [units][D][D] delta rule's sigma(k)^T diag(1/denk) sigma(k) (zeroed)
   float *qz;     // [units][D] delta rule's sigma(k)^T ddenk (zeroed)
