@@ -1014,12 +1014,20 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
     if (KIND == 0 && t < kKT) sX[t] = t < cnt ? dden[src_row(c0u + t)] : 0.f;
     __syncthreads();
     if (KIND == 1) {
-      // B = sigma(k) / (sigma(k) . z + eps), row by row.
-      if (t < kKT) {
-        float d = eps;
-        for (int c = 0; c < D; ++c)
-          d += (bf16_to_f32(sAh[t][c]) + bf16_to_f32(sAl[t][c])) * sZ[c];
-        sX[t] = 1.f / d;
+      // B = sigma(k) / (sigma(k) . z + eps), row by row: eight threads per
+      // row take D / 8 columns each, then add their sums in a butterfly (the
+      // same order on every lane of the eight).
+      {
+        static_assert(kThreads == 8 * kKT, "eight threads per staged row");
+        const int r = t >> 3, part = t & 7;
+        float d = 0.f;
+#pragma unroll
+        for (int c = part * (D / 8); c < (part + 1) * (D / 8); ++c)
+          d += (bf16_to_f32(sAh[r][c]) + bf16_to_f32(sAl[r][c])) * sZ[c];
+        d += __shfl_xor(d, 1);
+        d += __shfl_xor(d, 2);
+        d += __shfl_xor(d, 4);
+        if (part == 0) sX[r] = 1.f / (d + eps);
       }
       __syncthreads();
       for (int idx = t; idx < kKT * D / 4; idx += kThreads) {
