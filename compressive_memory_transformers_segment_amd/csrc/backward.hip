@@ -955,18 +955,6 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
     }
     return static_cast<size_t>(kvh) * L + a + u;
   };
-  // Four consecutive elements of row `row` of a [rows][D] tensor as fp32.
-  auto load4 = [&](const T *src, size_t row, int c) __attribute__((always_inline)) {
-    float4 r;
-    if constexpr (BF) {
-      const u32x2 w2 = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(src) +
-                                                        row * D + c);
-      r = make_float4(lo_bf16(w2[0]), hi_bf16(w2[0]), lo_bf16(w2[1]), hi_bf16(w2[1]));
-    } else {
-      r = *reinterpret_cast<const float4 *>(src + row * D + c);
-    }
-    return r;
-  };
   // Split four values into bf16 hi and lo parts and store them at (r, c).
   auto put4 = [&](uint16_t (*th)[PB], uint16_t (*tl)[PB], int r, int c, const float (&v)[4])
                   __attribute__((always_inline)) {
@@ -982,37 +970,73 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
     if (tl != nullptr) *reinterpret_cast<u32x2 *>(&tl[r][c]) = u32x2{lw[0], lw[1]};
   };
 
+  // The next chunk's rows travel in registers (raw words: bf16 pairs or
+  // fp32) while the current chunk is worked on; the barriers inside the loop
+  // order LDS only, so that they do not wait for those loads.
+  constexpr int IT = kKT * D / 4 / kThreads;  // 4-element groups per thread
+  static_assert(IT >= 1 && IT * kThreads == kKT * D / 4, "whole groups per thread");
+  using Raw = typename std::conditional<BF, u32x2, float4>::type;
+  auto raw_load = [&](const T *src, size_t row, int c) __attribute__((always_inline)) {
+    if constexpr (BF)
+      return *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(src) + row * D + c);
+    else
+      return *reinterpret_cast<const float4 *>(src + row * D + c);
+  };
+  auto raw_f32 = [&](const Raw &w2) __attribute__((always_inline)) {
+    if constexpr (BF)
+      return make_float4(lo_bf16(w2[0]), hi_bf16(w2[0]), lo_bf16(w2[1]), hi_bf16(w2[1]));
+    else
+      return w2;
+  };
+  Raw fa[IT], fb[IT];
+  float fg[IT], fx = 0.f;
+  auto fetch = [&](int c0u) __attribute__((always_inline)) {
+    const int cnt = min(kKT, u1 - c0u);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = t + kThreads * it, r = idx / (D / 4), c = 4 * (idx % (D / 4));
+      // rows past the range read the range's first row; staging zeroes them
+      const size_t row = src_row(c0u + (r < cnt ? r : 0));
+      fa[it] = raw_load(x, row, c);
+      if (KIND == 0) fg[it] = gd[row];
+      if (KIND != 1) fb[it] = raw_load(x2, row, c);
+    }
+    if (KIND == 0 && t < kKT) fx = t < cnt ? dden[src_row(c0u + t)] : 0.f;
+  };
+
   f32x16 acc[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) acc[i] = zero16();
   float racc = 0.f;
+  fetch(u0);
   for (int c0u = u0; c0u < u1; c0u += kKT) {
     const int cnt = min(kKT, u1 - c0u);
-    __syncthreads();
-    for (int idx = t; idx < kKT * D / 4; idx += kThreads) {
-      const int r = idx / (D / 4), c = 4 * (idx % (D / 4));
+    lds_barrier();
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = t + kThreads * it, r = idx / (D / 4), c = 4 * (idx % (D / 4));
       float av[4] = {0.f, 0.f, 0.f, 0.f}, bv[4] = {0.f, 0.f, 0.f, 0.f};
       if (r < cnt) {
-        const size_t row = src_row(c0u + r);
-        const float4 xa = load4(x, row, c);
+        const float4 xa = raw_f32(fa[it]);
         av[0] = elu1(xa.x);
         av[1] = elu1(xa.y);
         av[2] = elu1(xa.z);
         av[3] = elu1(xa.w);
         if (KIND == 0) {
-          const float gr = gd[row];
-          const float4 o4 = load4(x2, row, c);
+          const float gr = fg[it];
+          const float4 o4 = raw_f32(fb[it]);
           bv[0] = gr * o4.x; bv[1] = gr * o4.y; bv[2] = gr * o4.z; bv[3] = gr * o4.w;
         } else if (KIND == 2) {
-          const float4 v4 = load4(x2, row, c);
+          const float4 v4 = raw_f32(fb[it]);
           bv[0] = v4.x; bv[1] = v4.y; bv[2] = v4.z; bv[3] = v4.w;
         }
       }
       put4(sAh, sAl, r, c, av);
       if (KIND != 1) put4(sBh, B_EXACT ? nullptr : sBl, r, c, bv);
     }
-    if (KIND == 0 && t < kKT) sX[t] = t < cnt ? dden[src_row(c0u + t)] : 0.f;
-    __syncthreads();
+    if (KIND == 0 && t < kKT) sX[t] = fx;
+    if (c0u + kKT < u1) fetch(c0u + kKT);
+    lds_barrier();
     if (KIND == 1) {
       // B = sigma(k) / (sigma(k) . z + eps), row by row: eight threads per
       // row take D / 8 columns each, then add their sums in a butterfly (the
@@ -1029,7 +1053,7 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
         d += __shfl_xor(d, 4);
         if (part == 0) sX[r] = 1.f / (d + eps);
       }
-      __syncthreads();
+      lds_barrier();
       for (int idx = t; idx < kKT * D / 4; idx += kThreads) {
         const int r = idx / (D / 4), c = 4 * (idx % (D / 4));
         float bv[4];
@@ -1038,7 +1062,7 @@ __global__ __launch_bounds__(kThreads) void bwd_outer_kernel(
           bv[i] = (bf16_to_f32(sAh[r][c + i]) + bf16_to_f32(sAl[r][c + i])) * sX[r];
         put4(sBh, sBl, r, c, bv);
       }
-      __syncthreads();
+      lds_barrier();
     }
     if (KIND == 0 && t < D)
       for (int kk = 0; kk < kKT; ++kk)
